@@ -1,0 +1,340 @@
+"""Benchmark of the MoE row-movement hot path on one MI355X.
+
+One step = ep_layout + ep_dispatch + ep_combine over one batch of the chosen
+workload (default: the training shape, T=4096 tokens, H=7168 bf16, E=256
+experts, top-8), inputs resident in HBM.  The expert op between dispatch and
+combine (a per-expert scale for this shape) is applied once before timing and
+is not part of a step.
+
+Prints ONE JSON line: whole-step algorithmic HBM GB/s with all CUs
+(``value``), tokens/s, the same at a 24-CU budget, per-kernel times, the
+roofline entry of the dominant kernel (HIP events on the launch stream) and
+the CPU oracle timed on the host.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
+  python bench.py --sweep FILE   # CU-budget x variant sweep + copy ceilings, JSONL
+"""
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s and tokens/s on 1 MI355X at 24 CUs and all CUs"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="train")
+    p.add_argument("--variant", default="auto")
+    p.add_argument("--budget", type=int, default=24, help="the restricted CU budget reported beside all CUs")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sweep", default=None, help="write a CU x variant sweep as JSONL to this file")
+    return p.parse_args()
+
+
+class Setup:
+    """Device buffers of one workload and the step that runs on them."""
+
+    def __init__(self, name):
+        import numpy as np
+        import torch
+
+        import bulk_async_tensor_amd as ep
+        from synth import algorithmic_bytes, make_workload
+
+        self.ep = ep
+        self.torch = torch
+        dev = torch.device("cuda:0")
+        wl = make_workload(name)
+        self.wl = wl
+        c = self.cfg = wl.config
+        self.T, self.H, self.E, self.k = c.T, c.H, c.E, c.k
+        R = c.T * c.k
+        self.idx = torch.from_numpy(wl.topk_idx).to(dev)
+        self.w = torch.from_numpy(wl.topk_w).to(dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.counts = torch.empty(c.E, **i32)
+        self.offsets = torch.empty(c.E + 1, **i32)
+        self.dest_row = torch.empty((c.T, c.k), **i32)
+        self.src_token = torch.empty(R, **i32)
+        self.status = torch.empty(1, **i32)
+        self.ws = torch.empty(max(16, ep.ep_layout_workspace_bytes(c.T, c.k, c.E)), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+        self.do_dispatch = c.ops != "combine"
+        self.layout()
+        if self.do_dispatch:
+            self.x = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
+            self.recv = torch.empty((R, c.H), dtype=torch.bfloat16, device=dev)
+            ep.ep_dispatch(self.x, self.dest_row, self.recv)
+            if c.expert == "scale":
+                # expert op (not timed): y[r] = bf16(s_e * recv[r]) for the expert e of row r
+                s = torch.from_numpy(wl.scales).to(dev)
+                row_scale = torch.repeat_interleave(s, self.counts.long(), output_size=R)
+                self.y = (self.recv.float() * row_scale[:, None]).to(torch.bfloat16)
+            else:
+                self.y = self.recv  # identity expert: combine reads what dispatch wrote
+        else:
+            self.y = torch.from_numpy(wl.y.view(np.int16)).to(dev).view(torch.bfloat16)
+        torch.cuda.synchronize()
+        if int(self.status.item()) != 0:
+            raise RuntimeError("layout flagged the routing as invalid")
+        self.bytes = algorithmic_bytes(c.T, c.H, c.k, c.E)
+        if not self.do_dispatch:
+            self.bytes["dispatch"] = 0
+        self.step_bytes = sum(self.bytes.values())
+
+    def layout(self):
+        self.ep.ep_layout(self.idx, self.E, self.counts, self.offsets, self.dest_row, self.src_token, self.status,
+                          self.ws)
+
+    def dispatch(self):
+        if self.do_dispatch:
+            self.ep.ep_dispatch(self.x, self.dest_row, self.recv)
+
+    def combine(self):
+        self.ep.ep_combine(self.y, self.dest_row, self.w, self.out)
+
+    def run(self, steps, warmup):
+        """Times `steps` whole steps; per-kernel times from HIP events recorded
+        on the stream the kernels are launched on."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            self.layout()
+            self.dispatch()
+            self.combine()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            e = ev[i]
+            e[0].record(stream)
+            self.layout()
+            e[1].record(stream)
+            self.dispatch()
+            e[2].record(stream)
+            self.combine()
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {"layout": 0.0, "dispatch": 0.0, "combine": 0.0}
+        for e in ev:
+            per["layout"] += e[0].elapsed_time(e[1])
+            per["dispatch"] += e[1].elapsed_time(e[2])
+            per["combine"] += e[2].elapsed_time(e[3])
+        per = {k: v / steps for k, v in per.items()}  # ms per launch
+        ms = wall * 1e3 / steps
+        return ms, per
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bulk_async_tensor_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when it
+    is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^([a-z_]+):\s*(\S+)", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_sources") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(name, seconds):
+    """The oracle as it stands, on the host, over the whole workload, repeated
+    until about `seconds` of CPU work; reported in the metric's unit."""
+    import oracle
+    from synth import algorithmic_bytes, make_workload
+
+    wl = make_workload(name)
+    c = wl.config
+    y_fixed = wl.y
+    scales = wl.scales
+    passes = 0
+    t_total = 0.0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        lay = oracle.layout(wl.topk_idx, c.E)
+        if c.ops != "combine":
+            recv = oracle.dispatch(wl.x, lay["dest_row"], c.T * c.k)
+        t1 = time.perf_counter()
+        # the expert op sits between the two and is not part of a step
+        if c.ops == "combine":
+            y = y_fixed
+        elif c.expert == "scale":
+            y = oracle.expert_scale(recv, lay["offsets"], scales)
+        else:
+            y = recv
+        t2 = time.perf_counter()
+        oracle.combine(y, lay["dest_row"], wl.topk_w)
+        t3 = time.perf_counter()
+        t_total += (t1 - t0) + (t3 - t2)
+        passes += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    per_step = t_total / passes
+    b = algorithmic_bytes(c.T, c.H, c.k, c.E)
+    step_bytes = b["layout"] + b["combine"] + (b["dispatch"] if c.ops != "combine" else 0)
+    return {
+        "value": round(step_bytes / per_step / 1e9, 3),
+        "unit": "GB/s",
+        "tokens_per_s": round(c.T / per_step, 1),
+        "s_per_step": round(per_step, 4),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole {name} workload (T={c.T}), {passes} pass(es) of layout+dispatch+combine, "
+                  f"single-threaded numpy/Python",
+    }
+
+
+def sweep(path, name, steps, warmup):
+    """CU budget x variant over the workload, plus the streaming-probe ceilings."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    s = Setup(name)
+    budgets = [16, 24, 32, 64, 128, 256, 0]
+    variants = ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"]
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
+    bb = torch.empty_like(a)
+    with open(path, "a") as fh:
+        for budget in budgets:
+            ep.ep_set_num_cus(budget)
+            for mode, label in [(0, "copy"), (1, "read"), (2, "write")]:
+                for _ in range(3):
+                    ep.ep_bw_probe(mode, a, bb, n)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    ep.ep_bw_probe(mode, a, bb, n)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 10
+                moved = 2 * n if mode == 0 else n
+                rec = {"kind": "probe", "mode": label, "num_cus": budget, "ms": ms, "GBs": moved / ms / 1e6}
+                fh.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), flush=True)
+            for v in variants:
+                ep.ep_set_variant(v)
+                ms, per = s.run(steps, warmup)
+                rec = {"kind": "step", "workload": name, "variant": v, "num_cus": budget, "ms_per_step": ms,
+                       "kernel_ms": per,
+                       "GBs": {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}}
+                fh.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), flush=True)
+    ep.ep_set_num_cus(0)
+    ep.ep_set_variant("auto")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is a single-GPU kernel library with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    ep.lib()
+    if args.sweep:
+        sweep(args.sweep, args.workload, max(20, args.steps // 4), 5)
+        return
+
+    ep.ep_set_variant(args.variant)
+    s = Setup(args.workload)
+    results = {}
+    for label, budget in (("all", 0), (f"cu{args.budget}", args.budget)):
+        ep.ep_set_num_cus(budget)
+        ms, per = s.run(args.steps, args.warmup)
+        results[label] = (ms, per)
+    ep.ep_set_num_cus(0)
+
+    ms, per = results["all"]
+    value = s.step_bytes / (ms * 1e-3) / 1e9
+    kernels = ["dispatch", "combine"] if s.do_dispatch else ["combine"]
+    dom = max(kernels, key=lambda k: per[k])
+    achieved = s.bytes[dom] / (per[dom] * 1e-3) / 1e9
+    kname = {"dispatch": "ep_dispatch", "combine": "ep_combine"}[dom]
+    traffic = read_traffic(dom, args.workload)
+    ms_b, per_b = results[f"cu{args.budget}"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": s.T, "H": s.H, "E": s.E, "k": s.k, "num_cus": "all",
+                   "variant": ep.ep_get_variant(), "step": "layout+dispatch+combine"},
+        "tokens_per_s": round(s.T / (ms * 1e-3), 1),
+        "kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        "kernel_GBs": {k: round(s.bytes[k] / (per[k] * 1e6), 1) for k in per if per[k] > 0 and s.bytes[k]},
+        f"cu{args.budget}": {
+            "value": round(s.step_bytes / (ms_b * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(ms_b, 5),
+            "tokens_per_s": round(s.T / (ms_b * 1e-3), 1),
+            "kernel_ms": {k: round(v, 5) for k, v in per_b.items()},
+            "kernel_GBs": {k: round(s.bytes[k] / (per_b[k] * 1e6), 1) for k in per_b if per_b[k] > 0 and s.bytes[k]},
+        },
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": s.bytes[dom],
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

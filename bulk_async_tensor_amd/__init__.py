@@ -1,0 +1,235 @@
+"""Python binding of libep.so, the MI355X (gfx950) MoE row-movement library.
+
+Argument marshalling only: every step of layout, dispatch and combine runs in
+the library's HIP kernels.  torch provides device memory and the stream
+(``torch.cuda.current_stream()`` unless one is given).  The functions carry
+the names of the C entry points declared in ``include/ep.h``.
+
+There is no fallback: if ``libep.so`` is missing or cannot be loaded, every
+call raises ``EpLibraryMissing``.  Build it with
+``python -m bulk_async_tensor_amd.build``.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep.so")
+
+EP_OK = 0
+EP_ERR_INVALID_ARG = -1
+EP_ERR_ALIGNMENT = -2
+EP_ERR_UNSUPPORTED = -3
+EP_ERR_WORKSPACE = -4
+EP_ERR_HIP = -5
+EP_STATUS_EXPERT_OUT_OF_RANGE = 1
+EP_STATUS_DUPLICATE_EXPERT = 2
+EP_MAX_TOPK = 32
+EP_MAX_EXPERTS = 1024
+
+VARIANTS = ("auto", "vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached")
+
+_c_int, _c_i64, _c_sz, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes), mirroring include/ep.h
+_SIGNATURES = {
+    "ep_set_num_cus": (_c_int, [_c_int]),
+    "ep_get_num_cus": (_c_int, []),
+    "ep_set_variant": (_c_int, [ctypes.c_char_p]),
+    "ep_get_variant": (ctypes.c_char_p, []),
+    "ep_layout_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "ep_layout": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p]),
+    "ep_dispatch": (_c_int, [_p, _c_int, _c_int, _p, _c_int, _p, _c_i64, _p]),
+    "ep_combine": (_c_int, [_p, _c_i64, _c_int, _p, _p, _c_int, _c_int, _p, _p]),
+    "ep_status_string": (ctypes.c_char_p, [_c_int]),
+    "ep_last_error": (ctypes.c_char_p, []),
+    "ep_bw_probe": (_c_int, [_c_int, _p, _p, _c_i64, _p]),
+    "ep_probe_placement": (_c_int, [_p, _c_int, _p]),
+}
+
+
+class EpLibraryMissing(RuntimeError):
+    pass
+
+
+class EpError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{message} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libep.so (raises EpLibraryMissing when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise EpLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m bulk_async_tensor_amd.build` (hipcc, gfx950)"
+            )
+        try:
+            handle = ctypes.CDLL(LIB_PATH)
+        except OSError as exc:  # pragma: no cover - depends on the machine
+            raise EpLibraryMissing(f"cannot load {LIB_PATH}: {exc}") from exc
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(rc, what):
+    if rc < 0:
+        detail = lib().ep_last_error().decode()
+        raise EpError(rc, f"{what}: {detail or lib().ep_status_string(rc).decode()}")
+    return rc
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _device_tensor(t, name, dtype=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ------------------------------------------------------------------ settings
+def ep_set_num_cus(n):
+    return _check(lib().ep_set_num_cus(int(n)), "ep_set_num_cus")
+
+
+def ep_get_num_cus():
+    return lib().ep_get_num_cus()
+
+
+def ep_set_variant(name):
+    return _check(lib().ep_set_variant(name.encode()), "ep_set_variant")
+
+
+def ep_get_variant():
+    return lib().ep_get_variant().decode()
+
+
+def ep_layout_workspace_bytes(T, k, E):
+    return lib().ep_layout_workspace_bytes(int(T), int(k), int(E))
+
+
+def ep_status_string(code):
+    return lib().ep_status_string(int(code)).decode()
+
+
+def ep_last_error():
+    return lib().ep_last_error().decode()
+
+
+# ------------------------------------------------------------------ hot path
+def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, src_token=None, status=None,
+              workspace=None, stream=None):
+    """Per-expert counts, offsets and stable destination rows of topk_idx [T, k] (int32).
+
+    Missing outputs are allocated with torch on the input's device.  Returns a
+    dict of the output tensors (``status`` is a 1-element int32 tensor).
+    """
+    import torch
+
+    _device_tensor(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    dev = topk_idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = torch.empty(E, **i32) if counts is None else _device_tensor(counts, "counts", torch.int32)
+    offsets = torch.empty(E + 1, **i32) if offsets is None else _device_tensor(offsets, "offsets", torch.int32)
+    dest_row = torch.empty((T, k), **i32) if dest_row is None else _device_tensor(dest_row, "dest_row", torch.int32)
+    if src_token is None:
+        src_token = torch.empty(T * k, **i32)
+    else:
+        _device_tensor(src_token, "src_token", torch.int32)
+    status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
+    need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(
+        lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
+                        _ptr(status), _ptr(workspace), ws_bytes, _stream(stream)),
+        "ep_layout",
+    )
+    return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
+
+
+def ep_dispatch(x, dest_row, recv, stream=None):
+    """recv[dest_row[t, j]] = x[t] for x [T, H] bf16, dest_row [T, k] int32, recv [R, H] bf16."""
+    import torch
+
+    _device_tensor(x, "x", torch.bfloat16)
+    _device_tensor(dest_row, "dest_row", torch.int32)
+    _device_tensor(recv, "recv", torch.bfloat16)
+    T, H = x.shape
+    if dest_row.dim() != 2 or dest_row.shape[0] != T:
+        raise ValueError("dest_row must be [T, k]")
+    if recv.dim() != 2 or recv.shape[1] != H:
+        raise ValueError("recv must be [R, H]")
+    k = dest_row.shape[1]
+    _check(lib().ep_dispatch(_ptr(x), T, H, _ptr(dest_row), k, _ptr(recv), recv.shape[0], _stream(stream)),
+           "ep_dispatch")
+    return recv
+
+
+def ep_combine(y, dest_row, topk_w, out, stream=None):
+    """out[t] = bf16(sum_j w[t, j] * y[dest_row[t, j]]) for y [R, H] bf16, out [T, H] bf16."""
+    import torch
+
+    _device_tensor(y, "y", torch.bfloat16)
+    _device_tensor(dest_row, "dest_row", torch.int32)
+    _device_tensor(topk_w, "topk_w", torch.float32)
+    _device_tensor(out, "out", torch.bfloat16)
+    T, H = out.shape
+    if dest_row.dim() != 2 or dest_row.shape[0] != T or tuple(topk_w.shape) != tuple(dest_row.shape):
+        raise ValueError("dest_row and topk_w must both be [T, k]")
+    if y.dim() != 2 or y.shape[1] != H:
+        raise ValueError("y must be [R, H]")
+    k = dest_row.shape[1]
+    _check(lib().ep_combine(_ptr(y), y.shape[0], H, _ptr(dest_row), _ptr(topk_w), T, k, _ptr(out),
+                            _stream(stream)), "ep_combine")
+    return out
+
+
+# ------------------------------------------------------------------ probes
+def ep_bw_probe(mode, src, dst, nbytes, stream=None):
+    """Streaming probe under the current CU budget (0 copy, 1 read, 2 write)."""
+    return _check(lib().ep_bw_probe(int(mode), _ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "ep_bw_probe")
+
+
+def ep_probe_placement(out, n_groups, stream=None):
+    """Writes {XCC, SE, (SH<<4)|CU, raw HW_ID} per workgroup into out (int32 [n_groups, 4])."""
+    import torch
+
+    _device_tensor(out, "out", torch.int32)
+    if out.numel() < 4 * n_groups:
+        raise ValueError("out must hold 4 * n_groups int32")
+    return _check(lib().ep_probe_placement(_ptr(out), int(n_groups), _stream(stream)), "ep_probe_placement")
+
+
+__all__ = [n for n in list(globals()) if n.startswith("ep_") or n.startswith("EP_")] + [
+    "lib", "LIB_PATH", "VARIANTS", "EpError", "EpLibraryMissing",
+]

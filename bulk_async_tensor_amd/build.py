@@ -1,0 +1,76 @@
+"""Build libep.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Usage: ``python -m bulk_async_tensor_amd.build`` or ``build()`` from Python.
+Objects go to ``bulk_async_tensor_amd/_build/``; the library is written to
+``bulk_async_tensor_amd/libep.so``.  Every call recompiles.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libep.so")
+SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "probe.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else (shutil.which("hipcc") or "hipcc")
+
+
+def common_flags():
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-ffp-contract=off",
+        # packed fp32 instructions stay off (hipcc's host pass warns it does
+        # not know the feature; the warning is harmless)
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall",
+        "-Wno-unused-command-line-argument",
+        f"-I{INCLUDE}",
+        f"-I{CSRC}",
+    ]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    return obj, res.stderr
+
+
+def build(verbose=False, jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        results = list(pool.map(_compile, SOURCES))
+    objs = [r[0] for r in results]
+    if verbose:
+        for _, err in results:
+            if err.strip():
+                print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

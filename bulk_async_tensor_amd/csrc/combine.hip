@@ -1,0 +1,420 @@
+// ep_combine: out[t, :] = bf16_rne( sum_{j<k} w[t, j] * f32(y[dest_row[t, j], :]) )
+//
+// The way back from the expert-grouped layout.  The pages show only the
+// dispatch direction; the combine here is its inverse gather, weighted by the
+// gate weights that the dispatch call of [DeepEP-TMA] ("High-Level DeepEP API
+// Usage") takes alongside the expert ids.  Accumulation is fp32 from +0.0 in
+// slot order with every product and sum rounded separately (contraction into
+// fused multiply-add is switched off), then one round-to-nearest-even to
+// bf16 with the hardware pack instruction.
+//
+// A work unit is (token, slab); the k source rows of the slab are gathered
+// with 16-byte loads.  Variants mirror the dispatch kernels:
+//   vgpr   all k x VPL loads of a unit issued together into registers;
+//   vgpr2  two register sets: the next unit's k rows load while the current
+//          one is summed and stored;
+//   lds1   k rows land in a per-wave LDS slice by direct-to-LDS loads, one
+//          stage;
+//   lds2   two stages: the next unit's direct-to-LDS loads are in flight while
+//          the current stage is read, summed and stored.
+// The k destination rows and weights of a unit are fetched with scalar loads
+// before its first row load.  EVEN = the row is a whole number of KiB, so no
+// per-lane row-end masks are needed.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+
+namespace ep {
+
+namespace {
+
+struct Unit {
+  int64_t t;
+  int c0;    // this lane's first vector of the slab
+  int nvec;  // vectors of the slab inside the row (uniform, >= 1)
+};
+
+template <int VPL>
+__device__ __forceinline__ Unit unit_of(int u, int nslab, int row_vec, int lane) {
+  Unit r;
+  const int t = u / nslab;
+  const int s = u - t * nslab;
+  const int first = s * (VPL * kWave);
+  r.t = t;
+  r.c0 = first + lane;
+  const int left = (row_vec - first + kWave - 1) / kWave;
+  r.nvec = left < VPL ? left : VPL;
+  return r;
+}
+
+__device__ __forceinline__ bool row_ok(int64_t d, int64_t rows) { return (uint64_t)d < (uint64_t)rows; }
+
+// Routing of one token: destination rows and gate weights of its k slots.
+template <int K>
+struct Slots {
+  int32_t d[K];
+  float w[K];
+};
+
+template <int K>
+__device__ __forceinline__ void fetch_slots(Slots<K>& s, const int32_t* __restrict__ dr, const float* __restrict__ wr) {
+#pragma unroll
+  for (int j = 0; j < K; ++j) s.d[j] = dr[j];
+#pragma unroll
+  for (int j = 0; j < K; ++j) s.w[j] = wr[j];
+}
+
+// acc += w * f32(v) for the 8 bf16 of each vector; no contraction.
+template <int VPL>
+__device__ __forceinline__ void accumulate(float (&acc)[VPL][8], const u32x4 (&v)[VPL], float w, int nvec) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < nvec) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p0 = w * bf16_lo(v[i][q]);
+        const float p1 = w * bf16_hi(v[i][q]);
+        acc[i][2 * q] = acc[i][2 * q] + p0;
+        acc[i][2 * q + 1] = acc[i][2 * q + 1] + p1;
+      }
+    }
+  }
+}
+
+template <int VPL>
+__device__ __forceinline__ void zero(float (&acc)[VPL][8]) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+}
+
+// Writes the slab; returns the number of store instructions issued (lane 0
+// is inside the row for every vector < nvec, so none is skipped).
+template <int VPL, bool EVEN, bool NT>
+__device__ __forceinline__ int store_out(u32x4* __restrict__ dst, const float (&acc)[VPL][8], const Unit& un,
+                                         int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+        st16<NT>(dst + c, o);
+      }
+    }
+  }
+  return un.nvec;
+}
+
+template <int VPL, bool EVEN, bool NT>
+__device__ __forceinline__ void load_slab(u32x4 (&v)[VPL], const u32x4* __restrict__ src, const Unit& un,
+                                          int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) v[i] = ld16<NT>(src + c);
+    }
+  }
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__device__ __forceinline__ void load_unit(u32x4 (&v)[K][VPL], const Slots<K>& s, const u32x4* __restrict__ y,
+                                          int64_t recv_rows, const Unit& un, int row_vec) {
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (row_ok(s.d[j], recv_rows)) load_slab<VPL, EVEN, NT>(v[j], y + (int64_t)s.d[j] * row_vec, un, row_vec);
+}
+
+template <int VPL, int K>
+__device__ __forceinline__ void sum_unit(float (&acc)[VPL][8], const u32x4 (&v)[K][VPL], const Slots<K>& s,
+                                         int64_t recv_rows, int nvec) {
+  zero<VPL>(acc);
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (row_ok(s.d[j], recv_rows)) accumulate<VPL>(acc, v[j], s.w[j], nvec);
+}
+
+#define EP_COMBINE_ARGS                                                                                        \
+  const u32x4 *__restrict__ y, u32x4 *__restrict__ out, const int32_t *__restrict__ dest_row,                 \
+      const float *__restrict__ w, int64_t recv_rows, int row_vec, int nslab, int k_rt, int units
+
+// Compile-time k: all k x VPL loads of a unit in flight together.
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void combine_vgpr_kernel(EP_COMBINE_ARGS) {
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  for (int u = blockIdx.x * wpg + wave_in_group(); u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);
+    Slots<K> s;
+    fetch_slots<K>(s, dest_row + un.t * K, w + un.t * K);
+    u32x4 v[K][VPL];
+    load_unit<VPL, K, EVEN, NT>(v, s, y, recv_rows, un, row_vec);
+    float acc[VPL][8];
+    sum_unit<VPL, K>(acc, v, s, recv_rows, un.nvec);
+    store_out<VPL, EVEN, NT>(out + un.t * row_vec, acc, un, row_vec);
+  }
+}
+
+// Any k: slots in batches of 8 whose loads are in flight together.
+template <int VPL, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void combine_vgpr_any_kernel(EP_COMBINE_ARGS) {
+  constexpr int KB = 8;
+  const int k = k_rt;
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  for (int u = blockIdx.x * wpg + wave_in_group(); u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);
+    const int32_t* dr = dest_row + un.t * k;
+    const float* wr = w + un.t * k;
+    float acc[VPL][8];
+    zero<VPL>(acc);
+    for (int jb = 0; jb < k; jb += KB) {
+      u32x4 v[KB][VPL];
+      int64_t d[KB];
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) d[jj] = (jb + jj < k) ? (int64_t)dr[jb + jj] : -1;
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj)
+        if (row_ok(d[jj], recv_rows)) load_slab<VPL, EVEN, NT>(v[jj], y + d[jj] * row_vec, un, row_vec);
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj)
+        if (row_ok(d[jj], recv_rows)) accumulate<VPL>(acc, v[jj], wr[jb + jj], un.nvec);
+    }
+    store_out<VPL, EVEN, NT>(out + un.t * row_vec, acc, un, row_vec);
+  }
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void combine_vgpr2_kernel(EP_COMBINE_ARGS) {
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  int u = blockIdx.x * wpg + wave_in_group();
+  if (u >= units) return;
+  Unit cur = unit_of<VPL>(u, nslab, row_vec, lane);
+  Slots<K> sa, sb;
+  fetch_slots<K>(sa, dest_row + cur.t * K, w + cur.t * K);
+  u32x4 a[K][VPL], b[K][VPL];
+  float acc[VPL][8];
+  load_unit<VPL, K, EVEN, NT>(a, sa, y, recv_rows, cur, row_vec);
+  for (;;) {
+    // two units per trip so that the register sets swap roles without moves
+    int un = u + stride;
+    Unit nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (un < units) {
+      fetch_slots<K>(sb, dest_row + nxt.t * K, w + nxt.t * K);
+      load_unit<VPL, K, EVEN, NT>(b, sb, y, recv_rows, nxt, row_vec);
+    }
+    sum_unit<VPL, K>(acc, a, sa, recv_rows, cur.nvec);
+    store_out<VPL, EVEN, NT>(out + cur.t * row_vec, acc, cur, row_vec);
+    if (un >= units) break;
+    u = un;
+    cur = nxt;
+    un = u + stride;
+    nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (un < units) {
+      fetch_slots<K>(sa, dest_row + nxt.t * K, w + nxt.t * K);
+      load_unit<VPL, K, EVEN, NT>(a, sa, y, recv_rows, nxt, row_vec);
+    }
+    sum_unit<VPL, K>(acc, b, sb, recv_rows, cur.nvec);
+    store_out<VPL, EVEN, NT>(out + cur.t * row_vec, acc, cur, row_vec);
+    if (un >= units) break;
+    u = un;
+    cur = nxt;
+  }
+}
+
+// Stage layout: slot j, vector i at stage + (j * VPL + i) KiB, lane L at +16 L.
+template <int VPL, int K, bool EVEN>
+__device__ __forceinline__ void dma_unit(char* stage, const Slots<K>& s, const u32x4* __restrict__ y,
+                                         int64_t recv_rows, const Unit& un, int row_vec) {
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (row_ok(s.d[j], recv_rows)) {
+      const u32x4* src = y + (int64_t)s.d[j] * row_vec;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        if (i < un.nvec) {
+          const int c = un.c0 + i * kWave;
+          if (EVEN || c < row_vec) dma16(src + c, (lds_void_t*)(stage + (j * VPL + i) * kWaveVecBytes));
+        }
+      }
+    }
+  }
+}
+
+// Reads the whole stage (slots that were not filled hold stale bytes of this
+// wave's own slice and are never summed): unconditional reads keep the
+// register allocation simple.
+template <int VPL, int K>
+__device__ __forceinline__ void read_unit(u32x4 (&v)[K][VPL], const char* stage, int lane) {
+  const uint32_t base = lds_addr_of(stage) + lane * kVecBytes;
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) lds_read16_async(v[j][i], base + (j * VPL + i) * kWaveVecBytes);
+  lds_wait_all();
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) lds_fence_value(v[j][i]);
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void combine_lds1_kernel(EP_COMBINE_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  char* stage = lds + wave * (K * VPL * kWaveVecBytes);
+  for (int u = blockIdx.x * wpg + wave; u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);
+    Slots<K> s;
+    fetch_slots<K>(s, dest_row + un.t * K, w + un.t * K);
+    dma_unit<VPL, K, EVEN>(stage, s, y, recv_rows, un, row_vec);
+    wait_vmcnt<0>();
+    u32x4 v[K][VPL];
+    read_unit<VPL, K>(v, stage, lane);
+    float acc[VPL][8];
+    sum_unit<VPL, K>(acc, v, s, recv_rows, un.nvec);
+    store_out<VPL, EVEN, NT>(out + un.t * row_vec, acc, un, row_vec);
+  }
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void combine_lds2_kernel(EP_COMBINE_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kStageBytes = K * VPL * kWaveVecBytes;
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  char* ring = lds + wave * (2 * kStageBytes);
+  int u = blockIdx.x * wpg + wave;
+  if (u >= units) return;
+  Unit cur = unit_of<VPL>(u, nslab, row_vec, lane);
+  Slots<K> scur, snxt;
+  fetch_slots<K>(scur, dest_row + cur.t * K, w + cur.t * K);
+  dma_unit<VPL, K, EVEN>(ring, scur, y, recv_rows, cur, row_vec);
+  int stage = 0;
+  int issued_after = 0;  // vector-memory instructions issued after the pending fill of `stage`
+  for (;;) {
+    // vmcnt retires in issue order: letting at most `issued_after` newer
+    // operations (the previous unit's output stores) stay outstanding is exact
+    if (issued_after >= VPL) wait_vmcnt<VPL>();
+    else wait_vmcnt<0>();
+    u32x4 v[K][VPL];
+    read_unit<VPL, K>(v, ring + stage * kStageBytes, lane);  // stage is free again
+    const int un = u + stride;
+    const bool more = un < units;
+    const Unit nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (more) {
+      fetch_slots<K>(snxt, dest_row + nxt.t * K, w + nxt.t * K);
+      dma_unit<VPL, K, EVEN>(ring + (stage ^ 1) * kStageBytes, snxt, y, recv_rows, nxt, row_vec);
+    }
+    float acc[VPL][8];
+    sum_unit<VPL, K>(acc, v, scur, recv_rows, cur.nvec);
+    issued_after = store_out<VPL, EVEN, NT>(out + cur.t * row_vec, acc, cur, row_vec);
+    if (!more) break;
+    u = un;
+    cur = nxt;
+    scur = snxt;
+    stage ^= 1;
+  }
+}
+
+using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);
+
+template <int VPL, int K, bool EVEN>
+CombineFn pick_kind(Variant v) {
+  switch (v) {
+    case Variant::Vgpr: return combine_vgpr_kernel<VPL, K, EVEN, true>;
+    case Variant::VgprCached: return combine_vgpr_kernel<VPL, K, EVEN, false>;
+    default: break;
+  }
+  if constexpr (VPL == 1) {
+    switch (v) {
+      case Variant::Vgpr2: return combine_vgpr2_kernel<VPL, K, EVEN, true>;
+      case Variant::Lds1: return combine_lds1_kernel<VPL, K, EVEN, true>;
+      case Variant::Lds2: return combine_lds2_kernel<VPL, K, EVEN, true>;
+      default: break;
+    }
+  }
+  return nullptr;
+}
+
+template <int VPL, bool EVEN>
+CombineFn pick_k(Variant v, int k) {
+  switch (k) {
+    case 2: return pick_kind<VPL, 2, EVEN>(v);
+    case 4: return pick_kind<VPL, 4, EVEN>(v);
+    case 6: return pick_kind<VPL, 6, EVEN>(v);
+    case 8: return pick_kind<VPL, 8, EVEN>(v);
+    default: return combine_vgpr_any_kernel<VPL, EVEN, true>;
+  }
+}
+
+template <bool EVEN>
+CombineFn pick_vpl(Variant v, int vpl, int k) {
+  switch (vpl) {
+    case 1: return pick_k<1, EVEN>(v, k);
+    default: return pick_k<2, EVEN>(v, k);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
+                          const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream) {
+  if (v == Variant::Auto) v = Variant::Vgpr;
+  const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
+  if (!known_k) v = Variant::Vgpr;  // the any-k kernel
+  const int row_vec = H / 8;
+  const bool even = row_vec % kWave == 0;
+  // in-flight registers grow as k x VPL: two vectors per lane per slot for
+  // the single-set kernel, one for the double-buffered and LDS ones
+  int vpl = (v == Variant::Vgpr || v == Variant::VgprCached) ? 2 : 1;
+  if (row_vec <= kWave) vpl = 1;
+  const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
+  if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
+  const int units = T * nslab;
+  CombineFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
+  if (!fn) return hipErrorInvalidValue;
+
+  const bool lds = (v == Variant::Lds1 || v == Variant::Lds2);
+  const size_t per_wave = lds ? (size_t)(v == Variant::Lds2 ? 2 : 1) * k * vpl * kWaveVecBytes : 0;
+  int wpg, grid;
+  size_t lds_bytes;
+  if (b.num_cus > 0) {
+    wpg = 16;
+    if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
+    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    lds_bytes = per_wave * wpg;
+    if (lds_bytes < kExclusiveLds) lds_bytes = kExclusiveLds;
+  } else {
+    wpg = 4;
+    int per_cu = per_wave ? (int)(kLdsPerCu / (per_wave * wpg)) : 8;
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    grid = (units + wpg - 1) / wpg;
+    if (grid > b.device_cus * per_cu) grid = b.device_cus * per_cu;
+    lds_bytes = per_wave * wpg;
+  }
+  if (grid < 1) grid = 1;
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(y),
+                     static_cast<u32x4*>(out), dest_row, w, recv_rows, row_vec, nslab, k, units);
+  return hipGetLastError();
+}
+
+}  // namespace ep

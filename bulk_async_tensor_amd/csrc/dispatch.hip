@@ -1,0 +1,365 @@
+// ep_dispatch: recv[dest_row[t, j], :] = x[t, :] -- every token row is read
+// from HBM once and written to its k destinations.
+//
+// This is the receive-side row copy of [DeepEP-TMA] section "Asynchronous
+// Copy Primitives" re-thought for CDNA4.  There, one elected lane per warp
+// hands a half row to the bulk-copy engine, waits on a transaction barrier
+// and hands the shared-memory slice back for the store.  gfx950 has no
+// bulk-copy engine: the wave itself is the issuing unit, and one wave
+// instruction moves 1 KiB (64 lanes x 16 bytes).  The kernels differ in where
+// a row waits between its load and its k stores:
+//
+//   vgpr   registers: VPL dwordx4 loads, then k x VPL dwordx4 stores;
+//   vgpr2  registers, two sets: the next unit's loads are issued before the
+//          current unit's stores;
+//   lds1   a per-wave LDS slice filled by direct-to-LDS loads
+//          (global_load_lds_dwordx4, no VGPR staging), one stage: load, wait,
+//          read the slice, store -- the single-slice loop of the pages;
+//   lds2   the same slice doubled: the next unit's direct-to-LDS load is in
+//          flight while the current one is read out and stored.
+//
+// A work unit is (token, slab), a slab being up to VPL x 64 16-byte vectors
+// of the row (VPL KiB).  Waves take units round-robin; wave-uniform values
+// (unit, token, destination rows) live in SGPRs, and the k destination rows
+// of a unit are fetched with one scalar load before its first store.
+// EVEN = the row is a whole number of KiB, so no lane ever falls off the row
+// end and no per-lane masks are needed.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+
+namespace ep {
+
+namespace {
+
+struct Unit {
+  int64_t t;
+  int c0;    // this lane's first vector of the slab
+  int nvec;  // vectors of the slab inside the row (uniform, >= 1)
+};
+
+template <int VPL>
+__device__ __forceinline__ Unit unit_of(int u, int nslab, int row_vec, int lane) {
+  Unit r;
+  const int t = u / nslab;
+  const int s = u - t * nslab;
+  const int first = s * (VPL * kWave);
+  r.t = t;
+  r.c0 = first + lane;
+  const int left = (row_vec - first + kWave - 1) / kWave;
+  r.nvec = left < VPL ? left : VPL;
+  return r;
+}
+
+template <int K>
+struct Dests {
+  int32_t d[K > 0 ? K : 1];
+};
+
+template <int K>
+__device__ __forceinline__ void fetch_dests(Dests<K>& ds, const int32_t* __restrict__ dr) {
+  if constexpr (K > 0) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) ds.d[j] = dr[j];
+  }
+}
+
+template <int VPL, bool EVEN, bool NT>
+__device__ __forceinline__ void load_slab(u32x4 (&v)[VPL], const u32x4* __restrict__ src, const Unit& un,
+                                          int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) v[i] = ld16<NT>(src + c);
+    }
+  }
+}
+
+template <int VPL, bool EVEN, bool NT>
+__device__ __forceinline__ void store_one(const u32x4 (&v)[VPL], u32x4* __restrict__ dst, const Unit& un,
+                                          int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) st16<NT>(dst + c, v[i]);
+    }
+  }
+}
+
+// Stores of one slab to its destinations.  Returns the number of store
+// instructions issued (valid destinations x vectors; lane 0 is inside the
+// row for every vector < nvec, so none is skipped), which bounds the
+// completion wait of the two-stage ring.
+template <int VPL, int K, bool EVEN, bool NT>
+__device__ __forceinline__ int store_slab(const u32x4 (&v)[VPL], u32x4* __restrict__ recv, const Dests<K>& ds,
+                                          const int32_t* __restrict__ dr, int k, int64_t recv_rows, const Unit& un,
+                                          int row_vec) {
+  int ndest = 0;
+  if constexpr (K > 0) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t d = ds.d[j];
+      if ((uint64_t)d < (uint64_t)recv_rows) {
+        ++ndest;
+        store_one<VPL, EVEN, NT>(v, recv + d * row_vec, un, row_vec);
+      }
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int64_t d = dr[j];
+      if ((uint64_t)d < (uint64_t)recv_rows) {
+        ++ndest;
+        store_one<VPL, EVEN, NT>(v, recv + d * row_vec, un, row_vec);
+      }
+    }
+  }
+  return ndest * un.nvec;
+}
+
+#define EP_DISPATCH_ARGS                                                                                     \
+  const u32x4 *__restrict__ x, u32x4 *__restrict__ recv, const int32_t *__restrict__ dest_row, int64_t recv_rows, \
+      int row_vec, int nslab, int k_rt, int units
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_vgpr_kernel(EP_DISPATCH_ARGS) {
+  const int k = K > 0 ? K : k_rt;
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  for (int u = blockIdx.x * wpg + wave_in_group(); u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);
+    const int32_t* dr = dest_row + un.t * k;
+    Dests<K> ds;
+    fetch_dests<K>(ds, dr);
+    u32x4 v[VPL];
+    load_slab<VPL, EVEN, NT>(v, x + un.t * row_vec, un, row_vec);
+    store_slab<VPL, K, EVEN, NT>(v, recv, ds, dr, k, recv_rows, un, row_vec);
+  }
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) {
+  const int k = K > 0 ? K : k_rt;
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  int u = blockIdx.x * wpg + wave_in_group();
+  if (u >= units) return;
+  Unit cur = unit_of<VPL>(u, nslab, row_vec, lane);
+  Dests<K> dcur, dnxt;
+  fetch_dests<K>(dcur, dest_row + cur.t * k);
+  u32x4 a[VPL], b[VPL];
+  load_slab<VPL, EVEN, NT>(a, x + cur.t * row_vec, cur, row_vec);
+  for (;;) {
+    // two units per trip so that the register sets swap roles without moves
+    int un = u + stride;
+    Unit nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (un < units) {
+      fetch_dests<K>(dnxt, dest_row + nxt.t * k);
+      load_slab<VPL, EVEN, NT>(b, x + nxt.t * row_vec, nxt, row_vec);
+    }
+    store_slab<VPL, K, EVEN, NT>(a, recv, dcur, dest_row + cur.t * k, k, recv_rows, cur, row_vec);
+    if (un >= units) break;
+    u = un;
+    cur = nxt;
+    un = u + stride;
+    nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (un < units) {
+      fetch_dests<K>(dcur, dest_row + nxt.t * k);
+      load_slab<VPL, EVEN, NT>(a, x + nxt.t * row_vec, nxt, row_vec);
+    }
+    store_slab<VPL, K, EVEN, NT>(b, recv, dnxt, dest_row + cur.t * k, k, recv_rows, cur, row_vec);
+    if (un >= units) break;
+    u = un;
+    cur = nxt;
+  }
+}
+
+// Direct-to-LDS fill of one slab: instruction i moves vector i of every lane
+// into slice + i KiB.  Every instruction with i < nvec is issued.
+template <int VPL, bool EVEN>
+__device__ __forceinline__ void dma_slab(const u32x4* __restrict__ src, char* slice, const Unit& un, int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) dma16(src + c, (lds_void_t*)(slice + i * kWaveVecBytes));
+    }
+  }
+}
+
+// Reads the whole slice (vectors past the slab hold stale bytes of this wave's
+// own slice and are never stored): unconditional reads keep the register
+// allocation simple.
+template <int VPL>
+__device__ __forceinline__ void read_slab(u32x4 (&v)[VPL], const char* slice, int lane) {
+  const uint32_t base = lds_addr_of(slice) + lane * kVecBytes;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) lds_read16_async(v[i], base + i * kWaveVecBytes);
+  lds_wait_all();
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) lds_fence_value(v[i]);
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_lds1_kernel(EP_DISPATCH_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int k = K > 0 ? K : k_rt;
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  char* slice = lds + wave * (VPL * kWaveVecBytes);
+  for (int u = blockIdx.x * wpg + wave; u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);
+    const int32_t* dr = dest_row + un.t * k;
+    Dests<K> ds;
+    fetch_dests<K>(ds, dr);
+    dma_slab<VPL, EVEN>(x + un.t * row_vec, slice, un, row_vec);
+    wait_vmcnt<0>();  // slice filled (this also drains the previous unit's stores)
+    u32x4 v[VPL];
+    read_slab<VPL>(v, slice, lane);
+    store_slab<VPL, K, EVEN, NT>(v, recv, ds, dr, k, recv_rows, un, row_vec);
+  }
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_lds2_kernel(EP_DISPATCH_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  static_assert(K > 0, "the two-stage ring needs a compile-time k for its wait counts");
+  // stores issued after a stage's fill when the previous unit was complete
+  constexpr int kFullStores = (K * VPL) < 63 ? (K * VPL) : 63;
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  char* ring = lds + wave * (2 * VPL * kWaveVecBytes);
+  int u = blockIdx.x * wpg + wave;
+  if (u >= units) return;
+  Unit cur = unit_of<VPL>(u, nslab, row_vec, lane);
+  Dests<K> dcur, dnxt;
+  fetch_dests<K>(dcur, dest_row + cur.t * K);
+  dma_slab<VPL, EVEN>(x + cur.t * row_vec, ring, cur, row_vec);
+  int stage = 0;
+  int issued_after = 0;  // vector-memory instructions issued after the pending fill of `stage`
+  for (;;) {
+    // wait for the fill of `stage`: vmcnt retires in issue order, so letting
+    // at most `issued_after` newer operations stay outstanding is exact
+    if (issued_after >= kFullStores) wait_vmcnt<kFullStores>();
+    else wait_vmcnt<0>();
+    u32x4 v[VPL];
+    read_slab<VPL>(v, ring + stage * (VPL * kWaveVecBytes), lane);  // stage is free again
+    const int un = u + stride;
+    const bool more = un < units;
+    const Unit nxt = unit_of<VPL>(un, nslab, row_vec, lane);
+    if (more) {
+      fetch_dests<K>(dnxt, dest_row + nxt.t * K);
+      dma_slab<VPL, EVEN>(x + nxt.t * row_vec, ring + (stage ^ 1) * (VPL * kWaveVecBytes), nxt, row_vec);
+    }
+    issued_after = store_slab<VPL, K, EVEN, NT>(v, recv, dcur, nullptr, K, recv_rows, cur, row_vec);
+    if (!more) break;
+    u = un;
+    cur = nxt;
+    dcur = dnxt;
+    stage ^= 1;
+  }
+}
+
+using DispatchFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, int, int, int);
+
+template <int VPL, int K, bool EVEN>
+DispatchFn pick_kind(Variant v) {
+  switch (v) {
+    case Variant::Vgpr: return dispatch_vgpr_kernel<VPL, K, EVEN, true>;
+    case Variant::VgprCached: return dispatch_vgpr_kernel<VPL, K, EVEN, false>;
+    case Variant::Vgpr2: return dispatch_vgpr2_kernel<VPL, K, EVEN, true>;
+    case Variant::Lds1: return dispatch_lds1_kernel<VPL, K, EVEN, true>;
+    case Variant::Lds2:
+      if constexpr (K > 0) return dispatch_lds2_kernel<VPL, K, EVEN, true>;
+      else return nullptr;
+    default: return nullptr;
+  }
+}
+
+template <int VPL, bool EVEN>
+DispatchFn pick_k(Variant v, int k) {
+  switch (k) {
+    case 2: return pick_kind<VPL, 2, EVEN>(v);
+    case 4: return pick_kind<VPL, 4, EVEN>(v);
+    case 6: return pick_kind<VPL, 6, EVEN>(v);
+    case 8: return pick_kind<VPL, 8, EVEN>(v);
+    default: return pick_kind<VPL, 0, EVEN>(v);
+  }
+}
+
+template <bool EVEN>
+DispatchFn pick_vpl(Variant v, int vpl, int k) {
+  switch (vpl) {
+    case 2: return pick_k<2, EVEN>(v, k);
+    case 4: return pick_k<4, EVEN>(v, k);
+    case 7: return pick_k<7, EVEN>(v, k);
+    default: return pick_k<8, EVEN>(v, k);
+  }
+}
+
+// Vectors per lane per slab: the whole row when it is at most 8 KiB, else
+// 8 or 7 when either splits the row evenly (7 gives the half rows of
+// H = 7168), else 8 with a ragged last slab.
+int choose_vpl(int row_vec) {
+  const int vpr = (row_vec + kWave - 1) / kWave;
+  if (vpr <= 2) return 2;
+  if (vpr <= 4) return 4;
+  if (vpr <= 8) return vpr == 7 ? 7 : 8;
+  if (vpr % 8 == 0) return 8;
+  if (vpr % 7 == 0) return 7;
+  return 8;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
+                           void* recv, int64_t recv_rows, hipStream_t stream) {
+  if (v == Variant::Auto) v = Variant::Vgpr;
+  const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
+  if (v == Variant::Lds2 && !known_k) v = Variant::Lds1;
+  const int row_vec = H / 8;
+  const bool even = row_vec % kWave == 0;
+  const int vpl = choose_vpl(row_vec);
+  const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
+  if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
+  const int units = T * nslab;
+  DispatchFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
+  if (!fn) return hipErrorInvalidValue;
+
+  const bool lds = (v == Variant::Lds1 || v == Variant::Lds2);
+  const size_t per_wave = lds ? (size_t)(v == Variant::Lds2 ? 2 : 1) * vpl * kWaveVecBytes : 0;
+  int wpg, grid;
+  size_t lds_bytes;
+  if (b.num_cus > 0) {
+    // persistent: one workgroup per CU, as many waves as the LDS ring allows
+    wpg = 16;
+    if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
+    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    lds_bytes = per_wave * wpg;
+    if (lds_bytes < kExclusiveLds) lds_bytes = kExclusiveLds;
+  } else {
+    wpg = 4;
+    int per_cu = per_wave ? (int)(kLdsPerCu / (per_wave * wpg)) : 8;
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    grid = (units + wpg - 1) / wpg;
+    if (grid > b.device_cus * per_cu) grid = b.device_cus * per_cu;
+    lds_bytes = per_wave * wpg;
+  }
+  if (grid < 1) grid = 1;
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x),
+                     static_cast<u32x4*>(recv), dest_row, recv_rows, row_vec, nslab, k, units);
+  return hipGetLastError();
+}
+
+}  // namespace ep

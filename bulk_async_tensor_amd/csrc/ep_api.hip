@@ -1,0 +1,261 @@
+// C ABI of libep.so: argument validation, the process-wide compute-unit
+// budget and variant, per-device attributes, and launches on the caller's
+// stream.  Every host-detectable error is reported before any HIP call is
+// made, so argument checks run on machines without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "ep.h"
+#include "ep_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_num_cus{-1};  // -1: not read from the environment yet
+std::atomic<int> g_variant{static_cast<int>(ep::Variant::Auto)};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(EP_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int num_cus_setting() {
+  int v = g_num_cus.load();
+  if (v < 0) {
+    const char* env = getenv("EP_NUM_CUS");
+    int n = env ? atoi(env) : 0;
+    if (n < 0) n = 0;
+    int expected = -1;
+    g_num_cus.compare_exchange_strong(expected, n);
+    v = g_num_cus.load();
+  }
+  return v;
+}
+
+struct DeviceInfo {
+  bool known = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Device of the calling thread, checked once: gfx950 and its CU count.
+int current_device(ep::Budget* b) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(EP_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.known) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.known = true;
+  }
+  if (!d.gfx950) return fail(EP_ERR_UNSUPPORTED, "libep is built for gfx950 only");
+  b->device_cus = d.cus;
+  b->num_cus = num_cus_setting();
+  return EP_OK;
+}
+
+int check_common(int T, int k, int H_or_E, const char* what) {
+  (void)H_or_E;
+  if (T < 0) return fail(EP_ERR_INVALID_ARG, "%s: T = %d < 0", what, T);
+  if (k < 1 || k > EP_MAX_TOPK) return fail(EP_ERR_INVALID_ARG, "%s: k = %d outside [1, %d]", what, k, EP_MAX_TOPK);
+  if ((int64_t)T * k > INT32_MAX) return fail(EP_ERR_INVALID_ARG, "%s: T * k = %lld overflows int32", what,
+                                              (long long)T * k);
+  return EP_OK;
+}
+
+int check_rows(int H, int64_t recv_rows, const char* what) {
+  if (H <= 0 || H % 8 != 0) return fail(EP_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 8", what, H);
+  if (recv_rows < 0 || recv_rows > INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_rows = %lld outside [0, 2^31)", what, (long long)recv_rows);
+  if ((int64_t)recv_rows * H * 2 / 2 / H != recv_rows) return fail(EP_ERR_INVALID_ARG, "%s: size overflow", what);
+  return EP_OK;
+}
+
+}  // namespace
+
+namespace ep {
+
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace ep
+
+extern "C" {
+
+int ep_set_num_cus(int n) {
+  if (n < 0 || n > 4096) return fail(EP_ERR_INVALID_ARG, "ep_set_num_cus: n = %d outside [0, 4096]", n);
+  g_num_cus.store(n);
+  return EP_OK;
+}
+
+int ep_get_num_cus(void) { return num_cus_setting(); }
+
+int ep_set_variant(const char* name) {
+  if (!name) return fail(EP_ERR_INVALID_ARG, "ep_set_variant: null name");
+  static const struct {
+    const char* name;
+    ep::Variant v;
+  } table[] = {{"auto", ep::Variant::Auto}, {"vgpr", ep::Variant::Vgpr}, {"vgpr2", ep::Variant::Vgpr2},
+               {"lds1", ep::Variant::Lds1}, {"lds2", ep::Variant::Lds2}, {"vgpr_cached", ep::Variant::VgprCached}};
+  for (const auto& e : table) {
+    if (strcmp(e.name, name) == 0) {
+      g_variant.store(static_cast<int>(e.v));
+      return EP_OK;
+    }
+  }
+  return fail(EP_ERR_UNSUPPORTED, "ep_set_variant: unknown variant '%s'", name);
+}
+
+const char* ep_get_variant(void) {
+  switch (static_cast<ep::Variant>(g_variant.load())) {
+    case ep::Variant::Vgpr: return "vgpr";
+    case ep::Variant::Vgpr2: return "vgpr2";
+    case ep::Variant::Lds1: return "lds1";
+    case ep::Variant::Lds2: return "lds2";
+    case ep::Variant::VgprCached: return "vgpr_cached";
+    default: return "auto";
+  }
+}
+
+size_t ep_layout_workspace_bytes(int T, int k, int E) {
+  if (T <= 0 || k < 1 || k > EP_MAX_TOPK || E < 1 || E > EP_MAX_EXPERTS) return 0;
+  return ep::layout_workspace_bytes(T, k, E);
+}
+
+int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+              int32_t* src_token, int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(T, k, E, "ep_layout");
+  if (rc) return rc;
+  if (E < 1 || E > EP_MAX_EXPERTS)
+    return fail(EP_ERR_INVALID_ARG, "ep_layout: E = %d outside [1, %d]", E, EP_MAX_EXPERTS);
+  if (k > E) return fail(EP_ERR_INVALID_ARG, "ep_layout: k = %d > E = %d", k, E);
+  if (!counts || !offsets) return fail(EP_ERR_INVALID_ARG, "ep_layout: null counts/offsets");
+  if (T > 0 && (!topk_idx || !dest_row)) return fail(EP_ERR_INVALID_ARG, "ep_layout: null topk_idx/dest_row");
+  const void* ptrs[] = {topk_idx, counts, offsets, dest_row, src_token, status};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return fail(EP_ERR_ALIGNMENT, "ep_layout: int32 tensor not 4-byte aligned");
+  const size_t need = ep::layout_workspace_bytes(T, k, E);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(EP_ERR_WORKSPACE, "ep_layout: workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(EP_ERR_ALIGNMENT, "ep_layout: workspace not 16-byte aligned");
+  }
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_layout launch");
+  return EP_OK;
+}
+
+int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, void* recv, int64_t recv_rows,
+                void* stream) {
+  int rc = check_common(T, k, H, "ep_dispatch");
+  if (rc) return rc;
+  rc = check_rows(H, recv_rows, "ep_dispatch");
+  if (rc) return rc;
+  if (T > 0 && (!x || !dest_row || (!recv && recv_rows > 0)))
+    return fail(EP_ERR_INVALID_ARG, "ep_dispatch: null x/dest_row/recv");
+  if ((x && !aligned(x, 16)) || (recv && !aligned(recv, 16)))
+    return fail(EP_ERR_ALIGNMENT, "ep_dispatch: bf16 tensor not 16-byte aligned");
+  if (dest_row && !aligned(dest_row, 4)) return fail(EP_ERR_ALIGNMENT, "ep_dispatch: dest_row not 4-byte aligned");
+  if (T == 0 || recv_rows == 0) return EP_OK;
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_dispatch(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, dest_row, k, recv,
+                                     recv_rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_dispatch launch");
+  return EP_OK;
+}
+
+int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row, const float* topk_w, int T, int k,
+               void* out, void* stream) {
+  int rc = check_common(T, k, H, "ep_combine");
+  if (rc) return rc;
+  rc = check_rows(H, recv_rows, "ep_combine");
+  if (rc) return rc;
+  if (T > 0 && (!dest_row || !topk_w || !out || (!y && recv_rows > 0)))
+    return fail(EP_ERR_INVALID_ARG, "ep_combine: null y/dest_row/topk_w/out");
+  if ((y && !aligned(y, 16)) || (out && !aligned(out, 16)))
+    return fail(EP_ERR_ALIGNMENT, "ep_combine: bf16 tensor not 16-byte aligned");
+  if ((dest_row && !aligned(dest_row, 4)) || (topk_w && !aligned(topk_w, 4)))
+    return fail(EP_ERR_ALIGNMENT, "ep_combine: dest_row/topk_w not 4-byte aligned");
+  if (T == 0) return EP_OK;
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_combine(static_cast<ep::Variant>(g_variant.load()), b, y, recv_rows, H, dest_row, topk_w,
+                                    T, k, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_combine launch");
+  return EP_OK;
+}
+
+const char* ep_status_string(int code) {
+  switch (code) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_ALIGNMENT: return "misaligned pointer";
+    case EP_ERR_UNSUPPORTED: return "unsupported device or variant";
+    case EP_ERR_WORKSPACE: return "workspace missing or too small";
+    case EP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown code";
+  }
+}
+
+const char* ep_last_error(void) { return g_err; }
+
+int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
+  if (mode < 0 || mode > 2) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode %d", mode);
+  if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: bytes must be a multiple of 16");
+  if ((mode != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
+  if ((src && !aligned(src, 16)) || !aligned(dst, 16)) return fail(EP_ERR_ALIGNMENT, "ep_bw_probe: alignment");
+  if (bytes == 0) return EP_OK;
+  ep::Budget b;
+  int rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_bw_probe(b, mode, src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_bw_probe launch");
+  return EP_OK;
+}
+
+int ep_probe_placement(int32_t* out, int n_groups, void* stream) {
+  if (!out || n_groups < 1 || n_groups > 65536)
+    return fail(EP_ERR_INVALID_ARG, "ep_probe_placement: bad output or n_groups");
+  if (!aligned(out, 4)) return fail(EP_ERR_ALIGNMENT, "ep_probe_placement: alignment");
+  ep::Budget b;
+  int rc = current_device(&b);
+  if (rc) return rc;
+  int launched = 0;
+  hipError_t e = ep::launch_placement(b, n_groups, out, static_cast<hipStream_t>(stream), &launched);
+  if (e != hipSuccess) return hip_fail(e, "ep_probe_placement launch");
+  return launched;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Host-side interfaces between the C ABI (ep_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+enum class Variant : int { Auto = 0, Vgpr = 1, Vgpr2 = 2, Lds1 = 3, Lds2 = 4, VgprCached = 5 };
+
+// Launch geometry chosen by the host for the row-movement kernels.
+struct Budget {
+  int num_cus;     // > 0: persistent grid of this many workgroups, one per CU
+  int device_cus;  // compute units of the current device
+};
+
+// One CU holds 160 KiB of LDS; a workgroup that asks for more than half of it
+// can never share a CU with another one.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr size_t kExclusiveLds = 80 * 1024 + 1024;
+
+// ---- layout (layout.hip)
+int layout_chunk_tokens(int k);
+int layout_num_chunks(int T, int k);
+size_t layout_workspace_bytes(int T, int k, int E);
+hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
+                         hipStream_t stream);
+
+// ---- dispatch (dispatch.hip)
+hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row,
+                           int k, void* recv, int64_t recv_rows, hipStream_t stream);
+
+// ---- combine (combine.hip)
+hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
+                          const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream);
+
+// ---- probes (probe.hip)
+hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes,
+                           hipStream_t stream);
+hipError_t launch_placement(const Budget& b, int n_groups, int32_t* out, hipStream_t stream, int* launched);
+
+// Raise the dynamic-LDS limit of a kernel once (needed above 64 KiB).
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
+
+}  // namespace ep

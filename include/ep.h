@@ -1,0 +1,189 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE row-movement library, libep.so.
+ *
+ * The library moves bf16 hidden-state rows between token order and an
+ * expert-grouped receive buffer on one GPU:
+ *
+ *   ep_layout   per-expert counts, their prefix sum, and the destination row
+ *               of every (token, slot) entry;
+ *   ep_dispatch copy each token's row to its k destination rows;
+ *   ep_combine  gather each token's k expert-output rows back as a
+ *               gate-weighted sum (fp32 accumulate, bf16 out).
+ *
+ * Sources.  "How DeepEP Utilizes TMA Instructions for Minimal SM Usage on
+ * Hopper GPUs" (instagit.com DeepEP deep-dive; cited as [DeepEP-TMA]),
+ * section "High-Level DeepEP API Usage", shows the dispatch call this ABI
+ * splits into ep_layout (its handle) and ep_dispatch (its output); section
+ * "Asynchronous Copy Primitives" shows the staged row copy; section
+ * "Minimal SM Occupancy Configuration" the knob that caps the compute units
+ * the copy kernels use.  The pages define neither the grouping order nor a
+ * combine; the readings taken are stated at each entry point.
+ *
+ * Conventions shared by every entry point:
+ *   - all tensor pointers are DEVICE pointers into memory the caller owns;
+ *     the library never allocates, frees or retains them;
+ *   - bf16 tensors are row-major with H elements per row, H % 8 == 0, and
+ *     16-byte aligned base pointers (rows are moved as 16-byte vectors);
+ *   - int32/float tensors are row-major and 4-byte aligned;
+ *   - `stream` is a hipStream_t handle (NULL = the default stream); every
+ *     call only enqueues work on it and returns without synchronising;
+ *   - a negative return is a host-detected error: nothing was enqueued and
+ *     ep_last_error() holds a message for the calling thread;
+ *   - T == 0 enqueues nothing and returns EP_OK (after argument checks),
+ *     except ep_layout, which still writes zero counts and offsets and a
+ *     zero status word.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+enum {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = -1, /* null pointer, negative or oversized count, k > E, H % 8 != 0 */
+  EP_ERR_ALIGNMENT = -2,   /* a bf16 tensor not 16-byte aligned, an int/float one not 4-byte aligned */
+  EP_ERR_UNSUPPORTED = -3, /* device is not gfx950, or an unknown variant name */
+  EP_ERR_WORKSPACE = -4,   /* workspace missing or smaller than ep_layout_workspace_bytes() */
+  EP_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+};
+
+/* bits of the device status word written by ep_layout */
+enum {
+  EP_STATUS_EXPERT_OUT_OF_RANGE = 1, /* some topk_idx entry is outside [0, E) */
+  EP_STATUS_DUPLICATE_EXPERT = 2     /* some token lists the same expert twice */
+};
+
+#define EP_MAX_TOPK 32
+#define EP_MAX_EXPERTS 1024
+
+/*
+ * Compute-unit budget of the copy kernels, after [DeepEP-TMA] section
+ * "Minimal SM Occupancy Configuration" (a process-wide cap on the SMs the
+ * communication kernels occupy).  n > 0: dispatch, combine and the probes
+ * launch a persistent grid of n workgroups, each holding more than half a
+ * CU's LDS so that no two share a CU (the hardware spreads consecutive
+ * workgroups over the 8 XCDs); n is clamped to the device's CU count at
+ * launch.  n == 0: an ordinary grid over the whole device.  The initial
+ * value comes from the environment variable EP_NUM_CUS (default 0).
+ * Returns EP_OK, or EP_ERR_INVALID_ARG for n < 0 or n > 4096.
+ */
+int ep_set_num_cus(int n);
+int ep_get_num_cus(void);
+
+/*
+ * Kernel variant for dispatch and combine (process-wide):
+ *   "auto"  the default choice per shape;
+ *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
+ *           or k loads feeding one store (combine);
+ *   "vgpr2" the same with the next work unit's loads issued before the
+ *           current unit's stores (register double buffer);
+ *   "lds1"  rows staged in a per-wave LDS slice by direct-to-LDS loads,
+ *           one stage;
+ *   "lds2"  the same with two stages per wave: the next unit's
+ *           direct-to-LDS load is in flight while the current one is stored.
+ * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
+ */
+int ep_set_variant(const char* name);
+const char* ep_get_variant(void);
+
+/* Bytes of scratch ep_layout needs for (T, k, E); 0 for T == 0. */
+size_t ep_layout_workspace_bytes(int T, int k, int E);
+
+/*
+ * ep_layout -- the routing handle of a dispatch ([DeepEP-TMA] "High-Level
+ * DeepEP API Usage": dispatch takes topk_idx and num_experts and returns a
+ * handle for the way back).
+ *
+ * Entries are the T*k (token, slot) pairs in row-major order.  Output:
+ *   counts[e]       number of entries with topk_idx == e           [E]
+ *   offsets[e]      sum of counts[0..e-1]; offsets[E] = total      [E+1]
+ *   dest_row[t*k+j] offsets[e] + (number of earlier entries, in row-major
+ *                   order, with the same expert e), i.e. a stable
+ *                   counting sort: tokens ascend inside each expert
+ *                   segment; -1 for an entry whose expert is out of range [T*k]
+ *   src_token[r]    the token whose row lands in receive row r, for
+ *                   r < offsets[E]; entries beyond are not written;
+ *                   may be NULL                                      [T*k]
+ *   status[0]       OR of EP_STATUS_* bits (0 when all ids are valid and
+ *                   distinct per token); always written when non-NULL.
+ * An out-of-range id is skipped (not counted, dest_row -1).  A repeated id
+ * inside one token is flagged but still placed as its own entry.
+ * workspace: device scratch of at least ep_layout_workspace_bytes(T, k, E)
+ * bytes, 16-byte aligned, owned by the caller, clobbered by the call.
+ * Limits: 1 <= k <= EP_MAX_TOPK, k <= E <= EP_MAX_EXPERTS, T*k < 2^31.
+ */
+int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+              int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * ep_dispatch -- recv[dest_row[t*k+j], :] = x[t, :] for all t < T, j < k
+ * (bit copy).  The row copy of [DeepEP-TMA] section "Asynchronous Copy
+ * Primitives": each source row is read once into an on-chip slice and
+ * written to each of its k destinations.
+ *   x         bf16 [T, H]
+ *   dest_row  int32 [T, k], normally from ep_layout
+ *   recv      bf16 [recv_rows, H]; an entry whose dest_row is outside
+ *             [0, recv_rows) is skipped; rows nobody targets are untouched.
+ * With valid, distinct routing recv_rows = T*k covers every entry.
+ * Limits: 1 <= k <= EP_MAX_TOPK, 0 <= recv_rows < 2^31, T*k < 2^31.
+ */
+int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, void* recv,
+                int64_t recv_rows, void* stream);
+
+/*
+ * ep_combine -- the way back from the expert-grouped layout, which the
+ * pages do not spell out; the plainest reading is used:
+ *   out[t, :] = bf16_rne( sum_{j=0..k-1} w[t, j] * f32(y[dest_row[t*k+j], :]) )
+ * accumulated in fp32 from +0.0, j ascending, each product and each sum
+ * rounded separately (never fused), then rounded once to bf16 (round to
+ * nearest even).  An entry whose dest_row is outside [0, recv_rows)
+ * contributes nothing.  Weights are used as given (not renormalised).
+ *   y         bf16 [recv_rows, H] expert outputs in the ep_layout order
+ *   dest_row  int32 [T, k]
+ *   topk_w    float32 [T, k]
+ *   out       bf16 [T, H]
+ * Limits as ep_dispatch.
+ */
+int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row, const float* topk_w,
+               int T, int k, void* out, void* stream);
+
+/* Static text for a return code. */
+const char* ep_status_string(int code);
+/* Detail of the calling thread's last negative return ("" if none). */
+const char* ep_last_error(void);
+
+/*
+ * Measurement helpers (not part of the routing path).
+ *
+ * ep_bw_probe: a plain streaming kernel under the same compute-unit budget
+ * as dispatch/combine, giving the achievable HBM ceiling at that budget.
+ *   mode 0: dst[i] = src[i]    (bytes read = bytes written = `bytes`)
+ *   mode 1: read src only (dst must hold 16 bytes; it is written only
+ *           for one improbable checksum, which keeps the reads alive)
+ *   mode 2: dst[i] = pattern   (src unused)
+ * bytes % 16 == 0, pointers 16-byte aligned.
+ */
+int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
+ * ep_probe_placement: launch min(n_groups, budget) workgroups that each
+ * need more than half a CU's LDS (budget = the CU count when
+ * ep_get_num_cus() > 0, else n_groups), each holding its CU for ~50 us, and
+ * have workgroup g write {XCC id, SE id, (SH << 4) | CU id, raw HW_ID} as 4
+ * int32 to out[4g .. 4g+3].  out holds 4 * n_groups int32 (device memory).
+ * Returns the number of workgroups launched, or a negative code.
+ */
+int ep_probe_placement(int32_t* out, int n_groups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,187 @@
+"""The C ABI without a GPU: libep.so loads, exports every entry point that
+include/ep.h declares, and rejects bad arguments on the host before making any
+HIP call (so these run on machines with no device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bulk_async_tensor_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+# fake device addresses: only their alignment matters, none is dereferenced
+A16 = 0x7F0000000000
+A4 = A16 + 4
+ODD = A16 + 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.fail("libep.so is not built (run __graft_entry__.build())")
+    return ep.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in ep._SIGNATURES, f"binding lacks {n}"
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(ep, "LIB_PATH", "/nonexistent/libep.so")
+    monkeypatch.setattr(ep, "_lib", None)
+    with pytest.raises(ep.EpLibraryMissing):
+        ep.lib()
+
+
+def test_num_cus_and_variant_settings(lib):
+    assert lib.ep_set_num_cus(-1) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_set_num_cus(4097) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_set_num_cus(24) == 0 and lib.ep_get_num_cus() == 24
+    assert lib.ep_set_num_cus(0) == 0 and lib.ep_get_num_cus() == 0
+    assert lib.ep_set_variant(b"bogus") == ep.EP_ERR_UNSUPPORTED
+    assert "bogus" in lib.ep_last_error().decode()
+    for v in ep.VARIANTS:
+        assert lib.ep_set_variant(v.encode()) == 0
+        assert lib.ep_get_variant().decode() == v
+    assert lib.ep_set_variant(b"auto") == 0
+
+
+def test_workspace_bytes(lib):
+    # 1024 entries per chunk: T=4096, k=8 -> 32 chunks; counts 32*256*4 = 32768 (256-aligned) + 32 status words
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256) == 32768 + 32 * 4
+    # k=6 -> 170 tokens per chunk -> 97 chunks for T=16384; 97*64*4 = 24832 -> 24832 + 97*4
+    assert lib.ep_layout_workspace_bytes(16384, 6, 64) == 24832 + 97 * 4
+    assert lib.ep_layout_workspace_bytes(0, 8, 256) == 0
+    assert lib.ep_layout_workspace_bytes(10, 0, 256) == 0
+
+
+def layout(lib, idx=A4, T=16, k=2, E=8, counts=A4, offsets=A4, dest=A4, src=A4, status=A4, ws=A16, wsb=1 << 20):
+    return lib.ep_layout(idx, T, k, E, counts, offsets, dest, src, status, ws, wsb, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(k=0), ep.EP_ERR_INVALID_ARG),
+        (dict(k=33, E=64), ep.EP_ERR_INVALID_ARG),
+        (dict(E=0), ep.EP_ERR_INVALID_ARG),
+        (dict(E=1025), ep.EP_ERR_INVALID_ARG),
+        (dict(k=9, E=8), ep.EP_ERR_INVALID_ARG),
+        (dict(T=2**30, k=4), ep.EP_ERR_INVALID_ARG),
+        (dict(counts=None), ep.EP_ERR_INVALID_ARG),
+        (dict(offsets=None), ep.EP_ERR_INVALID_ARG),
+        (dict(idx=None), ep.EP_ERR_INVALID_ARG),
+        (dict(dest=None), ep.EP_ERR_INVALID_ARG),
+        (dict(dest=ODD), ep.EP_ERR_ALIGNMENT),
+        (dict(idx=ODD), ep.EP_ERR_ALIGNMENT),
+        (dict(status=A4 + 2), ep.EP_ERR_ALIGNMENT),
+        (dict(ws=None), ep.EP_ERR_WORKSPACE),
+        (dict(wsb=16), ep.EP_ERR_WORKSPACE),
+        (dict(ws=A4), ep.EP_ERR_ALIGNMENT),
+    ],
+)
+def test_layout_rejects(lib, kw, code):
+    assert layout(lib, **kw) == code
+    assert lib.ep_last_error().decode() != ""
+
+
+def dispatch(lib, x=A16, T=16, H=1024, dest=A4, k=2, recv=A16, rows=32):
+    return lib.ep_dispatch(x, T, H, dest, k, recv, rows, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(H=0), ep.EP_ERR_INVALID_ARG),
+        (dict(H=1020), ep.EP_ERR_INVALID_ARG),
+        (dict(k=0), ep.EP_ERR_INVALID_ARG),
+        (dict(k=33), ep.EP_ERR_INVALID_ARG),
+        (dict(rows=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(rows=2**31), ep.EP_ERR_INVALID_ARG),
+        (dict(T=2**30, k=4), ep.EP_ERR_INVALID_ARG),
+        (dict(x=None), ep.EP_ERR_INVALID_ARG),
+        (dict(dest=None), ep.EP_ERR_INVALID_ARG),
+        (dict(recv=None), ep.EP_ERR_INVALID_ARG),
+        (dict(x=A16 + 8), ep.EP_ERR_ALIGNMENT),
+        (dict(recv=A4), ep.EP_ERR_ALIGNMENT),
+        (dict(dest=ODD), ep.EP_ERR_ALIGNMENT),
+    ],
+)
+def test_dispatch_rejects(lib, kw, code):
+    assert dispatch(lib, **kw) == code
+
+
+def combine(lib, y=A16, rows=32, H=1024, dest=A4, w=A4, T=16, k=2, out=A16):
+    return lib.ep_combine(y, rows, H, dest, w, T, k, out, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(H=12), ep.EP_ERR_INVALID_ARG),
+        (dict(k=0), ep.EP_ERR_INVALID_ARG),
+        (dict(rows=-5), ep.EP_ERR_INVALID_ARG),
+        (dict(w=None), ep.EP_ERR_INVALID_ARG),
+        (dict(out=None), ep.EP_ERR_INVALID_ARG),
+        (dict(y=None), ep.EP_ERR_INVALID_ARG),
+        (dict(out=A16 + 4), ep.EP_ERR_ALIGNMENT),
+        (dict(y=A16 + 2), ep.EP_ERR_ALIGNMENT),
+        (dict(w=ODD), ep.EP_ERR_ALIGNMENT),
+    ],
+)
+def test_combine_rejects(lib, kw, code):
+    assert combine(lib, **kw) == code
+
+
+def test_empty_batches_are_host_no_ops(lib):
+    # T == 0 returns before touching the device
+    assert dispatch(lib, T=0, x=None, dest=None, recv=None) == 0
+    assert combine(lib, T=0, y=None, dest=None, w=None, out=None) == 0
+    # so does an empty receive buffer
+    assert dispatch(lib, rows=0, recv=None) == 0
+
+
+def test_probe_rejects(lib):
+    assert lib.ep_bw_probe(3, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_bw_probe(0, A16, A16, 1000 + 4, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_bw_probe(0, None, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_bw_probe(0, A16 + 4, A16, 1024, None) == ep.EP_ERR_ALIGNMENT
+    assert lib.ep_bw_probe(0, A16, A16, 0, None) == 0
+    assert lib.ep_probe_placement(None, 4, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_probe_placement(A4, 0, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in [0, -1, -2, -3, -4, -5]:
+        s = lib.ep_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.ep_status_string(-99).decode() == "unknown code"
+
+
+def test_binding_checks_tensors_before_the_library():
+    import torch
+
+    cpu = torch.zeros((4, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ep.ep_dispatch(cpu, torch.zeros((4, 2), dtype=torch.int32), cpu)
+    with pytest.raises(TypeError):
+        ep.ep_combine(None, None, None, cpu)

@@ -1,0 +1,262 @@
+"""GPU parity through the C ABI against the CPU oracle.
+
+Layout and dispatch must be bit-exact; combine must be within
+abs(g - r) <= 1e-2 * abs(r) + 1e-3 and is, in addition, expected bit-exact
+(same slot order, no fused multiply-add, one RNE rounding on both sides).
+Every workload shape runs at full size; smaller cases cover ragged chunk and
+row tails, empty and degenerate routing, and every kernel variant at several
+compute-unit budgets (the budgets of the benchmark among them).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bulk_async_tensor_amd as ep
+import oracle
+from synth import CONFIGS, make_workload
+
+from gpu_helpers import (
+    DEV,
+    assert_combine_close,
+    expert_outputs,
+    from_dev_bf16,
+    oracle_layout,
+    oracle_out,
+    oracle_recv,
+    to_dev,
+    to_dev_bf16,
+    workload,
+)
+
+pytestmark = pytest.mark.gpu
+
+DISPATCH_CONFIGS = [n for n, c in CONFIGS.items() if c.ops != "combine"]
+BUDGETS = [0, 16, 24, 32, 64, 256]
+
+
+@pytest.fixture(autouse=True)
+def _reset_settings():
+    ep.ep_set_num_cus(0)
+    ep.ep_set_variant("auto")
+    yield
+    ep.ep_set_num_cus(0)
+    ep.ep_set_variant("auto")
+
+
+def gpu_layout(wl):
+    lay = ep.ep_layout(to_dev(wl.topk_idx), wl.config.E)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in lay.items()}
+
+
+def check_layout(got, ref, T, k):
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["dest_row"].reshape(T, k), ref["dest_row"])
+    n = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(got["src_token"][:n], ref["src_token"][:n])
+    assert int(got["status"][0]) == ref["status"]
+
+
+# ----------------------------------------------------------------- layout
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_layout_full_size(name):
+    wl = workload(name)
+    check_layout(gpu_layout(wl), oracle_layout(name), wl.config.T, wl.config.k)
+
+
+@pytest.mark.parametrize(
+    "T,E,k",
+    [(1, 1, 1), (1, 8, 8), (7, 5, 3), (171, 64, 6), (1000, 64, 6), (129, 1024, 32), (3000, 3, 2), (5000, 1024, 1)],
+)
+def test_layout_ragged_and_extreme(T, E, k):
+    wl = make_workload("prefill", seed=T * 31 + E, T=T, E=E, k=k)
+    check_layout(gpu_layout(wl), oracle.layout(wl.topk_idx, E), T, k)
+
+
+def test_layout_empty_batch():
+    lay = ep.ep_layout(torch.zeros((0, 4), dtype=torch.int32, device=DEV), 16)
+    torch.cuda.synchronize()
+    assert lay["counts"].cpu().tolist() == [0] * 16
+    assert lay["offsets"].cpu().tolist() == [0] * 17
+    assert int(lay["status"].item()) == 0
+
+
+def test_layout_flags_bad_ids():
+    rng = np.random.default_rng(5)
+    idx = np.array([rng.permutation(16)[:4] for _ in range(600)], dtype=np.int32)
+    idx[3, 1] = 16
+    idx[77, 0] = -2
+    idx[500, 2] = 1 << 30
+    idx[10, 3] = idx[10, 0]
+    for T, want in [(600, 3), (3, 0)]:
+        sub = np.ascontiguousarray(idx[:T])
+        ref = oracle.layout(sub, 16)
+        assert ref["status"] == want
+        lay = ep.ep_layout(to_dev(sub), 16)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in lay.items()}
+        check_layout(got, ref, T, 4)
+
+
+def test_layout_is_deterministic():
+    wl = workload("train")
+    a = gpu_layout(wl)
+    b = gpu_layout(wl)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+# ----------------------------------------------------------------- dispatch
+def run_dispatch(wl, dest_row_np, recv_rows, fill=0x7E57):
+    x = to_dev_bf16(wl.x)
+    recv = torch.full((recv_rows, wl.config.H), fill, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep.ep_dispatch(x, to_dev(dest_row_np), recv)
+    torch.cuda.synchronize()
+    return from_dev_bf16(recv)
+
+
+@pytest.mark.parametrize("name", DISPATCH_CONFIGS)
+def test_dispatch_full_size(name):
+    wl = workload(name)
+    lay = oracle_layout(name)
+    got = run_dispatch(wl, lay["dest_row"], wl.config.T * wl.config.k)
+    np.testing.assert_array_equal(got, oracle_recv(name))
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"])
+@pytest.mark.parametrize("budget", BUDGETS)
+def test_dispatch_variants_train(variant, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    wl = workload("train")
+    got = run_dispatch(wl, oracle_layout("train")["dest_row"], wl.config.T * wl.config.k)
+    np.testing.assert_array_equal(got, oracle_recv("train"))
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("H", [8, 520, 1024, 4104, 7168, 7176, 16384])
+@pytest.mark.parametrize("k", [2, 3, 6])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_dispatch_ragged_rows(variant, H, k, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    T = 37
+    wl = make_workload("prefill", seed=H + k, T=T, H=H, E=16, k=k)
+    lay = oracle.layout(wl.topk_idx, 16)
+    got = run_dispatch(wl, lay["dest_row"], T * k)
+    np.testing.assert_array_equal(got, oracle.dispatch(wl.x, lay["dest_row"], T * k))
+
+
+def test_dispatch_skips_rows_outside_recv():
+    wl = make_workload("decode", T=64)
+    lay = oracle.layout(wl.topk_idx, 256)
+    dest = lay["dest_row"].copy()
+    dest[5, 2] = -1
+    dest[9, 0] = 1 << 30
+    rows = 300  # smaller than T*k: entries at or past row 300 are skipped
+    fill = 0x7E57
+    got = run_dispatch(wl, dest, rows, fill=fill)
+    ref = oracle.dispatch(wl.x, dest, rows, recv=np.full((rows, wl.config.H), fill, dtype=np.uint16))
+    np.testing.assert_array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- combine
+def run_combine(wl, y_u16, dest_row_np):
+    out = torch.empty((wl.config.T, wl.config.H), dtype=torch.bfloat16, device=DEV)
+    ep.ep_combine(to_dev_bf16(y_u16), to_dev(dest_row_np), to_dev(wl.topk_w), out)
+    torch.cuda.synchronize()
+    return from_dev_bf16(out)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_combine_full_size(name):
+    wl = workload(name)
+    got = run_combine(wl, expert_outputs(name), oracle_layout(name)["dest_row"])
+    assert_combine_close(got, oracle_out(name))
+    if wl.config.expert == "identity":
+        # closed form: combine(dispatch(x)) == x with weights summing to 1
+        assert np.array_equal(oracle.bf16_to_f32(got), oracle.bf16_to_f32(wl.x))
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"])
+@pytest.mark.parametrize("budget", BUDGETS)
+def test_combine_variants_stress(variant, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    name = "combine_stress"
+    wl = workload(name)
+    got = run_combine(wl, expert_outputs(name), oracle_layout(name)["dest_row"])
+    assert_combine_close(got, oracle_out(name))
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_combine_variants_train(variant, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    wl = workload("train")
+    got = run_combine(wl, expert_outputs("train"), oracle_layout("train")["dest_row"])
+    assert_combine_close(got, oracle_out("train"))
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("H", [8, 520, 4104, 7176])
+@pytest.mark.parametrize("k", [1, 3, 6, 8, 11])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_combine_ragged_rows(variant, H, k, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    T = 29
+    wl = make_workload("combine_stress", seed=H + k, T=T, H=H, E=32, k=k)
+    lay = oracle.layout(wl.topk_idx, 32)
+    dest = lay["dest_row"].copy()
+    dest[3, 0] = -1  # a slot that contributes nothing
+    y = wl.y
+    ref = oracle.combine(y, dest, wl.topk_w)
+    got = run_combine(wl, y, dest)
+    assert_combine_close(got, ref)
+
+
+def test_combine_unnormalised_weights_and_signed_zero():
+    wl = make_workload("tiny", T=16)
+    lay = oracle.layout(wl.topk_idx, 8)
+    recv = oracle.dispatch(wl.x, lay["dest_row"], 32)
+    recv[:4] = 0x8000  # -0.0 rows
+    wl.topk_w = (wl.topk_w * np.float32(3.5)).astype(np.float32)
+    got = run_combine(wl, recv, lay["dest_row"])
+    assert_combine_close(got, oracle.combine(recv, lay["dest_row"], wl.topk_w))
+
+
+# ----------------------------------------------------------------- probes
+def test_bw_probe_copies_and_writes():
+    n = (1 << 22) + 4096
+    src = torch.randint(-(1 << 31), 1 << 31, (n // 4,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    for budget in (0, 24):
+        ep.ep_set_num_cus(budget)
+        dst.zero_()
+        ep.ep_bw_probe(0, src, dst, n)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        ep.ep_bw_probe(1, src, dst, n)
+        ep.ep_bw_probe(2, None, dst, n)
+        torch.cuda.synchronize()
+        v = dst.view(-1, 4).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        idx = np.arange(v.shape[0])
+        assert np.array_equal(v[:, 0], idx & 0xFFFFFFFF) and np.all(v[:, 1] == 0x5A5A5A5A)
+
+
+@pytest.mark.parametrize("budget", [16, 24, 32, 64])
+def test_persistent_grid_gets_distinct_cus(budget):
+    ep.ep_set_num_cus(budget)
+    out = torch.full((budget, 4), -1, dtype=torch.int32, device=DEV)
+    n = ep.ep_probe_placement(out, budget)
+    torch.cuda.synchronize()
+    assert n == budget
+    rows = [tuple(r) for r in out.cpu().numpy()[:, :3].tolist()]
+    assert len(set(rows)) == budget, f"workgroups shared a CU: {sorted(rows)}"
+    per_xcc = np.bincount([r[0] for r in rows], minlength=8)
+    print(f"budget {budget}: workgroups per XCD {per_xcc.tolist()}", flush=True)
+    assert per_xcc.max() - per_xcc.min() <= 1
