@@ -41,13 +41,15 @@ def parse_args():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="write a CU x variant sweep as JSONL to this file")
+    p.add_argument("--sweep-budgets", default="16,24,32,64,128,256,0")
+    p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
     return p.parse_args()
 
 
 class Setup:
     """Device buffers of one workload and the step that runs on them."""
 
-    def __init__(self, name):
+    def __init__(self, name, stream=None):
         import numpy as np
         import torch
 
@@ -56,6 +58,7 @@ class Setup:
 
         self.ep = ep
         self.torch = torch
+        self.stream = stream
         dev = torch.device("cuda:0")
         wl = make_workload(name)
         self.wl = wl
@@ -97,45 +100,48 @@ class Setup:
 
     def layout(self):
         self.ep.ep_layout(self.idx, self.E, self.counts, self.offsets, self.dest_row, self.src_token, self.status,
-                          self.ws)
+                          self.ws, stream=self.stream)
 
     def dispatch(self):
         if self.do_dispatch:
-            self.ep.ep_dispatch(self.x, self.dest_row, self.recv)
+            self.ep.ep_dispatch(self.x, self.dest_row, self.recv, stream=self.stream)
 
     def combine(self):
-        self.ep.ep_combine(self.y, self.dest_row, self.w, self.out)
+        self.ep.ep_combine(self.y, self.dest_row, self.w, self.out, stream=self.stream)
 
     def run(self, steps, warmup):
-        """Times `steps` whole steps; per-kernel times from HIP events recorded
-        on the stream the kernels are launched on."""
+        """Whole steps: `steps` back-to-back steps between two synchronisations
+        (no events inside the loop).  Per kernel: `steps` back-to-back launches
+        of that kernel alone between two HIP events recorded on the stream the
+        kernels are launched on; returns ms per step and ms per launch."""
         torch = self.torch
-        stream = torch.cuda.current_stream()
+        stream = self.stream if self.stream is not None else torch.cuda.current_stream()
         for _ in range(warmup):
             self.layout()
             self.dispatch()
             self.combine()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            e = ev[i]
-            e[0].record(stream)
+        for _ in range(steps):
             self.layout()
-            e[1].record(stream)
             self.dispatch()
-            e[2].record(stream)
             self.combine()
-            e[3].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = {"layout": 0.0, "dispatch": 0.0, "combine": 0.0}
-        for e in ev:
-            per["layout"] += e[0].elapsed_time(e[1])
-            per["dispatch"] += e[1].elapsed_time(e[2])
-            per["combine"] += e[2].elapsed_time(e[3])
-        per = {k: v / steps for k, v in per.items()}  # ms per launch
-        ms = wall * 1e3 / steps
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        per = {}
+        for name, fn in (("layout", self.layout), ("dispatch", self.dispatch), ("combine", self.combine)):
+            if name == "dispatch" and not self.do_dispatch:
+                per[name] = 0.0
+                continue
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per[name] = e0.elapsed_time(e1) / steps
         return ms, per
 
 
@@ -218,45 +224,101 @@ def cpu_baseline(name, seconds):
     }
 
 
-def sweep(path, name, steps, warmup):
+def parse_budget(tok):
+    """'24' -> persistent grid of 24 workgroups; 'm24' -> ordinary grid on a
+    stream masked to the first 24 CUs; '0' -> ordinary grid, whole device."""
+    tok = str(tok).strip()
+    if tok.startswith("m"):
+        return "mask", int(tok[1:])
+    return "grid", int(tok)
+
+
+def sweep(path, name, steps, warmup, budgets):
     """CU budget x variant over the workload, plus the streaming-probe ceilings."""
     import torch
 
     import bulk_async_tensor_amd as ep
 
     s = Setup(name)
-    budgets = [16, 24, 32, 64, 128, 256, 0]
     variants = ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"]
     n = 1 << 30
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
     bb = torch.empty_like(a)
     with open(path, "a") as fh:
-        for budget in budgets:
-            ep.ep_set_num_cus(budget)
-            for mode, label in [(0, "copy"), (1, "read"), (2, "write")]:
+        for tok in budgets:
+            kind, budget = parse_budget(tok)
+            stream = None
+            if kind == "mask":
+                stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(budget)))
+                ep.ep_set_num_cus(0)
+            else:
+                ep.ep_set_num_cus(budget)
+            s.stream = stream
+            st = stream if stream is not None else torch.cuda.current_stream()
+            for mode, label in [(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32")]:
                 for _ in range(3):
-                    ep.ep_bw_probe(mode, a, bb, n)
+                    ep.ep_bw_probe(mode, a, bb, n, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+                e0.record(st)
                 for _ in range(10):
-                    ep.ep_bw_probe(mode, a, bb, n)
-                e1.record()
+                    ep.ep_bw_probe(mode, a, bb, n, stream=st)
+                e1.record(st)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
                 moved = 2 * n if mode == 0 else n
-                rec = {"kind": "probe", "mode": label, "num_cus": budget, "ms": ms, "GBs": moved / ms / 1e6}
+                rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
             for v in variants:
                 ep.ep_set_variant(v)
                 ms, per = s.run(steps, warmup)
-                rec = {"kind": "step", "workload": name, "variant": v, "num_cus": budget, "ms_per_step": ms,
+                rec = {"kind": "step", "workload": name, "variant": v, "num_cus": str(tok), "ms_per_step": ms,
                        "kernel_ms": per,
                        "GBs": {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
+            s.stream = None
+            if stream is not None:
+                torch.cuda.synchronize()
+                ep.ep_stream_destroy(stream)
     ep.ep_set_num_cus(0)
     ep.ep_set_variant("auto")
+
+
+def probe_sweep(path, budgets):
+    """Streaming-probe matrix: operation x in-flight depth x load cache policy
+    at each CU budget (1 GiB buffers, 10 timed launches each)."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    cases = [(0, d, 0) for d in range(3)] + [(2, d, 0) for d in range(3)]
+    cases += [(1, d, p) for d in range(3) for p in range(6)] + [(3, 0, p) for p in range(6)]
+    names = {0: "copy", 1: "read", 2: "write", 3: "read_lds"}
+    pols = {0: "nt", 1: "none", 2: "sc0", 3: "sc1", 4: "sc0sc1", 5: "nt_buf"}
+    with open(path, "a") as fh:
+        for budget in budgets:
+            ep.ep_set_num_cus(budget)
+            for op, d, p in cases:
+                mode = op | (d << 4) | (p << 8)
+                for _ in range(2):
+                    ep.ep_bw_probe(mode, a, b, n)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    ep.ep_bw_probe(mode, a, b, n)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 10
+                moved = 2 * n if op == 0 else n
+                rec = {"kind": "probe", "op": names[op], "depth": 8 << d, "policy": pols[p], "num_cus": budget,
+                       "ms": round(ms, 4), "GBs": round(moved / ms / 1e6, 1)}
+                fh.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), flush=True)
+    ep.ep_set_num_cus(0)
 
 
 def main():
@@ -273,8 +335,12 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
     ep.lib()
+    budgets = args.sweep_budgets.split(",")
+    if args.probe_sweep:
+        probe_sweep(args.probe_sweep, [int(b) for b in budgets])
+        return
     if args.sweep:
-        sweep(args.sweep, args.workload, max(20, args.steps // 4), 5)
+        sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets)
         return
 
     ep.ep_set_variant(args.variant)

@@ -45,6 +45,8 @@ _SIGNATURES = {
     "ep_last_error": (ctypes.c_char_p, []),
     "ep_bw_probe": (_c_int, [_c_int, _p, _p, _c_i64, _p]),
     "ep_probe_placement": (_c_int, [_p, _c_int, _p]),
+    "ep_stream_create_cu_masked": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, ctypes.POINTER(_p)]),
+    "ep_stream_destroy": (_c_int, [_p]),
 }
 
 
@@ -230,6 +232,31 @@ def ep_probe_placement(out, n_groups, stream=None):
     return _check(lib().ep_probe_placement(_ptr(out), int(n_groups), _stream(stream)), "ep_probe_placement")
 
 
+# ------------------------------------------------------------------ CU-masked streams
+def cu_mask_words(cus, n_words=8):
+    """Mask words with the bits of the given CU indices set."""
+    words = [0] * n_words
+    for c in cus:
+        words[c // 32] |= 1 << (c % 32)
+    return words
+
+
+def ep_stream_create_cu_masked(mask_words):
+    """A torch ExternalStream over a new HIP stream restricted to the CUs whose
+    bits are set in mask_words (a list of uint32)."""
+    import torch
+
+    arr = (ctypes.c_uint32 * len(mask_words))(*[int(w) & 0xFFFFFFFF for w in mask_words])
+    out = ctypes.c_void_p()
+    _check(lib().ep_stream_create_cu_masked(arr, len(mask_words), ctypes.byref(out)), "ep_stream_create_cu_masked")
+    return torch.cuda.ExternalStream(out.value)
+
+
+def ep_stream_destroy(stream):
+    """Destroys a stream made by ep_stream_create_cu_masked (after use)."""
+    return _check(lib().ep_stream_destroy(ctypes.c_void_p(stream.cuda_stream)), "ep_stream_destroy")
+
+
 __all__ = [n for n in list(globals()) if n.startswith("ep_") or n.startswith("EP_")] + [
-    "lib", "LIB_PATH", "VARIANTS", "EpError", "EpLibraryMissing",
+    "lib", "LIB_PATH", "VARIANTS", "EpError", "EpLibraryMissing", "cu_mask_words",
 ]

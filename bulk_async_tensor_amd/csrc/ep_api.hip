@@ -232,9 +232,12 @@ const char* ep_status_string(int code) {
 const char* ep_last_error(void) { return g_err; }
 
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
-  if (mode < 0 || mode > 2) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode %d", mode);
+  if (mode < 0 || (mode & ~0x733) != 0 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
+    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode 0x%x", mode);
   if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: bytes must be a multiple of 16");
-  if ((mode != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
+  if (((mode & 3) != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
+  if ((mode & 3) != 0 && (mode & 3) != 2 && bytes > ((int64_t)1 << 40))
+    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: size");
   if ((src && !aligned(src, 16)) || !aligned(dst, 16)) return fail(EP_ERR_ALIGNMENT, "ep_bw_probe: alignment");
   if (bytes == 0) return EP_OK;
   ep::Budget b;
@@ -256,6 +259,27 @@ int ep_probe_placement(int32_t* out, int n_groups, void* stream) {
   hipError_t e = ep::launch_placement(b, n_groups, out, static_cast<hipStream_t>(stream), &launched);
   if (e != hipSuccess) return hip_fail(e, "ep_probe_placement launch");
   return launched;
+}
+
+int ep_stream_create_cu_masked(const uint32_t* mask, int mask_words, void** stream) {
+  if (!mask || !stream) return fail(EP_ERR_INVALID_ARG, "ep_stream_create_cu_masked: null pointer");
+  if (mask_words < 1 || mask_words > 64)
+    return fail(EP_ERR_INVALID_ARG, "ep_stream_create_cu_masked: mask_words = %d outside [1, 64]", mask_words);
+  uint32_t any = 0;
+  for (int i = 0; i < mask_words; ++i) any |= mask[i];
+  if (!any) return fail(EP_ERR_INVALID_ARG, "ep_stream_create_cu_masked: empty mask");
+  hipStream_t s = nullptr;
+  hipError_t e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask_words, mask);
+  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask");
+  *stream = s;
+  return EP_OK;
+}
+
+int ep_stream_destroy(void* stream) {
+  if (!stream) return fail(EP_ERR_INVALID_ARG, "ep_stream_destroy: null stream");
+  hipError_t e = hipStreamDestroy(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamDestroy");
+  return EP_OK;
 }
 
 }  // extern "C"

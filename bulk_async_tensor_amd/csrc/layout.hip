@@ -1,19 +1,24 @@
 // ep_layout: per-expert counts, prefix-sum offsets and stable destination
 // rows of the (token, slot) entries -- the routing handle that the dispatch
 // call of [DeepEP-TMA] ("High-Level DeepEP API Usage") returns for the way
-// back.  Three launches on the caller's stream:
+// back.  Entries of one expert are placed in row-major (token, slot) order;
+// no atomic operation decides a row, so the result is deterministic.
 //
-//   count  one workgroup per chunk of tokens: LDS histogram of the chunk's
-//          expert ids, id validation (range, repeats inside a token);
-//   scan   one workgroup: per-expert totals, exclusive scan over experts,
-//          and the base row of every (chunk, expert) pair;
-//   place  one wave per chunk: walks the chunk's entries 64 at a time in
-//          row-major order; lanes holding the same expert find each other
-//          with log2(E) ballots, rank themselves with mbcnt, and the highest
-//          lane of each group advances that expert's running row in LDS.
+// Fused path (one launch; used while the per-chunk histogram fits in LDS):
+// workgroup c owns entries [1024 c, 1024 c + 1024), one 64-entry step per
+// wave.  Every workgroup reads all T*k ids (a few hundred KiB at most) and
+// builds the full (chunk, expert) histogram in LDS, so it knows each
+// expert's total and the part that precedes its chunk without any
+// inter-workgroup communication; a block scan over experts gives the
+// offsets.  Inside the chunk, lanes holding the same expert find each other
+// with log2(E) ballots, rank themselves with mbcnt, and the per-step group
+// sizes (written to LDS by the highest lane of each group) give each wave
+// the rows taken by the steps before it.
 //
-// The order is deterministic (no atomics decide a row): entries of one
-// expert are placed in row-major (token, slot) order.
+// Large path (three launches): count (LDS histogram per chunk of tokens),
+// scan (one workgroup: totals, offsets and the base row of every (chunk,
+// expert)), place (one wave per chunk walking its entries 64 at a time,
+// advancing per-expert cursors in LDS).
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -193,12 +198,195 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
     if (ok) r = run[e] + rank;
     // the highest lane of each group moves the expert's cursor past the group
     if (ok && (m >> lane) == 1ull) run[e] = r + 1;
-    __syncthreads();
+    // one wave: its LDS operations complete in program order, so the next
+    // step's reads see these writes; no barrier (a barrier would also wait
+    // for the global stores below)
+    __builtin_amdgcn_wave_barrier();
     if (in_chunk) {
       dest_row[i0 + i] = r;
       if (ok && src_token) src_token[r] = t0 + i / k;
     }
   }
+}
+
+constexpr int kFusedChunk = 1024;   // entries per workgroup: 16 waves x 64
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of one value per thread over a 1024-thread block; *total
+// receives the sum.  s_wave holds kFusedWaves + 1 ints of LDS.
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int wt = lane < kFusedWaves ? s_wave[lane] : 0;
+    const int ws = wave_incl_scan(wt, lane);
+    if (lane < kFusedWaves) s_wave[lane] = ws - wt;
+    if (lane == kFusedWaves - 1) s_wave[kFusedWaves] = ws;
+  }
+  __syncthreads();
+  *total = s_wave[kFusedWaves];
+  return incl - v + s_wave[wave];
+}
+
+// Reads the k ids of token t, checks them and adds them to the (chunk,
+// expert) histogram.  KT > 0: k known at compile time, so the loads of a
+// token are independent and issued together.
+template <int KT>
+__device__ __forceinline__ void count_token(const int32_t* __restrict__ idx, int t, int k, int E, int32_t* cnt,
+                                            int& bad) {
+  constexpr int KA = KT > 0 ? KT : 1;
+  if constexpr (KT > 0) {
+    int e[KA];
+#pragma unroll
+    for (int j = 0; j < KA; ++j) e[j] = idx[(int64_t)t * KA + j];
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+      const int i = t * KA + j;
+      if ((unsigned)e[j] < (unsigned)E) {
+        atomicAdd(&cnt[(i >> 10) * E + e[j]], 1);
+#pragma unroll
+        for (int j2 = 0; j2 < j; ++j2)
+          if (e[j2] == e[j]) bad |= kStatusDuplicate;
+      } else {
+        bad |= kStatusOutOfRange;
+      }
+    }
+  } else {
+    const int32_t* r = idx + (int64_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      const int e = r[j];
+      const int i = t * k + j;
+      if ((unsigned)e < (unsigned)E) {
+        atomicAdd(&cnt[(i >> 10) * E + e], 1);
+        for (int j2 = 0; j2 < j; ++j2)
+          if (r[j2] == e) bad |= kStatusDuplicate;
+      } else {
+        bad |= kStatusOutOfRange;
+      }
+    }
+  }
+}
+
+template <int KT>
+__global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                                     int E, int nbits, int nchunks,
+                                                                     int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ dest_row,
+                                                                     int32_t* __restrict__ src_token,
+                                                                     int32_t* __restrict__ status) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;                         // [nchunks][E] entries per (chunk, expert)
+  int32_t* stepc = cnt + nchunks * E;         // [16][E] group sizes per step of this chunk
+  int32_t* base = stepc + kFusedWaves * E;    // [E] first row of each expert for this chunk
+  __shared__ int32_t s_wave[kFusedWaves + 1];
+  __shared__ int32_t s_status;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int N = T * k;
+
+  for (int i = tid; i < (nchunks + kFusedWaves) * E; i += kFusedThreads) cnt[i] = 0;
+  if (tid == 0) s_status = 0;
+  const int my_i = c * kFusedChunk + tid;
+  const int my_e = my_i < N ? idx[my_i] : -1;
+  __syncthreads();
+
+  // Every workgroup histograms all tokens (thread per token) and validates
+  // them, so each one knows the totals and the global status by itself.
+  // Two tokens per trip keep 2k loads in flight per thread.
+  int bad = 0;
+  for (int t = tid; t < T; t += 2 * kFusedThreads) {
+    count_token<KT>(idx, t, k, E, cnt, bad);
+    if (t + kFusedThreads < T) count_token<KT>(idx, t + kFusedThreads, k, E, cnt, bad);
+  }
+  if (bad) atomicOr(&s_status, bad);
+  __syncthreads();
+
+  // expert totals, the part before this chunk, and the offsets
+  int tot = 0, pre = 0;
+  if (tid < E) {
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int v = cnt[cc * E + tid];
+      tot += v;
+      pre += (cc < c) ? v : 0;
+    }
+  }
+  int all = 0;
+  const int excl = block_excl_scan(tot, s_wave, &all);
+  if (tid < E) base[tid] = excl + pre;
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = tot;
+      offsets[tid] = excl;
+    }
+    if (tid == 0) {
+      offsets[E] = all;
+      if (status) status[0] = s_status;
+    }
+  }
+
+  // ranks inside this wave's 64-entry step
+  const bool in_range = my_i < N;
+  const bool ok = in_range && (unsigned)my_e < (unsigned)E;
+  uint64_t m = ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (my_e >> b) & 1;
+    const uint64_t bal = ballot(ok && bit);
+    m &= bit ? bal : ~bal;
+  }
+  const int rank = mask_rank(m);
+  if (ok && (m >> lane) == 1ull) stepc[wave * E + my_e] = __builtin_popcountll(m);
+  __syncthreads();
+  if (in_range) {
+    int r = -1;
+    if (ok) {
+      r = base[my_e] + rank;
+      for (int w = 0; w < wave; ++w) r += stepc[w * E + my_e];
+      if (src_token) src_token[r] = my_i / k;
+    }
+    dest_row[my_i] = r;
+  }
+}
+
+using FusedFn = void (*)(const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*);
+
+FusedFn fused_for(int k) {
+  switch (k) {
+    case 1: return layout_fused_kernel<1>;
+    case 2: return layout_fused_kernel<2>;
+    case 4: return layout_fused_kernel<4>;
+    case 6: return layout_fused_kernel<6>;
+    case 8: return layout_fused_kernel<8>;
+    default: return layout_fused_kernel<0>;
+  }
+}
+
+size_t fused_lds_bytes(int T, int k, int E) {
+  const int64_t N = (int64_t)T * k;
+  const int64_t nchunks = (N + kFusedChunk - 1) / kFusedChunk;
+  return (size_t)(nchunks + kFusedWaves + 1) * E * sizeof(int32_t);
+}
+
+bool use_fused(int T, int k, int E) {
+  const int64_t N = (int64_t)T * k;
+  const int64_t nchunks = (N + kFusedChunk - 1) / kFusedChunk;
+  return nchunks <= 128 && fused_lds_bytes(T, k, E) <= 144 * 1024;
 }
 
 }  // namespace
@@ -211,7 +399,7 @@ int layout_num_chunks(int T, int k) {
 }
 
 size_t layout_workspace_bytes(int T, int k, int E) {
-  if (T <= 0) return 0;
+  if (T <= 0 || use_fused(T, k, E)) return 0;
   const size_t nch = (size_t)layout_num_chunks(T, k);
   size_t counts = nch * (size_t)E * sizeof(int32_t);
   counts = (counts + 255) & ~(size_t)255;
@@ -225,6 +413,19 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
   while (epad < E) epad <<= 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (T == 0 || use_fused(T, k, E)) {
+    const int N = T * k;
+    const int nchunks = (N + kFusedChunk - 1) / kFusedChunk;
+    const size_t lds = fused_lds_bytes(T, k, E);
+    FusedFn fn = fused_for(k);
+    if (lds > 64 * 1024) {
+      hipError_t e = allow_dynamic_lds((const void*)fn, lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(nchunks > 0 ? nchunks : 1), dim3(kFusedThreads), lds, stream, idx, T, k, E, nbits,
+                       nchunks, counts, offsets, dest_row, src_token, status);
+    return hipGetLastError();
+  }
   const int ct = layout_chunk_tokens(k);
   const int nch = T > 0 ? layout_num_chunks(T, k) : 0;
 

@@ -9,37 +9,104 @@ namespace ep {
 
 namespace {
 
-constexpr int kProbeVpl = 8;  // 8 KiB per wave per trip
+// Probe parameters packed in `mode`: bits [1:0] operation (0 copy, 1 read,
+// 2 write, 3 read into LDS by direct-to-LDS loads), bits [5:4] depth (16-byte
+// vectors in flight per lane: 8, 16 or 32), bits [10:8] cache policy of the
+// loads (0 nt, 1 none, 2 sc0, 3 sc1, 4 sc0+sc1, 5 nt through a buffer load).
+constexpr int kPolicyAux[6] = {2, 0, 1, 16, 17, 2};  // gfx940-family CPol bits: sc0 = 1, nt = 2, sc1 = 16
 
-template <int MODE>
+template <int POL>
+__device__ __forceinline__ u32x4 probe_load(const u32x4* __restrict__ src, __amdgpu_buffer_rsrc_t rsrc, int64_t c,
+                                            int64_t win_base) {
+  if constexpr (POL == 0) {
+    return ld16<true>(src + c);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)((c - win_base) * 16), 0, kPolicyAux[POL]);
+    return __builtin_bit_cast(u32x4, v);
+  }
+}
+
+template <int OP, int D, int POL>
 __global__ __launch_bounds__(1024) void bw_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                   int64_t nvec) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = lane_id();
+  const int wave = wave_in_group();
   const int64_t wpg = blockDim.x >> 6;
-  const int64_t chunk = (int64_t)kProbeVpl * kWave;
+  const int64_t chunk = (int64_t)D * kWave;
   const int64_t stride = (int64_t)gridDim.x * wpg * chunk;
   u32x4 sum = {0u, 0u, 0u, 0u};
-  for (int64_t base = ((int64_t)blockIdx.x * wpg + wave_in_group()) * chunk; base < nvec; base += stride) {
-    u32x4 v[kProbeVpl];
-    if (MODE != 2) {
-#pragma unroll
-      for (int i = 0; i < kProbeVpl; ++i) {
-        const int64_t c = base + i * kWave + lane;
-        if (c < nvec) v[i] = ld16<true>(src + c);
+  // buffer loads address a window of at most 2 GiB at a time
+  constexpr int64_t kWin = (int64_t)1 << 27;  // vectors
+  int64_t win_base = -1;
+  __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 0x7FFFFFFF, 0x00020000);
+  char* slice = lds + wave * (D * kWaveVecBytes);
+  for (int64_t base = ((int64_t)blockIdx.x * wpg + wave) * chunk; base < nvec; base += stride) {
+    if constexpr (POL != 0) {
+      const int64_t wb = base & ~(kWin - 1);
+      if (wb != win_base) {
+        win_base = wb;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(src + wb), 0, 0x7FFFFFFF, 0x00020000);
       }
     }
+    if constexpr (OP == 3) {
 #pragma unroll
-    for (int i = 0; i < kProbeVpl; ++i) {
-      const int64_t c = base + i * kWave + lane;
-      if (c < nvec) {
-        if (MODE == 0) st16<true>(dst + c, v[i]);
-        else if (MODE == 1) sum ^= v[i];
-        else st16<true>(dst + c, u32x4{(uint32_t)c, 0x5a5a5a5au, (uint32_t)(c >> 32), 0xa5a5a5a5u});
+      for (int i = 0; i < D; ++i) {
+        const int64_t c = base + i * kWave + lane;
+        if (c < nvec) __builtin_amdgcn_global_load_lds(src + c, (lds_void_t*)(slice + i * kWaveVecBytes), 16, 0,
+                                                       kPolicyAux[POL]);
+      }
+      wait_vmcnt<0>();
+      u32x4 v;
+      lds_read16_async(v, lds_addr_of(slice) + lane * kVecBytes);
+      lds_wait_all();
+      lds_fence_value(v);
+      sum ^= v;
+    } else {
+      u32x4 v[D];
+      if constexpr (OP != 2) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const int64_t c = base + i * kWave + lane;
+          if (c < nvec) v[i] = probe_load<POL>(src, rsrc, c, win_base < 0 ? 0 : win_base);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int64_t c = base + i * kWave + lane;
+        if (c < nvec) {
+          if constexpr (OP == 0) st16<true>(dst + c, v[i]);
+          else if constexpr (OP == 1) sum ^= v[i];
+          else st16<true>(dst + c, u32x4{(uint32_t)c, 0x5a5a5a5au, (uint32_t)(c >> 32), 0xa5a5a5a5u});
+        }
       }
     }
   }
   // keeps the reads alive; true only for a vanishingly unlikely checksum
-  if (MODE == 1 && sum[0] == 0x9e3779b9u && sum[1] == 0x7f4a7c15u && sum[2] == 0x94d049bbu) dst[0] = sum;
+  if ((OP == 1 || OP == 3) && sum[0] == 0x9e3779b9u && sum[1] == 0x7f4a7c15u && sum[2] == 0x94d049bbu) dst[0] = sum;
+}
+
+using BwFn = void (*)(const u32x4*, u32x4*, int64_t);
+
+template <int OP, int D>
+BwFn bw_pick_pol(int pol) {
+  switch (pol) {
+    case 1: return bw_kernel<OP, D, 1>;
+    case 2: return bw_kernel<OP, D, 2>;
+    case 3: return bw_kernel<OP, D, 3>;
+    case 4: return bw_kernel<OP, D, 4>;
+    case 5: return bw_kernel<OP, D, 5>;
+    default: return bw_kernel<OP, D, 0>;
+  }
+}
+
+template <int OP>
+BwFn bw_pick_depth(int depth, int pol) {
+  switch (depth) {
+    case 1: return bw_pick_pol<OP, 16>(pol);
+    case 2: return bw_pick_pol<OP, 32>(pol);
+    default: return bw_pick_pol<OP, 8>(pol);
+  }
 }
 
 // Each workgroup records where it runs, then holds its CU for ~50 us (a
@@ -64,31 +131,43 @@ __global__ __launch_bounds__(64) void placement_kernel(int32_t* __restrict__ out
 }  // namespace
 
 hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  const int op = mode & 3;
+  const int depth_code = (mode >> 4) & 3;
+  const int pol = (mode >> 8) & 7;
+  const int depth = depth_code == 1 ? 16 : depth_code == 2 ? 32 : 8;
+  if (depth_code == 3 || pol > 5) return hipErrorInvalidValue;
   const int64_t nvec = bytes / 16;
+  BwFn fn = op == 0 ? bw_pick_depth<0>(depth_code, 0)
+          : op == 1 ? bw_pick_depth<1>(depth_code, pol)
+          : op == 2 ? bw_pick_depth<2>(depth_code, 0)
+                    : bw_pick_depth<3>(depth_code, pol);
+  const size_t per_wave = op == 3 ? (size_t)depth * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds = 0;
   if (b.num_cus > 0) {
     wpg = 16;
+    if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
     grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-    lds = kExclusiveLds;
+    lds = per_wave * wpg;
+    if (lds < kExclusiveLds) lds = kExclusiveLds;
   } else {
     wpg = 4;
-    const int64_t want = (nvec + (int64_t)kProbeVpl * kWave * wpg - 1) / ((int64_t)kProbeVpl * kWave * wpg);
-    const int64_t cap = (int64_t)b.device_cus * 8;
+    const int64_t per_group = (int64_t)depth * kWave * wpg;
+    const int64_t want = (nvec + per_group - 1) / per_group;
+    int per_cu = per_wave ? (int)(kLdsPerCu / (per_wave * wpg)) : 8;
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t cap = (int64_t)b.device_cus * per_cu;
     grid = (int)(want < cap ? want : cap);
+    lds = per_wave * wpg;
   }
   if (grid < 1) grid = 1;
-  const void* fn = mode == 0 ? (const void*)bw_kernel<0> : mode == 1 ? (const void*)bw_kernel<1>
-                                                                       : (const void*)bw_kernel<2>;
   if (lds > 64 * 1024) {
-    hipError_t e = allow_dynamic_lds(fn, lds);
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds);
     if (e != hipSuccess) return e;
   }
-  const u32x4* s = static_cast<const u32x4*>(src);
-  u32x4* d = static_cast<u32x4*>(dst);
-  if (mode == 0) hipLaunchKernelGGL(bw_kernel<0>, dim3(grid), dim3(wpg * kWave), lds, stream, s, d, nvec);
-  else if (mode == 1) hipLaunchKernelGGL(bw_kernel<1>, dim3(grid), dim3(wpg * kWave), lds, stream, s, d, nvec);
-  else hipLaunchKernelGGL(bw_kernel<2>, dim3(grid), dim3(wpg * kWave), lds, stream, s, d, nvec);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds, stream, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), nvec);
   return hipGetLastError();
 }
 

@@ -164,10 +164,18 @@ const char* ep_last_error(void);
  *
  * ep_bw_probe: a plain streaming kernel under the same compute-unit budget
  * as dispatch/combine, giving the achievable HBM ceiling at that budget.
- *   mode 0: dst[i] = src[i]    (bytes read = bytes written = `bytes`)
- *   mode 1: read src only (dst must hold 16 bytes; it is written only
- *           for one improbable checksum, which keeps the reads alive)
- *   mode 2: dst[i] = pattern   (src unused)
+ * `mode` packs three fields:
+ *   bits [1:0]  operation: 0 copy dst[i] = src[i] (reads and writes `bytes`);
+ *               1 read src (dst must hold 16 bytes; written only for one
+ *               improbable checksum, which keeps the reads alive);
+ *               2 write a pattern to dst (src unused);
+ *               3 read src into per-wave LDS slices with direct-to-LDS loads
+ *               (dst as for 1)
+ *   bits [5:4]  depth: 16-byte vectors in flight per lane, 0 -> 8, 1 -> 16,
+ *               2 -> 32 (3 is invalid)
+ *   bits [10:8] cache policy of the loads of operations 1 and 3: 0 nt,
+ *               1 none, 2 sc0, 3 sc1, 4 sc0+sc1, 5 nt (policies 1-5 use
+ *               buffer loads)
  * bytes % 16 == 0, pointers 16-byte aligned.
  */
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream);
@@ -181,6 +189,22 @@ int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* strea
  * Returns the number of workgroups launched, or a negative code.
  */
 int ep_probe_placement(int32_t* out, int n_groups, void* stream);
+
+/*
+ * CU-masked streams, for running the copy kernels on a chosen set of compute
+ * units beside other work ([DeepEP-TMA] "Minimal SM Occupancy
+ * Configuration": the communication kernels keep to a few units so that the
+ * rest stay free for computation).
+ *
+ * ep_stream_create_cu_masked: a new default-priority HIP stream whose
+ * kernels may only run on the compute units whose bits are set in
+ * mask[0 .. mask_words-1] (bit i of word w = CU 32 w + i in the runtime's
+ * CU numbering).  *stream receives the hipStream_t handle; the caller
+ * releases it with ep_stream_destroy.  Returns EP_OK, EP_ERR_INVALID_ARG
+ * (null pointers, mask_words outside [1, 64], an empty mask) or EP_ERR_HIP.
+ */
+int ep_stream_create_cu_masked(const uint32_t* mask, int mask_words, void** stream);
+int ep_stream_destroy(void* stream);
 
 #ifdef __cplusplus
 }

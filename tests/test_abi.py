@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -61,10 +61,14 @@ def test_num_cus_and_variant_settings(lib):
 
 
 def test_workspace_bytes(lib):
-    # 1024 entries per chunk: T=4096, k=8 -> 32 chunks; counts 32*256*4 = 32768 (256-aligned) + 32 status words
-    assert lib.ep_layout_workspace_bytes(4096, 8, 256) == 32768 + 32 * 4
-    # k=6 -> 170 tokens per chunk -> 97 chunks for T=16384; 97*64*4 = 24832 -> 24832 + 97*4
-    assert lib.ep_layout_workspace_bytes(16384, 6, 64) == 24832 + 97 * 4
+    # shapes whose (chunk, expert) histogram fits in LDS use the one-launch path: no workspace
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256) == 0
+    assert lib.ep_layout_workspace_bytes(16384, 6, 64) == 0
+    # larger ones: chunks of 1024 // k tokens; counts per (chunk, expert), 256-aligned, + one status per chunk
+    # T=131072, k=8 -> 1024 chunks; 1024*256*4 = 1 MiB
+    assert lib.ep_layout_workspace_bytes(131072, 8, 256) == 1024 * 256 * 4 + 1024 * 4
+    # T=40000, k=32, E=1024 -> 32 tokens per chunk -> 1250 chunks; 1250*1024*4 = 5,120,000 (256-aligned)
+    assert lib.ep_layout_workspace_bytes(40000, 32, 1024) == 1250 * 1024 * 4 + 1250 * 4
     assert lib.ep_layout_workspace_bytes(0, 8, 256) == 0
     assert lib.ep_layout_workspace_bytes(10, 0, 256) == 0
 
@@ -90,9 +94,10 @@ def layout(lib, idx=A4, T=16, k=2, E=8, counts=A4, offsets=A4, dest=A4, src=A4, 
         (dict(dest=ODD), ep.EP_ERR_ALIGNMENT),
         (dict(idx=ODD), ep.EP_ERR_ALIGNMENT),
         (dict(status=A4 + 2), ep.EP_ERR_ALIGNMENT),
-        (dict(ws=None), ep.EP_ERR_WORKSPACE),
-        (dict(wsb=16), ep.EP_ERR_WORKSPACE),
-        (dict(ws=A4), ep.EP_ERR_ALIGNMENT),
+        # shapes on the three-launch path need a workspace
+        (dict(T=131072, k=8, E=256, ws=None), ep.EP_ERR_WORKSPACE),
+        (dict(T=131072, k=8, E=256, wsb=16), ep.EP_ERR_WORKSPACE),
+        (dict(T=131072, k=8, E=256, ws=A4, wsb=1 << 24), ep.EP_ERR_ALIGNMENT),
     ],
 )
 def test_layout_rejects(lib, kw, code):
@@ -159,13 +164,28 @@ def test_empty_batches_are_host_no_ops(lib):
 
 
 def test_probe_rejects(lib):
-    assert lib.ep_bw_probe(3, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_bw_probe(-1, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_bw_probe(0x30, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # depth code 3
+    assert lib.ep_bw_probe(0x601, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # policy 6
+    assert lib.ep_bw_probe(0x1000, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # unknown bit
     assert lib.ep_bw_probe(0, A16, A16, 1000 + 4, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_bw_probe(0, None, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_bw_probe(0, A16 + 4, A16, 1024, None) == ep.EP_ERR_ALIGNMENT
     assert lib.ep_bw_probe(0, A16, A16, 0, None) == 0
     assert lib.ep_probe_placement(None, 4, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_probe_placement(A4, 0, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_masked_stream_rejects(lib):
+    out = ctypes.c_void_p()
+    mask = (ctypes.c_uint32 * 8)(*([0] * 8))
+    assert lib.ep_stream_create_cu_masked(None, 8, ctypes.byref(out)) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_masked(mask, 8, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_masked(mask, 0, ctypes.byref(out)) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_masked(mask, 65, ctypes.byref(out)) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_masked(mask, 8, ctypes.byref(out)) == ep.EP_ERR_INVALID_ARG  # empty
+    assert lib.ep_stream_destroy(None) == ep.EP_ERR_INVALID_ARG
+    assert ep.cu_mask_words([0, 33, 255]) == [1, 2, 0, 0, 0, 0, 0, 1 << 31]
 
 
 def test_status_strings(lib):

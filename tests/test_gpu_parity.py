@@ -68,7 +68,11 @@ def test_layout_full_size(name):
 
 @pytest.mark.parametrize(
     "T,E,k",
-    [(1, 1, 1), (1, 8, 8), (7, 5, 3), (171, 64, 6), (1000, 64, 6), (129, 1024, 32), (3000, 3, 2), (5000, 1024, 1)],
+    [
+        (1, 1, 1), (1, 8, 8), (7, 5, 3), (171, 64, 6), (1000, 64, 6), (129, 1024, 32), (3000, 3, 2), (5000, 1024, 1),
+        # three-launch path: too many chunks, or a (chunk, expert) histogram too big for LDS
+        (140000, 256, 8), (1024, 1024, 32), (20001, 1024, 7),
+    ],
 )
 def test_layout_ragged_and_extreme(T, E, k):
     wl = make_workload("prefill", seed=T * 31 + E, T=T, E=E, k=k)
@@ -260,3 +264,33 @@ def test_persistent_grid_gets_distinct_cus(budget):
     per_xcc = np.bincount([r[0] for r in rows], minlength=8)
     print(f"budget {budget}: workgroups per XCD {per_xcc.tolist()}", flush=True)
     assert per_xcc.max() - per_xcc.min() <= 1
+
+
+def test_cu_masked_stream_confines_work():
+    n = 24
+    stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n)))
+    try:
+        out = torch.full((96, 4), -1, dtype=torch.int32, device=DEV)
+        with torch.cuda.stream(stream):
+            launched = ep.ep_probe_placement(out, 96, stream=stream)
+        stream.synchronize()
+        assert launched == 96
+        rows = {tuple(r) for r in out.cpu().numpy()[:, :3].tolist()}
+        per_xcc = np.bincount([r[0] for r in rows], minlength=8)
+        print(f"mask of {n} CUs: {len(rows)} distinct CUs used, per XCD {per_xcc.tolist()}", flush=True)
+        assert 0 < len(rows) <= n
+        # the copy kernels run correctly on it, full grid or persistent
+        wl = workload("train")
+        for budget in (0, 24):
+            ep.ep_set_num_cus(budget)
+            ep.ep_set_variant("lds1")
+            x = to_dev_bf16(wl.x)
+            dest = to_dev(oracle_layout("train")["dest_row"])
+            recv = torch.empty((wl.config.T * wl.config.k, wl.config.H), dtype=torch.bfloat16, device=DEV)
+            torch.cuda.synchronize()
+            ep.ep_dispatch(x, dest, recv, stream=stream)
+            stream.synchronize()
+            np.testing.assert_array_equal(from_dev_bf16(recv), oracle_recv("train"))
+    finally:
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(stream)
