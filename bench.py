@@ -42,6 +42,12 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="write a CU x variant sweep as JSONL to this file")
     p.add_argument("--sweep-budgets", default="16,24,32,64,128,256,0")
+    p.add_argument("--sweep-variants", default="vgpr,vgpr2,lds1,lds2,vgpr_cached")
+    p.add_argument("--sweep-slabs", default="0", help="slab sizes (vectors per lane) to sweep; 0 = default")
+    p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
+    p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
+    p.add_argument("--kernels-only", action="store_true",
+                   help="a few launches of each kernel and of a 256 MiB copy probe (for counter passes)")
     p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
     return p.parse_args()
 
@@ -145,17 +151,6 @@ class Setup:
         return ms, per
 
 
-def kernel_source_hash():
-    import hashlib
-
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "bulk_async_tensor_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None when it
     is missing or was taken on different kernel sources."""
@@ -168,6 +163,8 @@ def read_traffic(kernel, workload):
             m = re.match(r"^([a-z_]+):\s*(\S+)", line.strip())
             if m:
                 fields[m.group(1)] = m.group(2)
+    from bulk_async_tensor_amd.build import kernel_source_hash
+
     if fields.get("kernel_sources") != kernel_source_hash():
         return None
     try:
@@ -233,14 +230,13 @@ def parse_budget(tok):
     return "grid", int(tok)
 
 
-def sweep(path, name, steps, warmup, budgets):
-    """CU budget x variant over the workload, plus the streaming-probe ceilings."""
+def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
+    """CU budget x variant x slab over the workload, plus the streaming-probe ceilings."""
     import torch
 
     import bulk_async_tensor_amd as ep
 
     s = Setup(name)
-    variants = ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"]
     n = 1 << 30
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
     bb = torch.empty_like(a)
@@ -255,7 +251,7 @@ def sweep(path, name, steps, warmup, budgets):
                 ep.ep_set_num_cus(budget)
             s.stream = stream
             st = stream if stream is not None else torch.cuda.current_stream()
-            for mode, label in [(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32")]:
+            for mode, label in ([(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32")] if probes else []):
                 for _ in range(3):
                     ep.ep_bw_probe(mode, a, bb, n, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -270,13 +266,16 @@ def sweep(path, name, steps, warmup, budgets):
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
             for v in variants:
-                ep.ep_set_variant(v)
-                ms, per = s.run(steps, warmup)
-                rec = {"kind": "step", "workload": name, "variant": v, "num_cus": str(tok), "ms_per_step": ms,
-                       "kernel_ms": per,
-                       "GBs": {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}}
-                fh.write(json.dumps(rec) + "\n")
-                print(json.dumps(rec), flush=True)
+                for slab in slabs:
+                    ep.ep_set_variant(v)
+                    ep.ep_set_slab(slab)
+                    ms, per = s.run(steps, warmup)
+                    rec = {"kind": "step", "workload": name, "variant": v, "slab": slab, "num_cus": str(tok),
+                           "ms_per_step": ms, "kernel_ms": per,
+                           "GBs": {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}}
+                    fh.write(json.dumps(rec) + "\n")
+                    print(json.dumps(rec), flush=True)
+            ep.ep_set_slab(0)
             s.stream = None
             if stream is not None:
                 torch.cuda.synchronize()
@@ -321,6 +320,28 @@ def probe_sweep(path, budgets):
     ep.ep_set_num_cus(0)
 
 
+def kernels_only(s, launches=5, copy_bytes=256 << 20):
+    """Short run for counter passes: `launches` of each kernel of the step,
+    then of a copy probe that reads and writes exactly `copy_bytes`."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    for _ in range(launches):
+        s.layout()
+    for _ in range(launches):
+        s.dispatch()
+    for _ in range(launches):
+        s.combine()
+    a = torch.empty(copy_bytes // 4, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(launches):
+        ep.ep_bw_probe(0, a, b, copy_bytes)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernels_only": True, "launches": launches, "copy_bytes": copy_bytes,
+                      "bytes": s.bytes}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -340,17 +361,31 @@ def main():
         probe_sweep(args.probe_sweep, [int(b) for b in budgets])
         return
     if args.sweep:
-        sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets)
+        sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
+              [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes)
         return
 
     ep.ep_set_variant(args.variant)
     s = Setup(args.workload)
+    if args.kernels_only:
+        kernels_only(s)
+        return
     results = {}
     for label, budget in (("all", 0), (f"cu{args.budget}", args.budget)):
+        if args.only_all and budget:
+            continue
         ep.ep_set_num_cus(budget)
         ms, per = s.run(args.steps, args.warmup)
         results[label] = (ms, per)
     ep.ep_set_num_cus(0)
+    if not args.only_all:
+        # the same budget as a CU-masked stream with an ordinary grid
+        mask_stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(args.budget)))
+        s.stream = mask_stream
+        results["mask"] = s.run(args.steps, args.warmup)
+        s.stream = None
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(mask_stream)
 
     ms, per = results["all"]
     value = s.step_bytes / (ms * 1e-3) / 1e9
@@ -359,7 +394,7 @@ def main():
     achieved = s.bytes[dom] / (per[dom] * 1e-3) / 1e9
     kname = {"dispatch": "ep_dispatch", "combine": "ep_combine"}[dom]
     traffic = read_traffic(dom, args.workload)
-    ms_b, per_b = results[f"cu{args.budget}"]
+    ms_b, per_b = results.get(f"cu{args.budget}", (ms, per))
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -378,13 +413,22 @@ def main():
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "kernel_GBs": {k: round(s.bytes[k] / (per[k] * 1e6), 1) for k in per if per[k] > 0 and s.bytes[k]},
-        f"cu{args.budget}": {
+        f"cu{args.budget}": None if f"cu{args.budget}" not in results else {
             "value": round(s.step_bytes / (ms_b * 1e-3) / 1e9, 2),
             "unit": "GB/s",
             "ms_per_step": round(ms_b, 5),
             "tokens_per_s": round(s.T / (ms_b * 1e-3), 1),
             "kernel_ms": {k: round(v, 5) for k, v in per_b.items()},
             "kernel_GBs": {k: round(s.bytes[k] / (per_b[k] * 1e6), 1) for k in per_b if per_b[k] > 0 and s.bytes[k]},
+        },
+        f"cu{args.budget}_masked_stream": None if "mask" not in results else {
+            "value": round(s.step_bytes / (results["mask"][0] * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(results["mask"][0], 5),
+            "tokens_per_s": round(s.T / (results["mask"][0] * 1e-3), 1),
+            "kernel_ms": {k: round(v, 5) for k, v in results["mask"][1].items()},
+            "kernel_GBs": {k: round(s.bytes[k] / (v * 1e6), 1) for k, v in results["mask"][1].items()
+                           if v > 0 and s.bytes[k]},
         },
         "roofline": {
             "kernel": kname,

@@ -37,6 +37,8 @@ _SIGNATURES = {
     "ep_get_num_cus": (_c_int, []),
     "ep_set_variant": (_c_int, [ctypes.c_char_p]),
     "ep_get_variant": (ctypes.c_char_p, []),
+    "ep_set_slab": (_c_int, [_c_int]),
+    "ep_get_slab": (_c_int, []),
     "ep_layout_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "ep_layout": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p]),
     "ep_dispatch": (_c_int, [_p, _c_int, _c_int, _p, _c_int, _p, _c_i64, _p]),
@@ -130,6 +132,14 @@ def ep_set_variant(name):
 
 def ep_get_variant():
     return lib().ep_get_variant().decode()
+
+
+def ep_set_slab(vectors_per_lane):
+    return _check(lib().ep_set_slab(int(vectors_per_lane)), "ep_set_slab")
+
+
+def ep_get_slab():
+    return lib().ep_get_slab()
 
 
 def ep_layout_workspace_bytes(T, k, E):

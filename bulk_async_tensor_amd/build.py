@@ -21,6 +21,18 @@ SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "probe.hip
 ARCH = "gfx950"
 
 
+def kernel_source_hash():
+    """Short hash of every file under csrc/ (identifies the kernels a
+    counter summary was taken on)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")

@@ -142,9 +142,16 @@ __device__ __forceinline__ void sum_unit(float (&acc)[VPL][8], const u32x4 (&v)[
   const u32x4 *__restrict__ y, u32x4 *__restrict__ out, const int32_t *__restrict__ dest_row,                 \
       const float *__restrict__ w, int64_t recv_rows, int row_vec, int nslab, int k_rt, int units
 
+// Threads per workgroup the register budget allows: k x VPL in-flight
+// vectors plus 8 VPL accumulators per lane.
+template <int VPL>
+constexpr int combine_max_threads() {
+  return VPL >= 4 ? 512 : 1024;
+}
+
 // Compile-time k: all k x VPL loads of a unit in flight together.
 template <int VPL, int K, bool EVEN, bool NT>
-__global__ __launch_bounds__(1024) void combine_vgpr_kernel(EP_COMBINE_ARGS) {
+__global__ __launch_bounds__(combine_max_threads<VPL>()) void combine_vgpr_kernel(EP_COMBINE_ARGS) {
   const int lane = lane_id();
   const int wpg = blockDim.x >> 6;
   const int stride = gridDim.x * wpg;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(1024) void combine_vgpr_kernel(EP_COMBINE_ARGS) {
 
 // Any k: slots in batches of 8 whose loads are in flight together.
 template <int VPL, bool EVEN, bool NT>
-__global__ __launch_bounds__(1024) void combine_vgpr_any_kernel(EP_COMBINE_ARGS) {
+__global__ __launch_bounds__(combine_max_threads<VPL>()) void combine_vgpr_any_kernel(EP_COMBINE_ARGS) {
   constexpr int KB = 8;
   const int k = k_rt;
   const int lane = lane_id();
@@ -365,7 +372,8 @@ template <bool EVEN>
 CombineFn pick_vpl(Variant v, int vpl, int k) {
   switch (vpl) {
     case 1: return pick_k<1, EVEN>(v, k);
-    default: return pick_k<2, EVEN>(v, k);
+    case 2: return pick_k<2, EVEN>(v, k);
+    default: return pick_k<4, EVEN>(v, k);
   }
 }
 
@@ -380,8 +388,11 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   const bool even = row_vec % kWave == 0;
   // in-flight registers grow as k x VPL: two vectors per lane per slot for
   // the single-set kernel, one for the double-buffered and LDS ones
-  int vpl = (v == Variant::Vgpr || v == Variant::VgprCached) ? 2 : 1;
+  const bool single = (v == Variant::Vgpr || v == Variant::VgprCached);
+  int vpl = single ? 2 : 1;
+  if (single && b.slab_vpl > 0) vpl = b.slab_vpl >= 4 ? 4 : b.slab_vpl >= 2 ? 2 : 1;
   if (row_vec <= kWave) vpl = 1;
+  const int max_wpg = (single && vpl >= 4) ? 8 : 16;
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;
@@ -393,7 +404,7 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   int wpg, grid;
   size_t lds_bytes;
   if (b.num_cus > 0) {
-    wpg = 16;
+    wpg = max_wpg;
     if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
     grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
     lds_bytes = per_wave * wpg;

@@ -273,20 +273,22 @@ DispatchFn pick_kind(Variant v) {
   switch (v) {
     case Variant::Vgpr: return dispatch_vgpr_kernel<VPL, K, EVEN, true>;
     case Variant::VgprCached: return dispatch_vgpr_kernel<VPL, K, EVEN, false>;
-    case Variant::Vgpr2: return dispatch_vgpr2_kernel<VPL, K, EVEN, true>;
     case Variant::Lds1: return dispatch_lds1_kernel<VPL, K, EVEN, true>;
-    case Variant::Lds2:
-      if constexpr (K > 0) return dispatch_lds2_kernel<VPL, K, EVEN, true>;
-      else return nullptr;
-    default: return nullptr;
+    default: break;
   }
+  // the double-buffered kernels hold two slabs: compiled up to 8 vectors per lane
+  if constexpr (VPL <= 8) {
+    if (v == Variant::Vgpr2) return dispatch_vgpr2_kernel<VPL, K, EVEN, true>;
+    if constexpr (K > 0)
+      if (v == Variant::Lds2) return dispatch_lds2_kernel<VPL, K, EVEN, true>;
+  }
+  return nullptr;
 }
 
 template <int VPL, bool EVEN>
 DispatchFn pick_k(Variant v, int k) {
   switch (k) {
     case 2: return pick_kind<VPL, 2, EVEN>(v);
-    case 4: return pick_kind<VPL, 4, EVEN>(v);
     case 6: return pick_kind<VPL, 6, EVEN>(v);
     case 8: return pick_kind<VPL, 8, EVEN>(v);
     default: return pick_kind<VPL, 0, EVEN>(v);
@@ -299,21 +301,33 @@ DispatchFn pick_vpl(Variant v, int vpl, int k) {
     case 2: return pick_k<2, EVEN>(v, k);
     case 4: return pick_k<4, EVEN>(v, k);
     case 7: return pick_k<7, EVEN>(v, k);
-    default: return pick_k<8, EVEN>(v, k);
+    case 8: return pick_k<8, EVEN>(v, k);
+    case 14: return pick_k<14, EVEN>(v, k);
+    default: return pick_k<16, EVEN>(v, k);
   }
 }
 
-// Vectors per lane per slab: the whole row when it is at most 8 KiB, else
-// 8 or 7 when either splits the row evenly (7 gives the half rows of
-// H = 7168), else 8 with a ragged last slab.
-int choose_vpl(int row_vec) {
+constexpr int kSlabChoices[] = {2, 4, 7, 8, 14, 16};
+constexpr int kWriteCus = 64;
+
+// Vectors per lane per slab.  Default: the whole row when it is at most
+// `cap` vectors per lane (rows then leave a wave as one contiguous burst per
+// destination), else the largest choice that splits the row evenly, else
+// `cap` with a ragged last slab.  A requested size is rounded down to a
+// compiled choice.
+int choose_vpl(int row_vec, int cap, int requested) {
   const int vpr = (row_vec + kWave - 1) / kWave;
-  if (vpr <= 2) return 2;
-  if (vpr <= 4) return 4;
-  if (vpr <= 8) return vpr == 7 ? 7 : 8;
-  if (vpr % 8 == 0) return 8;
-  if (vpr % 7 == 0) return 7;
-  return 8;
+  if (requested > 0) {
+    int best = 2;
+    for (int c : kSlabChoices)
+      if (c <= requested && c <= cap) best = c;
+    return best;
+  }
+  for (int c : kSlabChoices)
+    if (c >= vpr && c <= cap) return c;
+  for (int i = (int)(sizeof(kSlabChoices) / sizeof(int)) - 1; i >= 0; --i)
+    if (kSlabChoices[i] <= cap && vpr % kSlabChoices[i] == 0) return kSlabChoices[i];
+  return cap;
 }
 
 }  // namespace
@@ -326,7 +340,11 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   if (v == Variant::Lds2 && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;
   const bool even = row_vec % kWave == 0;
-  const int vpl = choose_vpl(row_vec);
+  // default slabs of at most 8 KiB (half rows at H = 7168); whole 14 KiB
+  // rows per wave measured no faster.  A requested size may go to 16 for the
+  // single-set kernels; the double-buffered ones hold two slabs, so 8.
+  const int cap = (v == Variant::Vgpr2 || v == Variant::Lds2 || b.slab_vpl == 0) ? 8 : 16;
+  const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;
@@ -337,11 +355,18 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const size_t per_wave = lds ? (size_t)(v == Variant::Lds2 ? 2 : 1) * vpl * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds_bytes;
-  if (b.num_cus > 0) {
+  // With no budget set, a large dispatch still runs as a persistent grid on
+  // kWriteCus CUs: its traffic is 8/9 writes, and HBM write throughput was
+  // measured highest with about a quarter of the CUs issuing them (more add
+  // contention, not bandwidth).  Small batches keep the ordinary grid, whose
+  // start-up is cheaper.
+  int budget = b.num_cus;
+  if (budget == 0 && units >= kWriteCus * 16 * 2) budget = kWriteCus;
+  if (budget > 0) {
     // persistent: one workgroup per CU, as many waves as the LDS ring allows
     wpg = 16;
     if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
-    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    grid = budget < b.device_cus ? budget : b.device_cus;
     lds_bytes = per_wave * wpg;
     if (lds_bytes < kExclusiveLds) lds_bytes = kExclusiveLds;
   } else {

@@ -18,6 +18,7 @@ namespace {
 thread_local char g_err[512] = "";
 std::atomic<int> g_num_cus{-1};  // -1: not read from the environment yet
 std::atomic<int> g_variant{static_cast<int>(ep::Variant::Auto)};
+std::atomic<int> g_slab{0};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -74,6 +75,7 @@ int current_device(ep::Budget* b) {
   if (!d.gfx950) return fail(EP_ERR_UNSUPPORTED, "libep is built for gfx950 only");
   b->device_cus = d.cus;
   b->num_cus = num_cus_setting();
+  b->slab_vpl = g_slab.load();
   return EP_OK;
 }
 
@@ -140,6 +142,19 @@ const char* ep_get_variant(void) {
     default: return "auto";
   }
 }
+
+int ep_set_slab(int vectors_per_lane) {
+  static const int ok[] = {0, 1, 2, 4, 7, 8, 14, 16};
+  for (int v : ok) {
+    if (v == vectors_per_lane) {
+      g_slab.store(v);
+      return EP_OK;
+    }
+  }
+  return fail(EP_ERR_UNSUPPORTED, "ep_set_slab: %d is not one of 0, 1, 2, 4, 7, 8, 14, 16", vectors_per_lane);
+}
+
+int ep_get_slab(void) { return g_slab.load(); }
 
 size_t ep_layout_workspace_bytes(int T, int k, int E) {
   if (T <= 0 || k < 1 || k > EP_MAX_TOPK || E < 1 || E > EP_MAX_EXPERTS) return 0;

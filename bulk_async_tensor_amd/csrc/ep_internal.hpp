@@ -13,6 +13,7 @@ enum class Variant : int { Auto = 0, Vgpr = 1, Vgpr2 = 2, Lds1 = 3, Lds2 = 4, Vg
 struct Budget {
   int num_cus;     // > 0: persistent grid of this many workgroups, one per CU
   int device_cus;  // compute units of the current device
+  int slab_vpl;    // 16-byte vectors per lane per row slab (0: the kernel's default)
 };
 
 // One CU holds 160 KiB of LDS; a workgroup that asks for more than half of it

@@ -1,0 +1,135 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+  python -m bulk_async_tensor_amd.profsum trace <kernel_stats.csv> <bench.log> --command "..."
+      kernel-trace statistics of our kernels beside the per-launch times the
+      benchmark measured with HIP events in the same run.
+
+  python -m bulk_async_tensor_amd.profsum hbm <fetch_counter_collection.csv> <write_counter_collection.csv>
+          --kernel dispatch|combine|layout --workload NAME --out FILE --command "..."
+      HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+      each scaled by what the same counter reads for the copy probe, which
+      reads and writes exactly --copy-bytes (default 256 MiB).
+"""
+
+import argparse
+import csv
+import json
+import statistics
+import sys
+
+from .build import kernel_source_hash
+
+KINDS = {
+    "layout": ("layout_",),
+    "dispatch": ("dispatch_",),
+    "combine": ("combine_",),
+    "copy_probe": ("bw_kernel<0",),
+}
+
+
+def kind_of(name):
+    short = name.replace("(anonymous namespace)", "anon").split("(")[0]
+    if "ep::" not in short:
+        return None
+    for kind, keys in KINDS.items():
+        if any(k in short for k in keys):
+            return kind
+    return None
+
+
+def trace(args):
+    rows = list(csv.DictReader(open(args.stats)))
+    bench = None
+    for line in open(args.bench_log):
+        line = line.strip()
+        if line.startswith("{") and '"metric"' in line:
+            bench = json.loads(line)
+    out = [f"# rocprofv3 kernel trace: {args.title}", f"# command: {args.command}", "",
+           f"{'kernel':<60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in rows:
+        k = kind_of(r["Name"])
+        if k is None:
+            continue
+        nm = r["Name"].replace("ep::(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        out.append(f"{nm[:60]:<60s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    if bench:
+        out += ["", "same run, HIP events on the launch stream (bench.py, ms per launch):"]
+        out.append("  " + json.dumps(bench.get("kernel_ms")))
+        out.append(f"  roofline: {json.dumps(bench.get('roofline'))}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
+def per_kind(path, counter):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = kind_of(r["Kernel_Name"])
+        if k is not None:
+            vals.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def hbm(args):
+    fetch, nf = per_kind(args.fetch, "FETCH_SIZE")
+    write, nw = per_kind(args.write, "WRITE_SIZE")
+    copy_kib = args.copy_bytes / 1024.0
+    f_scale = copy_kib / fetch["copy_probe"]
+    w_scale = copy_kib / write["copy_probe"]
+    k = args.kernel
+    read_b = fetch[k] * f_scale * 1024.0
+    write_b = write[k] * w_scale * 1024.0
+    lines = [
+        f"# HBM traffic per launch of ep_{k} on the {args.workload} workload (rocprofv3 --pmc)",
+        f"# command (FETCH_SIZE pass): {args.command_fetch}",
+        f"# command (WRITE_SIZE pass): {args.command_write}",
+        f"# summarised by: python -m bulk_async_tensor_amd.profsum hbm ...",
+        f"kernel: ep_{k}",
+        f"workload: {args.workload}",
+        f"kernel_sources: {kernel_source_hash()}",
+        f"launches_fetch: {nf.get(k, 0)}",
+        f"launches_write: {nw.get(k, 0)}",
+        f"fetch_kib_per_launch: {fetch[k]:.1f}",
+        f"write_kib_per_launch: {write[k]:.1f}",
+        f"copy_probe_bytes: {args.copy_bytes}",
+        f"copy_probe_fetch_kib: {fetch['copy_probe']:.1f}",
+        f"copy_probe_write_kib: {write['copy_probe']:.1f}",
+        f"fetch_scale: {f_scale:.5f}",
+        f"write_scale: {w_scale:.5f}",
+        f"hbm_read_bytes_per_launch: {read_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {read_b + write_b:.0f}",
+    ]
+    if args.algorithmic:
+        lines.append(f"algorithmic_bytes_per_launch: {args.algorithmic}")
+        lines.append(f"traffic_over_algorithmic: {(read_b + write_b) / args.algorithmic:.4f}")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats")
+    t.add_argument("bench_log")
+    t.add_argument("--title", default="")
+    t.add_argument("--command", default="")
+    h = sub.add_parser("hbm")
+    h.add_argument("fetch")
+    h.add_argument("write")
+    h.add_argument("--kernel", required=True, choices=["layout", "dispatch", "combine"])
+    h.add_argument("--workload", required=True)
+    h.add_argument("--out", required=True)
+    h.add_argument("--copy-bytes", type=int, default=256 << 20)
+    h.add_argument("--algorithmic", type=int, default=0)
+    h.add_argument("--command-fetch", default="")
+    h.add_argument("--command-write", default="")
+    args = p.parse_args(argv)
+    trace(args) if args.mode == "trace" else hbm(args)
+
+
+if __name__ == "__main__":
+    main()

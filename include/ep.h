@@ -69,8 +69,12 @@ enum {
  * launch a persistent grid of n workgroups, each holding more than half a
  * CU's LDS so that no two share a CU (the hardware spreads consecutive
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
- * launch.  n == 0: an ordinary grid over the whole device.  The initial
- * value comes from the environment variable EP_NUM_CUS (default 0).
+ * launch.  n == 0: no budget; the library picks the launch per kernel --
+ * an ordinary grid over the whole device, except that a dispatch of at
+ * least 2048 work units runs persistent on 64 CUs (its traffic is 8/9
+ * writes, and HBM write throughput peaks with about a quarter of the CUs
+ * issuing them).  The initial value comes from the environment variable
+ * EP_NUM_CUS (default 0).
  * Returns EP_OK, or EP_ERR_INVALID_ARG for n < 0 or n > 4096.
  */
 int ep_set_num_cus(int n);
@@ -91,6 +95,19 @@ int ep_get_num_cus(void);
  */
 int ep_set_variant(const char* name);
 const char* ep_get_variant(void);
+
+/*
+ * Staging geometry (process-wide): the row slab a wave moves per work unit,
+ * in 16-byte vectors per lane (one vector per lane = 1 KiB per wave).
+ * 0 = each kernel's default (dispatch: the whole row when it is at most
+ * 8 KiB, else slabs of at most 8 KiB -- half rows at H = 7168; combine:
+ * 2 KiB per source row).  Accepted: 0, 1, 2, 4, 7, 8, 14, 16; a kernel
+ * rounds a value down to the sizes it is compiled for (combine: 1, 2, 4).
+ * The choice changes only speed, never results.  Returns EP_OK or
+ * EP_ERR_UNSUPPORTED.
+ */
+int ep_set_slab(int vectors_per_lane);
+int ep_get_slab(void);
 
 /* Bytes of scratch ep_layout needs for (T, k, E); 0 for T == 0. */
 size_t ep_layout_workspace_bytes(int T, int k, int E);

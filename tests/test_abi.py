@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -58,6 +58,14 @@ def test_num_cus_and_variant_settings(lib):
         assert lib.ep_set_variant(v.encode()) == 0
         assert lib.ep_get_variant().decode() == v
     assert lib.ep_set_variant(b"auto") == 0
+
+
+def test_slab_setting(lib):
+    for v in (0, 1, 2, 4, 7, 8, 14, 16):
+        assert lib.ep_set_slab(v) == 0 and lib.ep_get_slab() == v
+    for v in (-1, 3, 5, 32):
+        assert lib.ep_set_slab(v) == ep.EP_ERR_UNSUPPORTED
+    assert lib.ep_set_slab(0) == 0
 
 
 def test_workspace_bytes(lib):

@@ -153,6 +153,25 @@ def test_dispatch_ragged_rows(variant, H, k, budget):
     np.testing.assert_array_equal(got, oracle.dispatch(wl.x, lay["dest_row"], T * k))
 
 
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("slab", [1, 2, 4, 7, 8, 14, 16])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_dispatch_slab_sizes(variant, slab, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_slab(slab)
+    ep.ep_set_num_cus(budget)
+    try:
+        wl = workload("train")
+        got = run_dispatch(wl, oracle_layout("train")["dest_row"], wl.config.T * wl.config.k)
+        np.testing.assert_array_equal(got, oracle_recv("train"))
+        wr = make_workload("prefill", seed=slab, T=53, H=7176, E=16, k=6)
+        lay = oracle.layout(wr.topk_idx, 16)
+        got = run_dispatch(wr, lay["dest_row"], 53 * 6)
+        np.testing.assert_array_equal(got, oracle.dispatch(wr.x, lay["dest_row"], 53 * 6))
+    finally:
+        ep.ep_set_slab(0)
+
+
 def test_dispatch_skips_rows_outside_recv():
     wl = make_workload("decode", T=64)
     lay = oracle.layout(wl.topk_idx, 256)
@@ -221,6 +240,26 @@ def test_combine_ragged_rows(variant, H, k, budget):
     ref = oracle.combine(y, dest, wl.topk_w)
     got = run_combine(wl, y, dest)
     assert_combine_close(got, ref)
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2"])
+@pytest.mark.parametrize("slab", [1, 2, 4])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_combine_slab_sizes(variant, slab, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_slab(slab)
+    ep.ep_set_num_cus(budget)
+    try:
+        wl = workload("train")
+        got = run_combine(wl, expert_outputs("train"), oracle_layout("train")["dest_row"])
+        assert_combine_close(got, oracle_out("train"))
+        for H, k in [(7176, 8), (4104, 3)]:
+            wr = make_workload("combine_stress", seed=H + slab, T=31, H=H, E=32, k=k)
+            lay = oracle.layout(wr.topk_idx, 32)
+            got = run_combine(wr, wr.y, lay["dest_row"])
+            assert_combine_close(got, oracle.combine(wr.y, lay["dest_row"], wr.topk_w))
+    finally:
+        ep.ep_set_slab(0)
 
 
 def test_combine_unnormalised_weights_and_signed_zero():
