@@ -46,6 +46,9 @@ def parse_args():
     p.add_argument("--sweep-slabs", default="0", help="slab sizes (vectors per lane) to sweep; 0 = default")
     p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
     p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
+    p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
+    p.add_argument("--overlap", default=None,
+                   help="CU-partitioned overlap with a bf16 GEMM, JSONL to this file (budgets from --sweep-budgets)")
     p.add_argument("--kernels-only", action="store_true",
                    help="a few launches of each kernel and of a 256 MiB copy probe (for counter passes)")
     p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
@@ -65,6 +68,7 @@ class Setup:
         self.ep = ep
         self.torch = torch
         self.stream = stream
+        self.gather = False  # True: dispatch through ep_dispatch_rows (gather form)
         dev = torch.device("cuda:0")
         wl = make_workload(name)
         self.wl = wl
@@ -110,7 +114,10 @@ class Setup:
 
     def dispatch(self):
         if self.do_dispatch:
-            self.ep.ep_dispatch(self.x, self.dest_row, self.recv, stream=self.stream)
+            if self.gather:
+                self.ep.ep_dispatch_rows(self.x, self.src_token, self.recv, stream=self.stream)
+            else:
+                self.ep.ep_dispatch(self.x, self.dest_row, self.recv, stream=self.stream)
 
     def combine(self):
         self.ep.ep_combine(self.y, self.dest_row, self.w, self.out, stream=self.stream)
@@ -251,7 +258,8 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 ep.ep_set_num_cus(budget)
             s.stream = stream
             st = stream if stream is not None else torch.cuda.current_stream()
-            for mode, label in ([(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32")] if probes else []):
+            for mode, label in ([(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32"), (4, "mix8to1"),
+                                 (5, "mix1to8")] if probes else []):
                 for _ in range(3):
                     ep.ep_bw_probe(mode, a, bb, n, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,13 +269,15 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 e1.record(st)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
-                moved = 2 * n if mode == 0 else n
+                moved = 2 * n if mode == 0 else (n + n // 8) if mode in (4, 5) else n
                 rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
             for v in variants:
                 for slab in slabs:
-                    ep.ep_set_variant(v)
+                    # "rows" / "rows_nt": the gather-form dispatch (cacheable / streaming x loads)
+                    s.gather = v.startswith("rows")
+                    ep.ep_set_variant({"rows": "auto", "rows_nt": "vgpr_cached"}.get(v, v))
                     ep.ep_set_slab(slab)
                     ms, per = s.run(steps, warmup)
                     rec = {"kind": "step", "workload": name, "variant": v, "slab": slab, "num_cus": str(tok),
@@ -276,6 +286,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                     fh.write(json.dumps(rec) + "\n")
                     print(json.dumps(rec), flush=True)
             ep.ep_set_slab(0)
+            s.gather = False
             s.stream = None
             if stream is not None:
                 torch.cuda.synchronize()
@@ -296,7 +307,8 @@ def probe_sweep(path, budgets):
     b = torch.empty_like(a)
     cases = [(0, d, 0) for d in range(3)] + [(2, d, 0) for d in range(3)]
     cases += [(1, d, p) for d in range(3) for p in range(6)] + [(3, 0, p) for p in range(6)]
-    names = {0: "copy", 1: "read", 2: "write", 3: "read_lds"}
+    cases += [(4, 0, 0), (5, 0, 0)]
+    names = {0: "copy", 1: "read", 2: "write", 3: "read_lds", 4: "mix8to1", 5: "mix1to8"}
     pols = {0: "nt", 1: "none", 2: "sc0", 3: "sc1", 4: "sc0sc1", 5: "nt_buf"}
     with open(path, "a") as fh:
         for budget in budgets:
@@ -312,12 +324,51 @@ def probe_sweep(path, budgets):
                 e1.record()
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
-                moved = 2 * n if op == 0 else n
+                moved = 2 * n if op == 0 else (n + n // 8) if op >= 4 else n
                 rec = {"kind": "probe", "op": names[op], "depth": 8 << d, "policy": pols[p], "num_cus": budget,
                        "ms": round(ms, 4), "GBs": round(moved / ms / 1e6, 1)}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
     ep.ep_set_num_cus(0)
+
+
+def graph_step(s, steps, warmup):
+    """One whole step captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: the step's device time without per-launch host overhead.
+    Returns (ms per replayed step, ms per eager step)."""
+    import torch
+
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            s.layout()
+            s.dispatch()
+            s.combine()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.layout()
+        s.dispatch()
+        s.combine()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        s.layout()
+        s.dispatch()
+        s.combine()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / steps
+    return ms_graph, ms_eager
 
 
 def kernels_only(s, launches=5, copy_bytes=256 << 20):
@@ -342,6 +393,97 @@ def kernels_only(s, launches=5, copy_bytes=256 << 20):
                       "bytes": s.bytes}), flush=True)
 
 
+def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
+    """Row movement on a stream masked to n CUs beside a bf16 GEMM on a stream
+    masked to the other CUs (the pages' premise: the copy kernels leave the
+    remaining units to computation).  Each side alone and concurrently; also
+    both concurrently without a partition."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    s = Setup(name)
+    dev = torch.device("cuda:0")
+    A = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+    B = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+    C = torch.empty((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+    n_all = torch.cuda.get_device_properties(0).multi_processor_count
+    flop = 2.0 * gemm_n ** 3
+
+    def timed(jobs):
+        """jobs: list of (stream, fn, reps); all start together; returns ms per stream."""
+        torch.cuda.synchronize()
+        evs = []
+        for st, fn, reps in jobs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            evs.append((e0, e1))
+        # record the starts first so the streams begin together
+        for (st, fn, reps), (e0, _) in zip(jobs, evs):
+            e0.record(st)
+        for (st, fn, reps), (_, e1) in zip(jobs, evs):
+            with torch.cuda.stream(st):
+                for _ in range(reps):
+                    fn(st)
+            e1.record(st)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    def gemm(st):
+        torch.matmul(A, B, out=C)
+
+    def step(st):
+        s.stream = st
+        s.layout()
+        s.dispatch()
+        s.combine()
+
+    default = torch.cuda.current_stream()
+    for _ in range(3):
+        gemm(default)
+        step(default)
+    g_full = timed([(default, gemm, 10)])[0] / 10
+    s_full = timed([(default, step, steps)])[0] / steps
+    reps_g = gemm_reps or max(4, int(round(steps * s_full / g_full)))
+    recs = []
+    with open(path, "a") as fh:
+        base = {"kind": "overlap_base", "workload": name, "gemm_n": gemm_n, "gemm_ms_all_cus": g_full,
+                "gemm_TFLOPs_all_cus": flop / g_full / 1e9, "step_ms_all_cus": s_full}
+        fh.write(json.dumps(base) + "\n")
+        print(json.dumps(base), flush=True)
+        # no partition: both on ordinary streams at once
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        t_g, t_s = timed([(s1, gemm, reps_g), (s2, step, steps)])
+        rec = {"kind": "overlap", "partition": "none", "gemm_ms": t_g / reps_g, "step_ms": t_s / steps,
+               "gemm_slowdown": (t_g / reps_g) / g_full, "step_slowdown": (t_s / steps) / s_full}
+        fh.write(json.dumps(rec) + "\n")
+        print(json.dumps(rec), flush=True)
+        for n in comm_cus_list:
+            comm = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n)))
+            comp = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n, n_all)))
+            for _ in range(2):
+                step(comm)
+                with torch.cuda.stream(comp):
+                    gemm(comp)
+            g_alone = timed([(comp, gemm, reps_g)])[0] / reps_g
+            s_alone = timed([(comm, step, steps)])[0] / steps
+            t_g, t_s = timed([(comp, gemm, reps_g), (comm, step, steps)])
+            rec = {"kind": "overlap", "partition": f"{n}/{n_all - n}", "comm_cus": n,
+                   "gemm_ms_alone_on_rest": g_alone, "step_ms_alone_on_n": s_alone,
+                   "gemm_ms": t_g / reps_g, "step_ms": t_s / steps,
+                   "gemm_slowdown_vs_alone_on_rest": (t_g / reps_g) / g_alone,
+                   "gemm_slowdown_vs_all_cus": (t_g / reps_g) / g_full,
+                   "step_slowdown_vs_alone_on_n": (t_s / steps) / s_alone,
+                   "step_GBs_concurrent": s.step_bytes / (t_s / steps) / 1e6,
+                   "gemm_TFLOPs_concurrent": flop / (t_g / reps_g) / 1e9}
+            fh.write(json.dumps(rec) + "\n")
+            print(json.dumps(rec), flush=True)
+            torch.cuda.synchronize()
+            s.stream = None
+            ep.ep_stream_destroy(comm)
+            ep.ep_stream_destroy(comp)
+    s.stream = None
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -359,6 +501,9 @@ def main():
     budgets = args.sweep_budgets.split(",")
     if args.probe_sweep:
         probe_sweep(args.probe_sweep, [int(b) for b in budgets])
+        return
+    if args.overlap:
+        overlap(args.overlap, args.workload, [int(b) for b in budgets], max(20, args.steps // 4))
         return
     if args.sweep:
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
@@ -441,6 +586,11 @@ def main():
             "algorithmic_bytes": s.bytes[dom],
         },
     }
+    if args.graph:
+        ms_g, ms_e = graph_step(s, args.steps, args.warmup)
+        line["graph_replay"] = {"ms_per_step": round(ms_g, 5), "eager_ms_per_step": round(ms_e, 5),
+                                "value": round(s.step_bytes / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                "tokens_per_s": round(s.T / (ms_g * 1e-3), 1)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "ep_layout_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "ep_layout": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p]),
     "ep_dispatch": (_c_int, [_p, _c_int, _c_int, _p, _c_int, _p, _c_i64, _p]),
+    "ep_dispatch_rows": (_c_int, [_p, _c_int, _c_int, _p, _p, _c_i64, _p]),
     "ep_combine": (_c_int, [_p, _c_i64, _c_int, _p, _p, _c_int, _c_int, _p, _p]),
     "ep_status_string": (ctypes.c_char_p, [_c_int]),
     "ep_last_error": (ctypes.c_char_p, []),
@@ -204,6 +205,21 @@ def ep_dispatch(x, dest_row, recv, stream=None):
     k = dest_row.shape[1]
     _check(lib().ep_dispatch(_ptr(x), T, H, _ptr(dest_row), k, _ptr(recv), recv.shape[0], _stream(stream)),
            "ep_dispatch")
+    return recv
+
+
+def ep_dispatch_rows(x, src_token, recv, stream=None):
+    """recv[r] = x[src_token[r]] for x [T, H] bf16, src_token [R] int32, recv [R, H] bf16."""
+    import torch
+
+    _device_tensor(x, "x", torch.bfloat16)
+    _device_tensor(src_token, "src_token", torch.int32)
+    _device_tensor(recv, "recv", torch.bfloat16)
+    T, H = x.shape
+    if recv.dim() != 2 or recv.shape[1] != H or src_token.numel() < recv.shape[0]:
+        raise ValueError("recv must be [R, H] and src_token hold at least R entries")
+    _check(lib().ep_dispatch_rows(_ptr(x), T, H, _ptr(src_token), _ptr(recv), recv.shape[0], _stream(stream)),
+           "ep_dispatch_rows")
     return recv
 
 

@@ -330,6 +330,42 @@ int choose_vpl(int row_vec, int cap, int requested) {
   return cap;
 }
 
+// Gather form of the same copy: recv[r, :] = x[src_token[r], :].  Waves take
+// (receive row, slab) units in order, so the receive buffer is written as
+// one sequential stream; each token row is read k times, mostly from the
+// caches (x is 58.7 MB at the training shape, below the 256 MB Infinity
+// Cache).  CL = true keeps the x loads cacheable.
+template <int VPL, bool EVEN, bool CL>
+__global__ __launch_bounds__(1024) void dispatch_rows_kernel(const u32x4* __restrict__ x, u32x4* __restrict__ recv,
+                                                            const int32_t* __restrict__ src_token, int T,
+                                                            int row_vec, int nslab, int units) {
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  for (int u = blockIdx.x * wpg + wave_in_group(); u < units; u += stride) {
+    const Unit un = unit_of<VPL>(u, nslab, row_vec, lane);  // un.t is the receive row here
+    const int t = src_token[un.t];
+    if ((unsigned)t >= (unsigned)T) continue;
+    u32x4 v[VPL];
+    load_slab<VPL, EVEN, !CL>(v, x + (int64_t)t * row_vec, un, row_vec);
+    store_one<VPL, EVEN, true>(v, recv + un.t * row_vec, un, row_vec);
+  }
+}
+
+using RowsFn = void (*)(const u32x4*, u32x4*, const int32_t*, int, int, int, int);
+
+template <bool EVEN, bool CL>
+RowsFn rows_pick(int vpl) {
+  switch (vpl) {
+    case 2: return dispatch_rows_kernel<2, EVEN, CL>;
+    case 4: return dispatch_rows_kernel<4, EVEN, CL>;
+    case 7: return dispatch_rows_kernel<7, EVEN, CL>;
+    case 8: return dispatch_rows_kernel<8, EVEN, CL>;
+    case 14: return dispatch_rows_kernel<14, EVEN, CL>;
+    default: return dispatch_rows_kernel<16, EVEN, CL>;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
@@ -385,6 +421,43 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x),
                      static_cast<u32x4*>(recv), dest_row, recv_rows, row_vec, nslab, k, units);
+  return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* src_token,
+                                void* recv, int64_t recv_rows, hipStream_t stream) {
+  const int row_vec = H / 8;
+  const bool even = row_vec % kWave == 0;
+  const int vpl = choose_vpl(row_vec, b.slab_vpl > 0 ? 16 : 8, b.slab_vpl);
+  const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
+  if (recv_rows * nslab > INT32_MAX) return hipErrorInvalidValue;
+  const int units = (int)recv_rows * nslab;
+  // "vgpr_cached" selects streaming (nt) loads of x; every other variant keeps them cacheable
+  const bool cl = v != Variant::VgprCached;
+  RowsFn fn = even ? (cl ? rows_pick<true, true>(vpl) : rows_pick<true, false>(vpl))
+                   : (cl ? rows_pick<false, true>(vpl) : rows_pick<false, false>(vpl));
+  int wpg, grid;
+  size_t lds_bytes = 0;
+  if (b.num_cus > 0) {
+    wpg = 16;
+    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    lds_bytes = kExclusiveLds;
+  } else {
+    wpg = 4;
+    grid = (units + wpg - 1) / wpg;
+    if (grid > b.device_cus * 8) grid = b.device_cus * 8;
+  }
+  if (grid < 1) grid = 1;
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x),
+                     static_cast<u32x4*>(recv), src_token, T, row_vec, nslab, units);
   return hipGetLastError();
 }
 

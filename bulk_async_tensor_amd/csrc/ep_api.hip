@@ -210,6 +210,27 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
   return EP_OK;
 }
 
+int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void* recv, int64_t recv_rows,
+                     void* stream) {
+  if (T < 0) return fail(EP_ERR_INVALID_ARG, "ep_dispatch_rows: T = %d < 0", T);
+  int rc = check_rows(H, recv_rows, "ep_dispatch_rows");
+  if (rc) return rc;
+  if (recv_rows > 0 && (!x || !src_token || !recv))
+    return fail(EP_ERR_INVALID_ARG, "ep_dispatch_rows: null x/src_token/recv");
+  if ((x && !aligned(x, 16)) || (recv && !aligned(recv, 16)))
+    return fail(EP_ERR_ALIGNMENT, "ep_dispatch_rows: bf16 tensor not 16-byte aligned");
+  if (src_token && !aligned(src_token, 4))
+    return fail(EP_ERR_ALIGNMENT, "ep_dispatch_rows: src_token not 4-byte aligned");
+  if (T == 0 || recv_rows == 0) return EP_OK;
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_dispatch_rows(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, src_token, recv,
+                                          recv_rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_dispatch_rows launch");
+  return EP_OK;
+}
+
 int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row, const float* topk_w, int T, int k,
                void* out, void* stream) {
   int rc = check_common(T, k, H, "ep_combine");
@@ -247,11 +268,13 @@ const char* ep_status_string(int code) {
 const char* ep_last_error(void) { return g_err; }
 
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
-  if (mode < 0 || (mode & ~0x733) != 0 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
+  if (mode < 0 || (mode & ~0x737) != 0 || (mode & 7) > 5 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
     return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode 0x%x", mode);
+  if ((mode & 7) >= 4 && bytes % 8192 != 0)
+    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mixed operations need bytes %% 8192 == 0");
   if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: bytes must be a multiple of 16");
-  if (((mode & 3) != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
-  if ((mode & 3) != 0 && (mode & 3) != 2 && bytes > ((int64_t)1 << 40))
+  if (((mode & 7) != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
+  if (((mode & 7) == 1 || (mode & 7) == 3) && bytes > ((int64_t)1 << 40))
     return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: size");
   if ((src && !aligned(src, 16)) || !aligned(dst, 16)) return fail(EP_ERR_ALIGNMENT, "ep_bw_probe: alignment");
   if (bytes == 0) return EP_OK;

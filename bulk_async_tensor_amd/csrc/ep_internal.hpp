@@ -33,6 +33,9 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row,
                            int k, void* recv, int64_t recv_rows, hipStream_t stream);
 
+hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* src_token,
+                                void* recv, int64_t recv_rows, hipStream_t stream);
+
 // ---- combine (combine.hip)
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream);

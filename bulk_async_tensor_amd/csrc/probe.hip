@@ -86,6 +86,33 @@ __global__ __launch_bounds__(1024) void bw_kernel(const u32x4* __restrict__ src,
   if ((OP == 1 || OP == 3) && sum[0] == 0x9e3779b9u && sum[1] == 0x7f4a7c15u && sum[2] == 0x94d049bbu) dst[0] = sum;
 }
 
+// Mixed-ratio streams.  DIR 0 (8:1, the combine mix): a wave reads 8 KiB
+// contiguous and writes 1 KiB.  DIR 1 (1:8, the dispatch mix): a wave reads
+// 1 KiB and writes 8 KiB contiguous.  nvec counts the larger side (multiple
+// of 512 vectors).
+template <int DIR>
+__global__ __launch_bounds__(1024) void bw_mix_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                      int64_t nvec) {
+  const int lane = lane_id();
+  const int64_t wpg = blockDim.x >> 6;
+  const int64_t nchunk = nvec / (8 * kWave);
+  for (int64_t q = (int64_t)blockIdx.x * wpg + wave_in_group(); q < nchunk; q += (int64_t)gridDim.x * wpg) {
+    if constexpr (DIR == 0) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ld16<true>(src + q * 8 * kWave + i * kWave + lane);
+      u32x4 x = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) x ^= v[i];
+      st16<true>(dst + q * kWave + lane, x);
+    } else {
+      const u32x4 v = ld16<true>(src + q * kWave + lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st16<true>(dst + q * 8 * kWave + i * kWave + lane, v ^ u32x4{(uint32_t)i, 0u, 0u, 0u});
+    }
+  }
+}
+
 using BwFn = void (*)(const u32x4*, u32x4*, int64_t);
 
 template <int OP, int D>
@@ -131,16 +158,19 @@ __global__ __launch_bounds__(64) void placement_kernel(int32_t* __restrict__ out
 }  // namespace
 
 hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream) {
-  const int op = mode & 3;
+  const int op = mode & 7;
   const int depth_code = (mode >> 4) & 3;
   const int pol = (mode >> 8) & 7;
   const int depth = depth_code == 1 ? 16 : depth_code == 2 ? 32 : 8;
   if (depth_code == 3 || pol > 5) return hipErrorInvalidValue;
   const int64_t nvec = bytes / 16;
+  if (op > 5) return hipErrorInvalidValue;
   BwFn fn = op == 0 ? bw_pick_depth<0>(depth_code, 0)
           : op == 1 ? bw_pick_depth<1>(depth_code, pol)
           : op == 2 ? bw_pick_depth<2>(depth_code, 0)
-                    : bw_pick_depth<3>(depth_code, pol);
+          : op == 3 ? bw_pick_depth<3>(depth_code, pol)
+          : op == 4 ? (BwFn)bw_mix_kernel<0>
+                    : (BwFn)bw_mix_kernel<1>;
   const size_t per_wave = op == 3 ? (size_t)depth * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds = 0;

@@ -155,6 +155,23 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
                 int64_t recv_rows, void* stream);
 
 /*
+ * ep_dispatch_rows -- the same copy in gather form:
+ *   recv[r, :] = x[src_token[r], :] for r < recv_rows
+ * with src_token from ep_layout (then recv_rows = offsets[E]); rows whose
+ * src_token is outside [0, T) are untouched.  With a layout of valid ids
+ * the result equals ep_dispatch's.  The receive buffer is written as one
+ * sequential stream and each token row is read k times (from the caches
+ * when x fits in them); which form is faster depends on the shape.
+ *   x          bf16 [T, H]
+ *   src_token  int32 [recv_rows]
+ *   recv       bf16 [recv_rows, H]
+ * Limits: 0 <= recv_rows < 2^31.  The variant "vgpr_cached" selects
+ * streaming (non-temporal) loads of x; every other keeps them cacheable.
+ */
+int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void* recv, int64_t recv_rows,
+                     void* stream);
+
+/*
  * ep_combine -- the way back from the expert-grouped layout, which the
  * pages do not spell out; the plainest reading is used:
  *   out[t, :] = bf16_rne( sum_{j=0..k-1} w[t, j] * f32(y[dest_row[t*k+j], :]) )
@@ -182,12 +199,17 @@ const char* ep_last_error(void);
  * ep_bw_probe: a plain streaming kernel under the same compute-unit budget
  * as dispatch/combine, giving the achievable HBM ceiling at that budget.
  * `mode` packs three fields:
- *   bits [1:0]  operation: 0 copy dst[i] = src[i] (reads and writes `bytes`);
+ *   bits [2:0]  operation: 0 copy dst[i] = src[i] (reads and writes `bytes`);
  *               1 read src (dst must hold 16 bytes; written only for one
  *               improbable checksum, which keeps the reads alive);
  *               2 write a pattern to dst (src unused);
  *               3 read src into per-wave LDS slices with direct-to-LDS loads
- *               (dst as for 1)
+ *               (dst as for 1);
+ *               4 mixed 8:1 -- read `bytes` of src, write bytes/8 of dst
+ *               (each wave: 8 KiB in, 1 KiB out);
+ *               5 mixed 1:8 -- read bytes/8 of src, write `bytes` of dst
+ *               (each wave: 1 KiB in, 8 KiB out); 4 and 5 need
+ *               bytes % 8192 == 0 and ignore depth and policy
  *   bits [5:4]  depth: 16-byte vectors in flight per lane, 0 -> 8, 1 -> 16,
  *               2 -> 32 (3 is invalid)
  *   bits [10:8] cache policy of the loads of operations 1 and 3: 0 nt,

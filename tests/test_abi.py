@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -163,6 +163,19 @@ def test_combine_rejects(lib, kw, code):
     assert combine(lib, **kw) == code
 
 
+def test_dispatch_rows_rejects(lib):
+    f = lib.ep_dispatch_rows
+    assert f(A16, -1, 1024, A4, A16, 32, None) == ep.EP_ERR_INVALID_ARG
+    assert f(A16, 16, 1020, A4, A16, 32, None) == ep.EP_ERR_INVALID_ARG
+    assert f(A16, 16, 1024, A4, A16, -1, None) == ep.EP_ERR_INVALID_ARG
+    assert f(None, 16, 1024, A4, A16, 32, None) == ep.EP_ERR_INVALID_ARG
+    assert f(A16, 16, 1024, None, A16, 32, None) == ep.EP_ERR_INVALID_ARG
+    assert f(A16 + 4, 16, 1024, A4, A16, 32, None) == ep.EP_ERR_ALIGNMENT
+    assert f(A16, 16, 1024, ODD, A16, 32, None) == ep.EP_ERR_ALIGNMENT
+    assert f(A16, 0, 1024, A4, A16, 32, None) == 0
+    assert f(None, 16, 1024, None, None, 0, None) == 0
+
+
 def test_empty_batches_are_host_no_ops(lib):
     # T == 0 returns before touching the device
     assert dispatch(lib, T=0, x=None, dest=None, recv=None) == 0
@@ -176,6 +189,8 @@ def test_probe_rejects(lib):
     assert lib.ep_bw_probe(0x30, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # depth code 3
     assert lib.ep_bw_probe(0x601, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # policy 6
     assert lib.ep_bw_probe(0x1000, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # unknown bit
+    assert lib.ep_bw_probe(6, A16, A16, 8192, None) == ep.EP_ERR_INVALID_ARG  # no operation 6
+    assert lib.ep_bw_probe(4, A16, A16, 4096, None) == ep.EP_ERR_INVALID_ARG  # mixed needs 8 KiB multiples
     assert lib.ep_bw_probe(0, A16, A16, 1000 + 4, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_bw_probe(0, None, A16, 1024, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_bw_probe(0, A16 + 4, A16, 1024, None) == ep.EP_ERR_ALIGNMENT

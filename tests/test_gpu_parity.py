@@ -172,6 +172,42 @@ def test_dispatch_slab_sizes(variant, slab, budget):
         ep.ep_set_slab(0)
 
 
+@pytest.mark.parametrize("name", DISPATCH_CONFIGS)
+@pytest.mark.parametrize("variant,budget", [("auto", 0), ("vgpr_cached", 0), ("auto", 24), ("auto", 64)])
+def test_dispatch_rows_matches(name, variant, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    wl = workload(name)
+    lay = oracle_layout(name)
+    R = wl.config.T * wl.config.k
+    recv = torch.full((R, wl.config.H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep.ep_dispatch_rows(to_bf16_x(wl), to_dev(lay["src_token"]), recv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(from_dev_bf16(recv), oracle_recv(name))
+
+
+@pytest.mark.parametrize("H", [8, 520, 7176])
+def test_dispatch_rows_ragged_and_invalid(H):
+    wl = make_workload("prefill", seed=H, T=41, H=H, E=16, k=3)
+    lay = oracle.layout(wl.topk_idx, 16)
+    src = lay["src_token"].copy()
+    src[5] = -1
+    src[7] = 41  # == T: out of range
+    fill = 0x7E57
+    recv = torch.full((41 * 3, H), fill, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep.ep_dispatch_rows(to_bf16_x(wl), to_dev(src), recv)
+    torch.cuda.synchronize()
+    # expected: the oracle's dispatch without the entries of rows 5 and 7
+    dest = lay["dest_row"].copy()
+    dest[np.isin(dest, [5, 7])] = -1
+    ref = oracle.dispatch(wl.x, dest, 41 * 3, recv=np.full((41 * 3, H), fill, dtype=np.uint16))
+    np.testing.assert_array_equal(from_dev_bf16(recv), ref)
+
+
+def to_bf16_x(wl):
+    return to_dev_bf16(wl.x)
+
+
 def test_dispatch_skips_rows_outside_recv():
     wl = make_workload("decode", T=64)
     lay = oracle.layout(wl.topk_idx, 256)
@@ -291,6 +327,26 @@ def test_bw_probe_copies_and_writes():
         assert np.array_equal(v[:, 0], idx & 0xFFFFFFFF) and np.all(v[:, 1] == 0x5A5A5A5A)
 
 
+def test_bw_probe_mixed_ratios():
+    n = 1 << 22  # bytes of the larger side
+    big = torch.randint(-(1 << 31), 1 << 31, (n // 4,), dtype=torch.int32, device=DEV)
+    small = torch.zeros(n // 32, dtype=torch.int32, device=DEV)
+    ep.ep_bw_probe(4, big, small, n)  # 8:1 -- xor of each 8 KiB chunk's vectors
+    torch.cuda.synchronize()
+    b = big.view(-1, 8, 64, 4).cpu().numpy()
+    want = np.bitwise_xor.reduce(b, axis=1).reshape(-1)
+    assert np.array_equal(small.cpu().numpy(), want)
+    out = torch.zeros_like(big)
+    ep.ep_bw_probe(5, small, out, n)  # 1:8 -- each 1 KiB chunk written 8 times (x ^ i in the first word)
+    torch.cuda.synchronize()
+    o = out.view(-1, 8, 64, 4).cpu().numpy()
+    s = small.view(-1, 64, 4).cpu().numpy()
+    for i in range(8):
+        w = s.copy()
+        w[:, :, 0] ^= i
+        assert np.array_equal(o[:, i], w)
+
+
 @pytest.mark.parametrize("budget", [16, 24, 32, 64])
 def test_persistent_grid_gets_distinct_cus(budget):
     ep.ep_set_num_cus(budget)
@@ -333,3 +389,54 @@ def test_cu_masked_stream_confines_work():
     finally:
         torch.cuda.synchronize()
         ep.ep_stream_destroy(stream)
+
+
+@pytest.mark.parametrize("name", ["decode", "tiny"])
+def test_graph_replay_matches_eager(name):
+    """The whole step captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, equals the oracle."""
+    wl = workload(name)
+    c = wl.config
+    idx = to_dev(wl.topk_idx)
+    x = to_dev_bf16(wl.x)
+    w = to_dev(wl.topk_w)
+    R = c.T * c.k
+    lay = {
+        "counts": torch.empty(c.E, dtype=torch.int32, device=DEV),
+        "offsets": torch.empty(c.E + 1, dtype=torch.int32, device=DEV),
+        "dest_row": torch.empty((c.T, c.k), dtype=torch.int32, device=DEV),
+        "src_token": torch.empty(R, dtype=torch.int32, device=DEV),
+        "status": torch.empty(1, dtype=torch.int32, device=DEV),
+    }
+    ws = torch.empty(max(16, ep.ep_layout_workspace_bytes(c.T, c.k, c.E)), dtype=torch.uint8, device=DEV)
+    recv = torch.empty((R, c.H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        ep.ep_layout(idx, c.E, lay["counts"], lay["offsets"], lay["dest_row"], lay["src_token"], lay["status"], ws)
+        ep.ep_dispatch(x, lay["dest_row"], recv)
+        ep.ep_combine(recv, lay["dest_row"], w, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ref_lay = oracle_layout(name)
+    ref_recv = oracle_recv(name)
+    for rep in range(4):
+        # clobber the outputs eagerly so each replay must rewrite them
+        recv.view(torch.int16).fill_(rep)
+        out.view(torch.int16).fill_(rep)
+        lay["dest_row"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(lay["dest_row"].cpu().numpy(), ref_lay["dest_row"])
+        np.testing.assert_array_equal(lay["offsets"].cpu().numpy(), ref_lay["offsets"])
+        np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
+        assert np.array_equal(oracle.bf16_to_f32(from_dev_bf16(out)), oracle.bf16_to_f32(wl.x))
