@@ -47,6 +47,7 @@ def parse_args():
     p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
     p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
     p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
+    p.add_argument("--fused", action="store_true", help="layout and dispatch through ep_layout_dispatch")
     p.add_argument("--overlap", default=None,
                    help="CU-partitioned overlap with a bf16 GEMM, JSONL to this file (budgets from --sweep-budgets)")
     p.add_argument("--kernels-only", action="store_true",
@@ -69,6 +70,7 @@ class Setup:
         self.torch = torch
         self.stream = stream
         self.gather = False  # True: dispatch through ep_dispatch_rows (gather form)
+        self.fused = False   # True: layout and dispatch through ep_layout_dispatch
         dev = torch.device("cuda:0")
         wl = make_workload(name)
         self.wl = wl
@@ -109,11 +111,15 @@ class Setup:
         self.step_bytes = sum(self.bytes.values())
 
     def layout(self):
+        if self.fused and self.do_dispatch:
+            self.ep.ep_layout_dispatch(self.idx, self.E, self.x, self.recv, self.counts, self.offsets,
+                                       self.dest_row, self.src_token, self.status, self.ws, stream=self.stream)
+            return
         self.ep.ep_layout(self.idx, self.E, self.counts, self.offsets, self.dest_row, self.src_token, self.status,
                           self.ws, stream=self.stream)
 
     def dispatch(self):
-        if self.do_dispatch:
+        if self.do_dispatch and not self.fused:
             if self.gather:
                 self.ep.ep_dispatch_rows(self.x, self.src_token, self.recv, stream=self.stream)
             else:
@@ -512,6 +518,7 @@ def main():
 
     ep.ep_set_variant(args.variant)
     s = Setup(args.workload)
+    s.fused = args.fused
     if args.kernels_only:
         kernels_only(s)
         return
@@ -554,7 +561,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "T": s.T, "H": s.H, "E": s.E, "k": s.k, "num_cus": "all",
-                   "variant": ep.ep_get_variant(), "step": "layout+dispatch+combine"},
+                   "variant": ep.ep_get_variant(),
+                   "step": "layout_dispatch+combine" if args.fused else "layout+dispatch+combine"},
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "kernel_GBs": {k: round(s.bytes[k] / (per[k] * 1e6), 1) for k in per if per[k] > 0 and s.bytes[k]},

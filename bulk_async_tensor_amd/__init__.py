@@ -43,6 +43,8 @@ _SIGNATURES = {
     "ep_layout": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p]),
     "ep_dispatch": (_c_int, [_p, _c_int, _c_int, _p, _c_int, _p, _c_i64, _p]),
     "ep_dispatch_rows": (_c_int, [_p, _c_int, _c_int, _p, _p, _c_i64, _p]),
+    "ep_layout_dispatch": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p,
+                                    _c_i64, _p]),
     "ep_combine": (_c_int, [_p, _c_i64, _c_int, _p, _p, _c_int, _c_int, _p, _p]),
     "ep_status_string": (ctypes.c_char_p, [_c_int]),
     "ep_last_error": (ctypes.c_char_p, []),
@@ -187,6 +189,37 @@ def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, s
                         _ptr(status), _ptr(workspace), ws_bytes, _stream(stream)),
         "ep_layout",
     )
+    return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
+
+
+def ep_layout_dispatch(topk_idx, num_experts, x, recv, counts=None, offsets=None, dest_row=None, src_token=None,
+                       status=None, workspace=None, stream=None):
+    """ep_layout then ep_dispatch (one launch for small batches).  Returns the layout dict."""
+    import torch
+
+    _device_tensor(topk_idx, "topk_idx", torch.int32)
+    _device_tensor(x, "x", torch.bfloat16)
+    _device_tensor(recv, "recv", torch.bfloat16)
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    H = x.shape[1]
+    if x.shape[0] != T or recv.dim() != 2 or recv.shape[1] != H:
+        raise ValueError("x must be [T, H] and recv [R, H]")
+    dev = topk_idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = torch.empty(E, **i32) if counts is None else _device_tensor(counts, "counts", torch.int32)
+    offsets = torch.empty(E + 1, **i32) if offsets is None else _device_tensor(offsets, "offsets", torch.int32)
+    dest_row = torch.empty((T, k), **i32) if dest_row is None else _device_tensor(dest_row, "dest_row", torch.int32)
+    src_token = torch.empty(T * k, **i32) if src_token is None else _device_tensor(src_token, "src_token",
+                                                                                   torch.int32)
+    status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
+    need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib().ep_layout_dispatch(_ptr(topk_idx), T, k, E, _ptr(x), H, _ptr(counts), _ptr(offsets),
+                                    _ptr(dest_row), _ptr(src_token), _ptr(status), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(recv), recv.shape[0],
+                                    _stream(stream)), "ep_layout_dispatch")
     return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
 
 

@@ -22,29 +22,11 @@
 // per-lane row-end masks are needed.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "row_io.hpp"
 
 namespace ep {
 
 namespace {
-
-struct Unit {
-  int64_t t;
-  int c0;    // this lane's first vector of the slab
-  int nvec;  // vectors of the slab inside the row (uniform, >= 1)
-};
-
-template <int VPL>
-__device__ __forceinline__ Unit unit_of(int u, int nslab, int row_vec, int lane) {
-  Unit r;
-  const int t = u / nslab;
-  const int s = u - t * nslab;
-  const int first = s * (VPL * kWave);
-  r.t = t;
-  r.c0 = first + lane;
-  const int left = (row_vec - first + kWave - 1) / kWave;
-  r.nvec = left < VPL ? left : VPL;
-  return r;
-}
 
 __device__ __forceinline__ bool row_ok(int64_t d, int64_t rows) { return (uint64_t)d < (uint64_t)rows; }
 
@@ -107,18 +89,6 @@ __device__ __forceinline__ int store_out(u32x4* __restrict__ dst, const float (&
     }
   }
   return un.nvec;
-}
-
-template <int VPL, bool EVEN, bool NT>
-__device__ __forceinline__ void load_slab(u32x4 (&v)[VPL], const u32x4* __restrict__ src, const Unit& un,
-                                          int row_vec) {
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i < un.nvec) {
-      const int c = un.c0 + i * kWave;
-      if (EVEN || c < row_vec) v[i] = ld16<NT>(src + c);
-    }
-  }
 }
 
 template <int VPL, int K, bool EVEN, bool NT>

@@ -26,29 +26,11 @@
 // end and no per-lane masks are needed.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "row_io.hpp"
 
 namespace ep {
 
 namespace {
-
-struct Unit {
-  int64_t t;
-  int c0;    // this lane's first vector of the slab
-  int nvec;  // vectors of the slab inside the row (uniform, >= 1)
-};
-
-template <int VPL>
-__device__ __forceinline__ Unit unit_of(int u, int nslab, int row_vec, int lane) {
-  Unit r;
-  const int t = u / nslab;
-  const int s = u - t * nslab;
-  const int first = s * (VPL * kWave);
-  r.t = t;
-  r.c0 = first + lane;
-  const int left = (row_vec - first + kWave - 1) / kWave;
-  r.nvec = left < VPL ? left : VPL;
-  return r;
-}
 
 template <int K>
 struct Dests {
@@ -60,30 +42,6 @@ __device__ __forceinline__ void fetch_dests(Dests<K>& ds, const int32_t* __restr
   if constexpr (K > 0) {
 #pragma unroll
     for (int j = 0; j < K; ++j) ds.d[j] = dr[j];
-  }
-}
-
-template <int VPL, bool EVEN, bool NT>
-__device__ __forceinline__ void load_slab(u32x4 (&v)[VPL], const u32x4* __restrict__ src, const Unit& un,
-                                          int row_vec) {
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i < un.nvec) {
-      const int c = un.c0 + i * kWave;
-      if (EVEN || c < row_vec) v[i] = ld16<NT>(src + c);
-    }
-  }
-}
-
-template <int VPL, bool EVEN, bool NT>
-__device__ __forceinline__ void store_one(const u32x4 (&v)[VPL], u32x4* __restrict__ dst, const Unit& un,
-                                          int row_vec) {
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i < un.nvec) {
-      const int c = un.c0 + i * kWave;
-      if (EVEN || c < row_vec) st16<NT>(dst + c, v[i]);
-    }
   }
 }
 

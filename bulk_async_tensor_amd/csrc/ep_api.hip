@@ -161,25 +161,41 @@ size_t ep_layout_workspace_bytes(int T, int k, int E) {
   return ep::layout_workspace_bytes(T, k, E);
 }
 
-int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* dest_row,
-              int32_t* src_token, int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(T, k, E, "ep_layout");
+}  // extern "C"
+
+namespace {
+
+int check_layout_args(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                      int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
+                      size_t workspace_bytes, const char* what) {
+  int rc = check_common(T, k, E, what);
   if (rc) return rc;
-  if (E < 1 || E > EP_MAX_EXPERTS)
-    return fail(EP_ERR_INVALID_ARG, "ep_layout: E = %d outside [1, %d]", E, EP_MAX_EXPERTS);
-  if (k > E) return fail(EP_ERR_INVALID_ARG, "ep_layout: k = %d > E = %d", k, E);
-  if (!counts || !offsets) return fail(EP_ERR_INVALID_ARG, "ep_layout: null counts/offsets");
-  if (T > 0 && (!topk_idx || !dest_row)) return fail(EP_ERR_INVALID_ARG, "ep_layout: null topk_idx/dest_row");
+  if (E < 1 || E > EP_MAX_EXPERTS) return fail(EP_ERR_INVALID_ARG, "%s: E = %d outside [1, %d]", what, E, EP_MAX_EXPERTS);
+  if (k > E) return fail(EP_ERR_INVALID_ARG, "%s: k = %d > E = %d", what, k, E);
+  if (!counts || !offsets) return fail(EP_ERR_INVALID_ARG, "%s: null counts/offsets", what);
+  if (T > 0 && (!topk_idx || !dest_row)) return fail(EP_ERR_INVALID_ARG, "%s: null topk_idx/dest_row", what);
   const void* ptrs[] = {topk_idx, counts, offsets, dest_row, src_token, status};
   for (const void* p : ptrs)
-    if (p && !aligned(p, 4)) return fail(EP_ERR_ALIGNMENT, "ep_layout: int32 tensor not 4-byte aligned");
+    if (p && !aligned(p, 4)) return fail(EP_ERR_ALIGNMENT, "%s: int32 tensor not 4-byte aligned", what);
   const size_t need = ep::layout_workspace_bytes(T, k, E);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
-      return fail(EP_ERR_WORKSPACE, "ep_layout: workspace of %zu bytes needed, %zu given", need,
+      return fail(EP_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                   workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(EP_ERR_ALIGNMENT, "ep_layout: workspace not 16-byte aligned");
+    if (!aligned(workspace, 16)) return fail(EP_ERR_ALIGNMENT, "%s: workspace not 16-byte aligned", what);
   }
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+              int32_t* src_token, int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layout_args(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
+                             workspace_bytes, "ep_layout");
+  if (rc) return rc;
   ep::Budget b;
   rc = current_device(&b);
   if (rc) return rc;
@@ -207,6 +223,36 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
   hipError_t e = ep::launch_dispatch(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, dest_row, k, recv,
                                      recv_rows, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ep_dispatch launch");
+  return EP_OK;
+}
+
+int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void* x, int H, int32_t* counts,
+                       int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* recv, int64_t recv_rows, void* stream) {
+  int rc = check_layout_args(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
+                             workspace_bytes, "ep_layout_dispatch");
+  if (rc) return rc;
+  rc = check_rows(H, recv_rows, "ep_layout_dispatch");
+  if (rc) return rc;
+  if (T > 0 && (!x || (!recv && recv_rows > 0)))
+    return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch: null x/recv");
+  if ((x && !aligned(x, 16)) || (recv && !aligned(recv, 16)))
+    return fail(EP_ERR_ALIGNMENT, "ep_layout_dispatch: bf16 tensor not 16-byte aligned");
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (T > 0 && ep::layout_dispatch_fits(T, k, E)) {
+    e = ep::launch_layout_dispatch(b, topk_idx, T, k, E, x, H, counts, offsets, dest_row, src_token, status, recv,
+                                   recv_rows, s);
+  } else {
+    e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace, s);
+    if (e == hipSuccess && T > 0 && recv_rows > 0)
+      e = ep::launch_dispatch(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, dest_row, k, recv, recv_rows,
+                              s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ep_layout_dispatch launch");
   return EP_OK;
 }
 

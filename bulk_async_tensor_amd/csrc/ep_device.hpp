@@ -31,6 +31,57 @@ __device__ __forceinline__ int mask_rank(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Mask of the lanes that hold the same value v as the calling lane, among
+// the lanes with ok set (v < 2^nbits): the intersection of one ballot per bit.
+__device__ __forceinline__ uint64_t same_value_lanes(bool ok, int v, int nbits) {
+  uint64_t m = ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (v >> b) & 1;
+    const uint64_t bal = ballot(ok && bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads and stores
+// issued before it stay in flight (__syncthreads would wait for them).
+// Valid wherever threads exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of one value per thread over a block of NWAVES waves;
+// *total receives the sum.  s_wave holds NWAVES + 1 ints of LDS.  Every
+// thread of the block must call it (it contains two LDS-only barriers).
+template <int NWAVES>
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  lds_barrier();
+  if (wave == 0) {
+    const int wt = lane < NWAVES ? s_wave[lane] : 0;
+    const int ws = wave_incl_scan(wt, lane);
+    if (lane < NWAVES) s_wave[lane] = ws - wt;
+    if (lane == NWAVES - 1) s_wave[NWAVES] = ws;
+  }
+  lds_barrier();
+  *total = s_wave[NWAVES];
+  return incl - v + s_wave[wave];
+}
+
 // ---------------------------------------------------------------- global I/O
 // NT = true marks the access as streaming (the "nt" cache-policy bit): the
 // line is not kept for reuse.

@@ -36,6 +36,12 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
 hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* src_token,
                                 void* recv, int64_t recv_rows, hipStream_t stream);
 
+// ---- fused layout + dispatch for small batches (decode.hip)
+bool layout_dispatch_fits(int T, int k, int E);
+hipError_t launch_layout_dispatch(const Budget& b, const int32_t* idx, int T, int k, int E, const void* x, int H,
+                                  int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* src_token,
+                                  int32_t* status, void* recv, int64_t recv_rows, hipStream_t stream);
+
 // ---- combine (combine.hip)
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream);

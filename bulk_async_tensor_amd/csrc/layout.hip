@@ -186,13 +186,7 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
     const bool in_chunk = i < n;
     const int e = ent[s];
     const bool ok = in_chunk && (unsigned)e < (unsigned)E;
-    // lanes holding the same expert: intersect the ballots of every id bit
-    uint64_t m = ballot(ok);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = ballot(ok && bit);
-      m &= bit ? bal : ~bal;
-    }
+    const uint64_t m = same_value_lanes(ok, e, nbits);
     const int rank = mask_rank(m);
     int r = -1;
     if (ok) r = run[e] + rank;
@@ -212,34 +206,6 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
 constexpr int kFusedChunk = 1024;   // entries per workgroup: 16 waves x 64
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// Exclusive scan of one value per thread over a 1024-thread block; *total
-// receives the sum.  s_wave holds kFusedWaves + 1 ints of LDS.
-__device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wave, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) s_wave[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    const int wt = lane < kFusedWaves ? s_wave[lane] : 0;
-    const int ws = wave_incl_scan(wt, lane);
-    if (lane < kFusedWaves) s_wave[lane] = ws - wt;
-    if (lane == kFusedWaves - 1) s_wave[kFusedWaves] = ws;
-  }
-  __syncthreads();
-  *total = s_wave[kFusedWaves];
-  return incl - v + s_wave[wave];
-}
 
 // Reads the k ids of token t, checks them and adds them to the (chunk,
 // expert) histogram.  KT > 0: k known at compile time, so the loads of a
@@ -328,7 +294,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
     }
   }
   int all = 0;
-  const int excl = block_excl_scan(tot, s_wave, &all);
+  const int excl = block_excl_scan<kFusedWaves>(tot, s_wave, &all);
   if (tid < E) base[tid] = excl + pre;
   if (c == 0) {
     if (tid < E) {
@@ -344,12 +310,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
   // ranks inside this wave's 64-entry step
   const bool in_range = my_i < N;
   const bool ok = in_range && (unsigned)my_e < (unsigned)E;
-  uint64_t m = ballot(ok);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (my_e >> b) & 1;
-    const uint64_t bal = ballot(ok && bit);
-    m &= bit ? bal : ~bal;
-  }
+  const uint64_t m = same_value_lanes(ok, my_e, nbits);
   const int rank = mask_rank(m);
   if (ok && (m >> lane) == 1ull) stepc[wave * E + my_e] = __builtin_popcountll(m);
   __syncthreads();

@@ -155,6 +155,19 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
                 int64_t recv_rows, void* stream);
 
 /*
+ * ep_layout_dispatch -- ep_layout followed by ep_dispatch, with identical
+ * outputs, in one launch when the batch is small (T*k <= 1024 entries): the
+ * low-latency decode shape, where launches rather than bytes set the time
+ * (the low-latency kernel family of [DeepEP-TMA], "TMA Implementation
+ * Across Kernel Types").  Larger batches run the two calls in order.
+ * Arguments as for ep_layout and ep_dispatch (x bf16 [T, H], recv bf16
+ * [recv_rows, H]); the workspace is needed only when ep_layout needs one.
+ */
+int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void* x, int H, int32_t* counts,
+                       int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* recv, int64_t recv_rows, void* stream);
+
+/*
  * ep_dispatch_rows -- the same copy in gather form:
  *   recv[r, :] = x[src_token[r], :] for r < recv_rows
  * with src_token from ep_layout (then recv_rows = offsets[E]); rows whose

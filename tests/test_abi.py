@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -161,6 +161,20 @@ def combine(lib, y=A16, rows=32, H=1024, dest=A4, w=A4, T=16, k=2, out=A16):
 )
 def test_combine_rejects(lib, kw, code):
     assert combine(lib, **kw) == code
+
+
+def test_layout_dispatch_rejects(lib):
+    def f(idx=A4, T=16, k=2, E=8, x=A16, H=1024, recv=A16, rows=32, ws=A16, wsb=1 << 20):
+        return lib.ep_layout_dispatch(idx, T, k, E, x, H, A4, A4, A4, A4, A4, ws, wsb, recv, rows, None)
+
+    assert f(T=-1) == ep.EP_ERR_INVALID_ARG
+    assert f(k=9) == ep.EP_ERR_INVALID_ARG
+    assert f(H=12) == ep.EP_ERR_INVALID_ARG
+    assert f(x=None) == ep.EP_ERR_INVALID_ARG
+    assert f(recv=None) == ep.EP_ERR_INVALID_ARG
+    assert f(x=A16 + 8) == ep.EP_ERR_ALIGNMENT
+    assert f(idx=ODD) == ep.EP_ERR_ALIGNMENT
+    assert f(T=131072, k=8, E=256, ws=None) == ep.EP_ERR_WORKSPACE
 
 
 def test_dispatch_rows_rejects(lib):

@@ -440,3 +440,39 @@ def test_graph_replay_matches_eager(name):
         np.testing.assert_array_equal(lay["offsets"].cpu().numpy(), ref_lay["offsets"])
         np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
         assert np.array_equal(oracle.bf16_to_f32(from_dev_bf16(out)), oracle.bf16_to_f32(wl.x))
+
+
+@pytest.mark.parametrize(
+    "name,over",
+    [("decode", {}), ("tiny", {}), ("prefill", dict(T=170, E=64, k=6)), ("prefill", dict(T=33, H=7176, E=16, k=3)),
+     ("prefill", dict(T=1, H=8, E=1, k=1)), ("prefill", dict(T=32, E=1024, k=32)),
+     ("train", dict(T=300)), ("prefill", dict(T=2000, E=64, k=6))],
+)
+@pytest.mark.parametrize("budget", [0, 24])
+def test_layout_dispatch_matches_two_calls(name, over, budget):
+    ep.ep_set_num_cus(budget)
+    wl = make_workload(name, seed=7, **over)
+    c = wl.config
+    ref = oracle.layout(wl.topk_idx, c.E)
+    R = c.T * c.k
+    recv = torch.full((R, c.H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay = ep.ep_layout_dispatch(to_dev(wl.topk_idx), c.E, to_dev_bf16(wl.x), recv)
+    torch.cuda.synchronize()
+    check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+    np.testing.assert_array_equal(from_dev_bf16(recv), oracle.dispatch(wl.x, ref["dest_row"], R))
+
+
+def test_layout_dispatch_flags_bad_ids():
+    rng = np.random.default_rng(11)
+    idx = np.array([rng.permutation(16)[:4] for _ in range(100)], dtype=np.int32)
+    idx[3, 1] = 99
+    idx[50, 2] = idx[50, 0]
+    x = rng.integers(0, 2**16, size=(100, 64), dtype=np.uint32).astype(np.uint16)
+    ref = oracle.layout(idx, 16)
+    assert ref["status"] == 3
+    recv = torch.full((400, 64), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay = ep.ep_layout_dispatch(to_dev(idx), 16, to_dev_bf16(x), recv)
+    torch.cuda.synchronize()
+    check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, 100, 4)
+    want = oracle.dispatch(x, ref["dest_row"], 400, recv=np.full((400, 64), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(from_dev_bf16(recv), want)
