@@ -100,7 +100,9 @@ __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
 // One wave instruction: every lane fetches 16 bytes from its own global
 // address and the data lands in LDS at lds_base + 16 * lane, without passing
 // through VGPRs (global_load_lds_dwordx4).  lds_base must be wave-uniform.
-// Completion is tracked by the wave's vmcnt counter only.
+// Completion is tracked by the wave's vmcnt counter only.  The load keeps
+// the default cache policy: marked streaming (nt) it cut dispatch from 6.1
+// to 2.95 TB/s.
 __device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 }
