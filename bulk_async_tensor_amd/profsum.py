@@ -109,6 +109,39 @@ def hbm(args):
     print("\n".join(lines))
 
 
+def sq(args):
+    """LDS bank conflicts and VALU busy per kernel from one SQ counter pass.
+    The CSV reports GRBM_GUI_ACTIVE summed over the XCDs; the busy-cycle
+    denominator is that sum / xcds (the per-XCD value), as the derived
+    metrics use the maximum over instances."""
+    per = {}
+    for r in csv.DictReader(open(args.counters)):
+        k = kind_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        nm = r["Kernel_Name"].replace("ep::(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        per.setdefault((nm, r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    by_kernel = {}
+    for (nm, _), c in per.items():
+        by_kernel.setdefault(nm, []).append(c)
+    out = [f"# SQ counters per launch: {args.title}", f"# command: {args.command}",
+           f"# LDSBankConflict% = 100*SQ_LDS_BANK_CONFLICT/GUI/CUs; conflict ratio = conflicts/(SQ_LDS_IDX_ACTIVE-"
+           f"conflicts); VALUBusy% = 100*SQ_ACTIVE_INST_VALU/CUs/GUI; GUI = GRBM_GUI_ACTIVE/{args.xcds}; "
+           f"CUs = {args.cus}", "",
+           f"{'kernel':<46s} {'launches':>8s} {'LDS_conf%':>9s} {'conf_ratio':>10s} {'VALUBusy%':>9s} "
+           f"{'VALU_insts':>11s} {'LDS_insts':>10s} {'waves':>7s}"]
+    for nm, cs in by_kernel.items():
+        med = {key: statistics.median(c.get(key, 0.0) for c in cs) for key in cs[0]}
+        gui = med["GRBM_GUI_ACTIVE"] / args.xcds
+        conf = med["SQ_LDS_BANK_CONFLICT"]
+        idx = med["SQ_LDS_IDX_ACTIVE"]
+        ratio = conf / (idx - conf) if idx > conf else 0.0
+        out.append(f"{nm[:46]:<46s} {len(cs):8d} {100 * conf / gui / args.cus:9.3f} {ratio:10.3f} "
+                   f"{100 * med['SQ_ACTIVE_INST_VALU'] / args.cus / gui:9.2f} {med['SQ_INSTS_VALU']:11.0f} "
+                   f"{med['SQ_INSTS_LDS']:10.0f} {med['SQ_WAVES']:7.0f}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="mode", required=True)
@@ -127,8 +160,14 @@ def main(argv=None):
     h.add_argument("--algorithmic", type=int, default=0)
     h.add_argument("--command-fetch", default="")
     h.add_argument("--command-write", default="")
+    q = sub.add_parser("sq")
+    q.add_argument("counters")
+    q.add_argument("--title", default="")
+    q.add_argument("--command", default="")
+    q.add_argument("--xcds", type=int, default=8)
+    q.add_argument("--cus", type=int, default=256)
     args = p.parse_args(argv)
-    trace(args) if args.mode == "trace" else hbm(args)
+    {"trace": trace, "hbm": hbm, "sq": sq}[args.mode](args)
 
 
 if __name__ == "__main__":
