@@ -178,7 +178,7 @@ def read_traffic(kernel, workload):
                 fields[m.group(1)] = m.group(2)
     from bulk_async_tensor_amd.build import kernel_source_hash
 
-    if fields.get("kernel_sources") != kernel_source_hash():
+    if fields.get("kernel_sources") != kernel_source_hash(kernel):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -265,7 +265,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
             s.stream = stream
             st = stream if stream is not None else torch.cuda.current_stream()
             for mode, label in ([(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32"), (4, "mix8to1"),
-                                 (5, "mix1to8")] if probes else []):
+                                 (6, "mix8to1_burst"), (5, "mix1to8")] if probes else []):
                 for _ in range(3):
                     ep.ep_bw_probe(mode, a, bb, n, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -275,7 +275,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 e1.record(st)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
-                moved = 2 * n if mode == 0 else (n + n // 8) if mode in (4, 5) else n
+                moved = 2 * n if mode == 0 else (n + n // 8) if mode in (4, 5, 6) else n
                 rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)

@@ -21,13 +21,22 @@ SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "decode.hi
 ARCH = "gfx950"
 
 
-def kernel_source_hash():
-    """Short hash of every file under csrc/ (identifies the kernels a
-    counter summary was taken on)."""
+# The sources each measured kernel is compiled and launched from.
+KERNEL_SOURCES = {
+    "layout": ["layout.hip", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
+    "dispatch": ["dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
+    "combine": ["combine.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
+}
+
+
+def kernel_source_hash(kernel=None):
+    """Short hash of the sources of one kernel (all of csrc/ when kernel is
+    None): identifies the code a counter summary was taken on."""
     import hashlib
 
+    files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(CSRC))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -314,10 +314,10 @@ const char* ep_status_string(int code) {
 const char* ep_last_error(void) { return g_err; }
 
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
-  if (mode < 0 || (mode & ~0x737) != 0 || (mode & 7) > 5 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
+  if (mode < 0 || (mode & ~0x737) != 0 || (mode & 7) > 6 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
     return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode 0x%x", mode);
-  if ((mode & 7) >= 4 && bytes % 8192 != 0)
-    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mixed operations need bytes %% 8192 == 0");
+  if ((mode & 7) >= 4 && bytes % ((mode & 7) == 6 ? 65536 : 8192) != 0)
+    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mixed operations need bytes in multiples of 8 KiB (64 KiB for 6)");
   if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: bytes must be a multiple of 16");
   if (((mode & 7) != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
   if (((mode & 7) == 1 || (mode & 7) == 3) && bytes > ((int64_t)1 << 40))

@@ -113,6 +113,30 @@ __global__ __launch_bounds__(1024) void bw_mix_kernel(const u32x4* __restrict__ 
   }
 }
 
+// The 8:1 mix with burstier writes: a wave reads 64 KiB contiguous (8 rounds
+// of 8 KiB, folded into 8 accumulators) and then writes 8 KiB contiguous.
+// nvec counts the read side (multiple of 4096 vectors).
+__global__ __launch_bounds__(1024) void bw_mix_burst_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int64_t nvec) {
+  const int lane = lane_id();
+  const int64_t wpg = blockDim.x >> 6;
+  const int64_t nchunk = nvec / (64 * kWave);
+  for (int64_t q = (int64_t)blockIdx.x * wpg + wave_in_group(); q < nchunk; q += (int64_t)gridDim.x * wpg) {
+    u32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 8; ++r) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ld16<true>(src + q * 64 * kWave + (r * 8 + i) * kWave + lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] ^= v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st16<true>(dst + q * 8 * kWave + i * kWave + lane, acc[i]);
+  }
+}
+
 using BwFn = void (*)(const u32x4*, u32x4*, int64_t);
 
 template <int OP, int D>
@@ -164,13 +188,14 @@ hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst
   const int depth = depth_code == 1 ? 16 : depth_code == 2 ? 32 : 8;
   if (depth_code == 3 || pol > 5) return hipErrorInvalidValue;
   const int64_t nvec = bytes / 16;
-  if (op > 5) return hipErrorInvalidValue;
+  if (op > 6) return hipErrorInvalidValue;
   BwFn fn = op == 0 ? bw_pick_depth<0>(depth_code, 0)
           : op == 1 ? bw_pick_depth<1>(depth_code, pol)
           : op == 2 ? bw_pick_depth<2>(depth_code, 0)
           : op == 3 ? bw_pick_depth<3>(depth_code, pol)
           : op == 4 ? (BwFn)bw_mix_kernel<0>
-                    : (BwFn)bw_mix_kernel<1>;
+          : op == 5 ? (BwFn)bw_mix_kernel<1>
+                    : (BwFn)bw_mix_burst_kernel;
   const size_t per_wave = op == 3 ? (size_t)depth * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds = 0;

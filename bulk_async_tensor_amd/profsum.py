@@ -87,7 +87,7 @@ def hbm(args):
         f"# summarised by: python -m bulk_async_tensor_amd.profsum hbm ...",
         f"kernel: ep_{k}",
         f"workload: {args.workload}",
-        f"kernel_sources: {kernel_source_hash()}",
+        f"kernel_sources: {kernel_source_hash(k)}",
         f"launches_fetch: {nf.get(k, 0)}",
         f"launches_write: {nw.get(k, 0)}",
         f"fetch_kib_per_launch: {fetch[k]:.1f}",

@@ -221,8 +221,11 @@ const char* ep_last_error(void);
  *               4 mixed 8:1 -- read `bytes` of src, write bytes/8 of dst
  *               (each wave: 8 KiB in, 1 KiB out);
  *               5 mixed 1:8 -- read bytes/8 of src, write `bytes` of dst
- *               (each wave: 1 KiB in, 8 KiB out); 4 and 5 need
- *               bytes % 8192 == 0 and ignore depth and policy
+ *               (each wave: 1 KiB in, 8 KiB out);
+ *               6 mixed 8:1 in bursts -- as 4, but each wave reads 64 KiB
+ *               and then writes 8 KiB;
+ *               4 and 5 need bytes % 8192 == 0, 6 bytes % 65536 == 0; they
+ *               ignore depth and policy
  *   bits [5:4]  depth: 16-byte vectors in flight per lane, 0 -> 8, 1 -> 16,
  *               2 -> 32 (3 is invalid)
  *   bits [10:8] cache policy of the loads of operations 1 and 3: 0 nt,

@@ -336,6 +336,12 @@ def test_bw_probe_mixed_ratios():
     b = big.view(-1, 8, 64, 4).cpu().numpy()
     want = np.bitwise_xor.reduce(b, axis=1).reshape(-1)
     assert np.array_equal(small.cpu().numpy(), want)
+    burst = torch.zeros(n // 32, dtype=torch.int32, device=DEV)
+    ep.ep_bw_probe(6, big, burst, n)  # 8:1 in bursts -- vector i of each 8 KiB out folds 8 rounds
+    torch.cuda.synchronize()
+    b64 = big.view(-1, 8, 8, 64, 4).cpu().numpy()  # [chunk, round, i, lane, word]
+    want = np.bitwise_xor.reduce(b64, axis=1).reshape(-1)
+    assert np.array_equal(burst.cpu().numpy(), want)
     out = torch.zeros_like(big)
     ep.ep_bw_probe(5, small, out, n)  # 1:8 -- each 1 KiB chunk written 8 times (x ^ i in the first word)
     torch.cuda.synchronize()
