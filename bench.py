@@ -251,6 +251,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
 
     s = Setup(name)
     n = 1 << 30
+    ndev = torch.cuda.get_device_properties(0).multi_processor_count
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
     bb = torch.empty_like(a)
     with open(path, "a") as fh:
@@ -264,19 +265,23 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 ep.ep_set_num_cus(budget)
             s.stream = stream
             st = stream if stream is not None else torch.cuda.current_stream()
-            for mode, label in ([(0, "copy"), (1, "read"), (2, "write"), (0x20 | 2, "write32"), (4, "mix8to1"),
-                                 (6, "mix8to1_burst"), (5, "mix1to8")] if probes else []):
+            # operation 7 once per wave: 128 KiB read by each of 16 waves on every CU of the grid
+            once = min(n, (budget if budget > 0 else ndev) * 16 * (128 << 10))
+            for mode, label, nb in ([(0, "copy", n), (1, "read", n), (2, "write", n), (0x20 | 2, "write32", n),
+                                     (4, "mix8to1", n), (6, "mix8to1_burst", n), (7, "mix8to1_phase", n),
+                                     (7, "mix8to1_phase_once", once), (5, "mix1to8", n)] if probes else []):
                 for _ in range(3):
-                    ep.ep_bw_probe(mode, a, bb, n, stream=st)
+                    ep.ep_bw_probe(mode, a, bb, nb, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(st)
                 for _ in range(10):
-                    ep.ep_bw_probe(mode, a, bb, n, stream=st)
+                    ep.ep_bw_probe(mode, a, bb, nb, stream=st)
                 e1.record(st)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
-                moved = 2 * n if mode == 0 else (n + n // 8) if mode in (4, 5, 6) else n
-                rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6}
+                moved = 2 * nb if mode == 0 else (nb + nb // 8) if mode in (4, 5, 6, 7) else nb
+                rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6,
+                       "bytes": nb}
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
             for v in variants:
@@ -309,6 +314,7 @@ def probe_sweep(path, budgets):
     import bulk_async_tensor_amd as ep
 
     n = 1 << 30
+    ndev = torch.cuda.get_device_properties(0).multi_processor_count
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
     b = torch.empty_like(a)
     cases = [(0, d, 0) for d in range(3)] + [(2, d, 0) for d in range(3)]

@@ -17,6 +17,12 @@
 //          stage;
 //   lds2   two stages: the next unit's direct-to-LDS loads are in flight while
 //          the current stage is read, summed and stored.
+//   phase  each wave holds up to 16 finished output vectors per lane (a
+//          whole row at H = 7168) in registers and stores them only after
+//          it has read all of their source rows.  With at most one such unit
+//          per wave, the grid reads first and writes last: HBM sees almost
+//          no read/write turnaround, which a steady 8:1 mix pays on every
+//          channel.
 // The k destination rows and weights of a unit are fetched with scalar loads
 // before its first row load.  EVEN = the row is a whole number of KiB, so no
 // per-lane row-end masks are needed.
@@ -307,6 +313,165 @@ __global__ __launch_bounds__(1024) void combine_lds2_kernel(EP_COMBINE_ARGS) {
   }
 }
 
+// Phase kernel geometry: vectors (16 bytes per lane) of finished output a
+// wave holds before storing.  A unit is tpu whole tokens when a row has at
+// most kHeld vectors per lane (nseg == 1), else one of nseg segments of seg
+// vectors of one token.
+constexpr int kHeld = 16;
+
+template <int K, bool EVEN>
+__global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __restrict__ y, u32x4* __restrict__ out,
+                                                             const int32_t* __restrict__ dest_row,
+                                                             const float* __restrict__ w, int64_t recv_rows,
+                                                             int row_vec, int nv, int T, int tpu, int nseg, int seg,
+                                                             int units) {
+  const int lane = lane_id();
+  const int stride = gridDim.x * (blockDim.x >> 6);
+  for (int u = blockIdx.x * (blockDim.x >> 6) + wave_in_group(); u < units; u += stride) {
+    int t0, c0, n_in;
+    if (nseg == 1) {
+      t0 = u * tpu;
+      c0 = 0;
+      n_in = (T - t0 < tpu ? T - t0 : tpu) * nv;
+    } else {
+      t0 = u / nseg;
+      c0 = (u - t0 * nseg) * seg;
+      n_in = nv - c0 < seg ? nv - c0 : seg;
+    }
+    // Each token's vectors are visited from a rotated start, so that waves
+    // that run in step do not all read the same offset of their rows at once
+    // (with power-of-two rows that would load a few HBM channels at a time).
+    const int span = nseg == 1 ? nv : n_in;
+    const int rot = u % span;
+    u32x4 held[kHeld];
+    int t = t0, p = 0, c = c0 + rot;
+    Slots<K> s;
+    fetch_slots<K>(s, dest_row + (int64_t)t * K, w + (int64_t)t * K);
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      if (i < n_in) {
+        if (i > 0 && p == 0) fetch_slots<K>(s, dest_row + (int64_t)t * K, w + (int64_t)t * K);
+        const int col = c * kWave + lane;
+        u32x4 v[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+          if (row_ok(s.d[j], recv_rows) && (EVEN || col < row_vec)) v[j] = ld16<true>(y + (int64_t)s.d[j] * row_vec + col);
+        float acc[1][8];
+        zero<1>(acc);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          if (row_ok(s.d[j], recv_rows)) {
+            const u32x4 one[1] = {v[j]};
+            accumulate<1>(acc, one, s.w[j], 1);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) held[i][q] = pack_bf16x2(acc[0][2 * q], acc[0][2 * q + 1]);
+        if (++c == c0 + span) c = c0;
+        if (++p == span) {
+          p = 0;
+          ++t;
+        }
+      }
+    }
+    t = t0;
+    p = 0;
+    c = c0 + rot;
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      if (i < n_in) {
+        const int col = c * kWave + lane;
+        if (EVEN || col < row_vec) st16<true>(out + (int64_t)t * row_vec + col, held[i]);
+        if (++c == c0 + span) c = c0;
+        if (++p == span) {
+          p = 0;
+          ++t;
+        }
+      }
+    }
+  }
+}
+
+using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int, int, int,
+                         int);
+
+template <bool EVEN>
+PhaseFn pick_phase(int k) {
+  switch (k) {
+    case 2: return combine_phase_kernel<2, EVEN>;
+    case 4: return combine_phase_kernel<4, EVEN>;
+    case 6: return combine_phase_kernel<6, EVEN>;
+    case 8: return combine_phase_kernel<8, EVEN>;
+    default: return nullptr;
+  }
+}
+
+struct PhaseShape {
+  int nv, tpu, nseg, seg;
+};
+
+PhaseShape phase_shape(int row_vec) {
+  PhaseShape p;
+  p.nv = (row_vec + kWave - 1) / kWave;
+  p.tpu = 1;
+  p.nseg = 1;
+  p.seg = p.nv;
+  if (p.nv <= kHeld) {
+    p.tpu = kHeld / p.nv;
+  } else {
+    p.nseg = (p.nv + kHeld - 1) / kHeld;
+    p.seg = (p.nv + p.nseg - 1) / p.nseg;
+  }
+  return p;
+}
+
+int64_t phase_units(const PhaseShape& p, int64_t T) { return p.nseg == 1 ? (T + p.tpu - 1) / p.tpu : T * p.nseg; }
+
+// 16 waves per workgroup; at this register use a CU holds one such workgroup.
+constexpr int kPhaseWpg = 16;
+
+hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int row_vec, const int32_t* dest_row,
+                        const float* w, int T, int k, void* out, hipStream_t stream) {
+  const bool even = row_vec % kWave == 0;
+  const PhaseShape ps = phase_shape(row_vec);
+  PhaseFn fn = even ? pick_phase<true>(k) : pick_phase<false>(k);
+  if (!fn) return hipErrorInvalidValue;
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  const size_t lds_bytes = b.num_cus > 0 ? kExclusiveLds : 0;
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  // One launch per batch of tokens that gives every wave of the grid one
+  // unit: the launch boundary keeps the read and write phases of the
+  // batches apart, which waves that loop over several units would not.
+  const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
+  const int64_t batch = ps.nseg == 1 ? wave_slots * ps.tpu : wave_slots / ps.nseg > 0 ? wave_slots / ps.nseg : 1;
+  for (int64_t t0 = 0; t0 < T; t0 += batch) {
+    const int tb = (int)(T - t0 < batch ? T - t0 : batch);
+    const int units = (int)phase_units(ps, tb);
+    int grid = (units + kPhaseWpg - 1) / kPhaseWpg;
+    if (grid > cus) grid = cus;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kPhaseWpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(y),
+                       static_cast<u32x4*>(out) + t0 * row_vec, dest_row + t0 * k, w + t0 * k, recv_rows, row_vec,
+                       ps.nv, tb, ps.tpu, ps.nseg, ps.seg, units);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The phase kernel is the default on the whole device when a launch gives
+// most waves of the grid a unit (it reads all rows of its unit before its
+// first store, so a wave with little work gains nothing and a small batch
+// would sit on few CUs).
+bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
+  if (b.num_cus > 0 || !(k == 2 || k == 4 || k == 6 || k == 8)) return false;
+  const int64_t units = phase_units(phase_shape(row_vec), T);
+  return units * 4 >= (int64_t)b.device_cus * kPhaseWpg * 3;
+}
+
 using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);
 
 template <int VPL, int K, bool EVEN>
@@ -351,10 +516,11 @@ CombineFn pick_vpl(Variant v, int vpl, int k) {
 
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream) {
-  if (v == Variant::Auto) v = Variant::Vgpr;
+  const int row_vec = H / 8;
+  if (v == Variant::Auto) v = phase_preferred(b, row_vec, T, k) ? Variant::Phase : Variant::Vgpr;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if (!known_k) v = Variant::Vgpr;  // the any-k kernel
-  const int row_vec = H / 8;
+  if (v == Variant::Phase) return launch_phase(b, y, recv_rows, row_vec, dest_row, w, T, k, out, stream);
   const bool even = row_vec % kWave == 0;
   // in-flight registers grow as k x VPL: two vectors per lane per slot for
   // the single-set kernel, one for the double-buffered and LDS ones

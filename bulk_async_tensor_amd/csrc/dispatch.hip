@@ -329,7 +329,8 @@ RowsFn rows_pick(int vpl) {
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {
   // direct-to-LDS staging measured fastest at every compute-unit budget
-  if (v == Variant::Auto) v = Variant::Lds1;
+  // ("phase" is a combine kernel; dispatch takes its default for it)
+  if (v == Variant::Auto || v == Variant::Phase) v = Variant::Lds1;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if (v == Variant::Lds2 && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;

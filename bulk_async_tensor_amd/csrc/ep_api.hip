@@ -122,7 +122,8 @@ int ep_set_variant(const char* name) {
     const char* name;
     ep::Variant v;
   } table[] = {{"auto", ep::Variant::Auto}, {"vgpr", ep::Variant::Vgpr}, {"vgpr2", ep::Variant::Vgpr2},
-               {"lds1", ep::Variant::Lds1}, {"lds2", ep::Variant::Lds2}, {"vgpr_cached", ep::Variant::VgprCached}};
+               {"lds1", ep::Variant::Lds1}, {"lds2", ep::Variant::Lds2}, {"vgpr_cached", ep::Variant::VgprCached},
+               {"phase", ep::Variant::Phase}};
   for (const auto& e : table) {
     if (strcmp(e.name, name) == 0) {
       g_variant.store(static_cast<int>(e.v));
@@ -139,6 +140,7 @@ const char* ep_get_variant(void) {
     case ep::Variant::Lds1: return "lds1";
     case ep::Variant::Lds2: return "lds2";
     case ep::Variant::VgprCached: return "vgpr_cached";
+    case ep::Variant::Phase: return "phase";
     default: return "auto";
   }
 }
@@ -314,10 +316,12 @@ const char* ep_status_string(int code) {
 const char* ep_last_error(void) { return g_err; }
 
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
-  if (mode < 0 || (mode & ~0x737) != 0 || (mode & 7) > 6 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
+  if (mode < 0 || (mode & ~0x737) != 0 || ((mode >> 4) & 3) == 3 || ((mode >> 8) & 7) > 5)
     return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mode 0x%x", mode);
-  if ((mode & 7) >= 4 && bytes % ((mode & 7) == 6 ? 65536 : 8192) != 0)
-    return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: mixed operations need bytes in multiples of 8 KiB (64 KiB for 6)");
+  const int op = mode & 7;
+  if (op >= 4 && bytes % (op == 7 ? 131072 : op == 6 ? 65536 : 8192) != 0)
+    return fail(EP_ERR_INVALID_ARG,
+                "ep_bw_probe: mixed operations need bytes in multiples of 8 KiB (64 KiB for 6, 128 KiB for 7)");
   if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: bytes must be a multiple of 16");
   if (((mode & 7) != 2 && !src) || !dst) return fail(EP_ERR_INVALID_ARG, "ep_bw_probe: null pointer");
   if (((mode & 7) == 1 || (mode & 7) == 3) && bytes > ((int64_t)1 << 40))

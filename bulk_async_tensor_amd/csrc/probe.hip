@@ -116,6 +116,38 @@ __global__ __launch_bounds__(1024) void bw_mix_kernel(const u32x4* __restrict__ 
 // The 8:1 mix with burstier writes: a wave reads 64 KiB contiguous (8 rounds
 // of 8 KiB, folded into 8 accumulators) and then writes 8 KiB contiguous.
 // nvec counts the read side (multiple of 4096 vectors).
+// Operation 7: the 8:1 mix in two phases per wave.  A wave reads 128 KiB
+// (eight 16 KiB blocks folded into 16 vectors per lane) before it writes its
+// 16 KiB.  Launched with one chunk per wave, every wave of the grid reads
+// first and writes at the end, so reads and writes meet only while the grid
+// starts and drains.
+__global__ __launch_bounds__(1024) void bw_phase_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t nvec) {
+  constexpr int kHeld = 16;
+  const int lane = lane_id();
+  const int64_t wpg = blockDim.x >> 6;
+  const int64_t nchunk = nvec / (8 * kHeld * kWave);
+  for (int64_t q = (int64_t)blockIdx.x * wpg + wave_in_group(); q < nchunk; q += (int64_t)gridDim.x * wpg) {
+    const u32x4* s = src + q * 8 * kHeld * kWave + lane;
+    u32x4 acc[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) acc[i] = ld16<true>(s + i * kWave);
+    // groups of 8 loads (8 KiB per wave in flight); the scheduling barrier
+    // keeps each group's loads ahead of its xors
+#pragma unroll
+    for (int g = 2; g < 16; ++g) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ld16<true>(s + (g * 8 + i) * kWave);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[(g & 1) * 8 + i] ^= v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) st16<true>(dst + q * kHeld * kWave + i * kWave + lane, acc[i]);
+  }
+}
+
 __global__ __launch_bounds__(1024) void bw_mix_burst_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                             int64_t nvec) {
   const int lane = lane_id();
@@ -188,21 +220,23 @@ hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst
   const int depth = depth_code == 1 ? 16 : depth_code == 2 ? 32 : 8;
   if (depth_code == 3 || pol > 5) return hipErrorInvalidValue;
   const int64_t nvec = bytes / 16;
-  if (op > 6) return hipErrorInvalidValue;
+
   BwFn fn = op == 0 ? bw_pick_depth<0>(depth_code, 0)
           : op == 1 ? bw_pick_depth<1>(depth_code, pol)
           : op == 2 ? bw_pick_depth<2>(depth_code, 0)
           : op == 3 ? bw_pick_depth<3>(depth_code, pol)
           : op == 4 ? (BwFn)bw_mix_kernel<0>
           : op == 5 ? (BwFn)bw_mix_kernel<1>
-                    : (BwFn)bw_mix_burst_kernel;
+          : op == 6 ? (BwFn)bw_mix_burst_kernel
+                    : (BwFn)bw_phase_kernel;
   const size_t per_wave = op == 3 ? (size_t)depth * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds = 0;
-  if (b.num_cus > 0) {
+  if (b.num_cus > 0 || op == 7) {
+    // one workgroup of 16 waves per CU (operation 7 always runs this way)
     wpg = 16;
     if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
-    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    grid = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
     lds = per_wave * wpg;
     if (lds < kExclusiveLds) lds = kExclusiveLds;
   } else {

@@ -90,7 +90,12 @@ int ep_get_num_cus(void);
  *   "lds1"  rows staged in a per-wave LDS slice by direct-to-LDS loads,
  *           one stage;
  *   "lds2"  the same with two stages per wave: the next unit's
- *           direct-to-LDS load is in flight while the current one is stored.
+ *           direct-to-LDS load is in flight while the current one is stored;
+ *   "phase" (combine; dispatch takes its default) each wave sums up to 16
+ *           KiB of output rows in registers and stores them only after all
+ *           their source rows are read: with one such unit per wave the
+ *           whole grid reads first and writes last.  k must be 2, 4, 6 or 8,
+ *           else the any-k register kernel runs.
  * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
  */
 int ep_set_variant(const char* name);
@@ -224,8 +229,13 @@ const char* ep_last_error(void);
  *               (each wave: 1 KiB in, 8 KiB out);
  *               6 mixed 8:1 in bursts -- as 4, but each wave reads 64 KiB
  *               and then writes 8 KiB;
- *               4 and 5 need bytes % 8192 == 0, 6 bytes % 65536 == 0; they
- *               ignore depth and policy
+ *               7 mixed 8:1 in phases -- as 4, but each wave reads 128 KiB
+ *               and then writes 16 KiB, on one workgroup of 16 waves per
+ *               CU whatever the budget; with bytes = 128 KiB x waves each
+ *               wave does this once, so the grid reads first and writes
+ *               last;
+ *               4 and 5 need bytes % 8192 == 0, 6 bytes % 65536 == 0,
+ *               7 bytes % 131072 == 0; they ignore depth and policy
  *   bits [5:4]  depth: 16-byte vectors in flight per lane, 0 -> 8, 1 -> 16,
  *               2 -> 32 (3 is invalid)
  *   bits [10:8] cache policy of the loads of operations 1 and 3: 0 nt,

@@ -203,7 +203,7 @@ def test_probe_rejects(lib):
     assert lib.ep_bw_probe(0x30, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # depth code 3
     assert lib.ep_bw_probe(0x601, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # policy 6
     assert lib.ep_bw_probe(0x1000, A16, A16, 1024, None) == ep.EP_ERR_INVALID_ARG  # unknown bit
-    assert lib.ep_bw_probe(7, A16, A16, 8192, None) == ep.EP_ERR_INVALID_ARG  # no operation 7
+    assert lib.ep_bw_probe(7, A16, A16, 65536, None) == ep.EP_ERR_INVALID_ARG  # phases need 128 KiB multiples
     assert lib.ep_bw_probe(6, A16, A16, 8192, None) == ep.EP_ERR_INVALID_ARG  # bursts need 64 KiB multiples
     assert lib.ep_bw_probe(4, A16, A16, 4096, None) == ep.EP_ERR_INVALID_ARG  # mixed needs 8 KiB multiples
     assert lib.ep_bw_probe(0, A16, A16, 1000 + 4, None) == ep.EP_ERR_INVALID_ARG

@@ -239,7 +239,7 @@ def test_combine_full_size(name):
         assert np.array_equal(oracle.bf16_to_f32(got), oracle.bf16_to_f32(wl.x))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached", "phase"])
 @pytest.mark.parametrize("budget", BUDGETS)
 def test_combine_variants_stress(variant, budget):
     ep.ep_set_variant(variant)
@@ -250,7 +250,7 @@ def test_combine_variants_stress(variant, budget):
     assert_combine_close(got, oracle_out(name))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "phase"])
 @pytest.mark.parametrize("budget", [0, 24])
 def test_combine_variants_train(variant, budget):
     ep.ep_set_variant(variant)
@@ -260,7 +260,7 @@ def test_combine_variants_train(variant, budget):
     assert_combine_close(got, oracle_out("train"))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "phase"])
 @pytest.mark.parametrize("H", [8, 520, 4104, 7176])
 @pytest.mark.parametrize("k", [1, 3, 6, 8, 11])
 @pytest.mark.parametrize("budget", [0, 24])
@@ -276,6 +276,25 @@ def test_combine_ragged_rows(variant, H, k, budget):
     ref = oracle.combine(y, dest, wl.topk_w)
     got = run_combine(wl, y, dest)
     assert_combine_close(got, ref)
+
+
+# The phase kernel's unit shapes: several tokens per unit (H = 8, 2048, 4104
+# ragged), one token (7168), a row split into segments (8712 ragged: 18
+# vectors per lane in two segments of 9; 16384: two of 16), a last unit that
+# is only partly filled, and several units per wave (budget 1: 16 waves).
+@pytest.mark.parametrize("H", [8, 2048, 4104, 7168, 8712, 16384])
+@pytest.mark.parametrize("T", [1, 29, 300])
+@pytest.mark.parametrize("budget", [0, 1, 24])
+def test_combine_phase_units(H, T, budget):
+    ep.ep_set_variant("phase")
+    ep.ep_set_num_cus(budget)
+    k = 8 if H % 3 else 6
+    wl = make_workload("combine_stress", seed=H + T, T=T, H=H, E=32, k=k)
+    lay = oracle.layout(wl.topk_idx, 32)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1  # a slot that contributes nothing
+    got = run_combine(wl, wl.y, dest)
+    assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
 
 
 @pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2"])
@@ -342,6 +361,12 @@ def test_bw_probe_mixed_ratios():
     b64 = big.view(-1, 8, 8, 64, 4).cpu().numpy()  # [chunk, round, i, lane, word]
     want = np.bitwise_xor.reduce(b64, axis=1).reshape(-1)
     assert np.array_equal(burst.cpu().numpy(), want)
+    phase = torch.zeros(n // 32, dtype=torch.int32, device=DEV)
+    ep.ep_bw_probe(7, big, phase, n)  # 8:1 in phases -- vector i of each 16 KiB out folds 8 blocks
+    torch.cuda.synchronize()
+    b16 = big.view(-1, 8, 16, 64, 4).cpu().numpy()  # [chunk, block, i, lane, word]
+    want = np.bitwise_xor.reduce(b16, axis=1).reshape(-1)
+    assert np.array_equal(phase.cpu().numpy(), want)
     out = torch.zeros_like(big)
     ep.ep_bw_probe(5, small, out, n)  # 1:8 -- each 1 KiB chunk written 8 times (x ^ i in the first word)
     torch.cuda.synchronize()
