@@ -269,7 +269,10 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
             once = min(n, (budget if budget > 0 else ndev) * 16 * (128 << 10))
             for mode, label, nb in ([(0, "copy", n), (1, "read", n), (2, "write", n), (0x20 | 2, "write32", n),
                                      (4, "mix8to1", n), (6, "mix8to1_burst", n), (7, "mix8to1_phase", n),
-                                     (7, "mix8to1_phase_once", once), (5, "mix1to8", n)] if probes else []):
+                                     (7, "mix8to1_phase_once", once), (5, "mix1to8", n),
+                                     (0x27, "mix8to1_phase_once_barrier", once),
+                                     (0x17, "mix1to8_phase", n), (0x17, "mix1to8_phase_once", once)]
+                                    if probes else []):
                 for _ in range(3):
                     ep.ep_bw_probe(mode, a, bb, nb, stream=st)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -279,7 +282,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 e1.record(st)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
-                moved = 2 * nb if mode == 0 else (nb + nb // 8) if mode in (4, 5, 6, 7) else nb
+                moved = 2 * nb if mode == 0 else (nb + nb // 8) if mode in (4, 5, 6, 7, 0x17, 0x27) else nb
                 rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6,
                        "bytes": nb}
                 fh.write(json.dumps(rec) + "\n")

@@ -319,12 +319,65 @@ __global__ __launch_bounds__(1024) void combine_lds2_kernel(EP_COMBINE_ARGS) {
 // vectors of one token.
 constexpr int kHeld = 16;
 
-template <int K, bool EVEN>
+// Loads slot j's SEG vectors at the given columns (row 0 when the slot's row
+// is out of range: those values are never summed).
+template <int K, int SEG>
+__device__ __forceinline__ void phase_load(u32x4 (&v)[SEG], const Slots<K>& s, int j, const u32x4* __restrict__ y,
+                                           int64_t recv_rows, int row_vec, const int (&col)[SEG]) {
+  const bool ok = row_ok(s.d[j], recv_rows);
+  const u32x4* src = y + (ok ? (int64_t)s.d[j] : 0) * row_vec;
+#pragma unroll
+  for (int e = 0; e < SEG; ++e) v[e] = ld16<true>(src + col[e]);
+}
+
+// acc += w_j * f32(v) when slot j's row is in range (a select, not a branch,
+// so no load waits on it); products and sums rounded separately.
+template <int K, int SEG>
+__device__ __forceinline__ void phase_sum(float (&acc)[SEG][8], const u32x4 (&v)[SEG], const Slots<K>& s, int j,
+                                          int64_t recv_rows) {
+#pragma clang fp contract(off)
+  const bool ok = row_ok(s.d[j], recv_rows);
+#pragma unroll
+  for (int e = 0; e < SEG; ++e) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float s0 = acc[e][2 * q] + s.w[j] * bf16_lo(v[e][q]);
+      const float s1 = acc[e][2 * q + 1] + s.w[j] * bf16_hi(v[e][q]);
+      acc[e][2 * q] = ok ? s0 : acc[e][2 * q];
+      acc[e][2 * q + 1] = ok ? s1 : acc[e][2 * q + 1];
+    }
+  }
+}
+
+// Slots j0 .. j0 + G - 1 (those below K) of a register set.
+template <int K, int SEG, int G>
+__device__ __forceinline__ void phase_load_set(u32x4 (&v)[G][SEG], const Slots<K>& s, int j0,
+                                               const u32x4* __restrict__ y, int64_t recv_rows, int row_vec,
+                                               const int (&col)[SEG]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (j0 + g < K) phase_load<K, SEG>(v[g], s, j0 + g, y, recv_rows, row_vec, col);
+}
+
+template <int K, int SEG, int G>
+__device__ __forceinline__ void phase_sum_set(float (&acc)[SEG][8], const u32x4 (&v)[G][SEG], const Slots<K>& s,
+                                              int j0, int64_t recv_rows) {
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (j0 + g < K) phase_sum<K, SEG>(acc, v[g], s, j0 + g, recv_rows);
+}
+
+// HELD <= kHeld output vectors held per wave; SEG vectors of a row are read
+// per source row and step (SEG KiB contiguous per row), G slots per register
+// set.  With several tokens per unit, SEG divides nv so that a step never
+// spans two tokens.
+template <int K, int SEG, int G, int HELD, bool EVEN>
 __global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __restrict__ y, u32x4* __restrict__ out,
                                                              const int32_t* __restrict__ dest_row,
                                                              const float* __restrict__ w, int64_t recv_rows,
                                                              int row_vec, int nv, int T, int tpu, int nseg, int seg,
                                                              int units) {
+  constexpr int kSteps = (HELD + SEG - 1) / SEG;
   const int lane = lane_id();
   const int stride = gridDim.x * (blockDim.x >> 6);
   for (int u = blockIdx.x * (blockDim.x >> 6) + wave_in_group(); u < units; u += stride) {
@@ -343,32 +396,53 @@ __global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __rest
     // (with power-of-two rows that would load a few HBM channels at a time).
     const int span = nseg == 1 ? nv : n_in;
     const int rot = u % span;
-    u32x4 held[kHeld];
+    u32x4 held[HELD];
     int t = t0, p = 0, c = c0 + rot;
     Slots<K> s;
     fetch_slots<K>(s, dest_row + (int64_t)t * K, w + (int64_t)t * K);
 #pragma unroll
-    for (int i = 0; i < kHeld; ++i) {
-      if (i < n_in) {
-        if (i > 0 && p == 0) fetch_slots<K>(s, dest_row + (int64_t)t * K, w + (int64_t)t * K);
-        const int col = c * kWave + lane;
-        u32x4 v[K];
+    for (int g = 0; g < kSteps; ++g) {
+      const int i0 = g * SEG;
+      if (i0 < n_in) {
+        if (i0 > 0 && p == 0) fetch_slots<K>(s, dest_row + (int64_t)t * K, w + (int64_t)t * K);
+        // Straight-line loads (no branch between a load and its use lets the
+        // compiler keep them all in flight): vectors past the unit and lanes
+        // past a ragged row end read a valid column and are never stored;
+        // slots whose row is out of range read row 0 and add nothing.
+        int col[SEG];
 #pragma unroll
-        for (int j = 0; j < K; ++j)
-          if (row_ok(s.d[j], recv_rows) && (EVEN || col < row_vec)) v[j] = ld16<true>(y + (int64_t)s.d[j] * row_vec + col);
-        float acc[1][8];
-        zero<1>(acc);
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-          if (row_ok(s.d[j], recv_rows)) {
-            const u32x4 one[1] = {v[j]};
-            accumulate<1>(acc, one, s.w[j], 1);
+        for (int e = 0; e < SEG; ++e) {
+          col[e] = c * kWave + lane;
+          if (!EVEN && col[e] >= row_vec) col[e] = row_vec - 1;
+          if (i0 + e < HELD && i0 + e < n_in) {
+            if (++c == c0 + span) c = c0;
+            ++p;
           }
         }
+        float acc[SEG][8];
+        zero<SEG>(acc);
+        // Two register sets of G slots each: the next set's loads are issued
+        // before the current set is summed, so G to 2G slots (G SEG to 2G SEG
+        // KiB per wave) stay in flight.  The scheduling barriers keep the
+        // compiler from trading that depth for fewer registers.  (Carrying
+        // the prefetch across steps as well spilled heavily.)
+        u32x4 va[G][SEG], vb[G][SEG];
+        phase_load_set<K, SEG, G>(va, s, 0, y, recv_rows, row_vec, col);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) held[i][q] = pack_bf16x2(acc[0][2 * q], acc[0][2 * q + 1]);
-        if (++c == c0 + span) c = c0;
-        if (++p == span) {
+        for (int j = 0; j < K; j += 2 * G) {
+          if (j + G < K) phase_load_set<K, SEG, G>(vb, s, j + G, y, recv_rows, row_vec, col);
+          __builtin_amdgcn_sched_barrier(0);
+          phase_sum_set<K, SEG, G>(acc, va, s, j, recv_rows);
+          if (j + 2 * G < K) phase_load_set<K, SEG, G>(va, s, j + 2 * G, y, recv_rows, row_vec, col);
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + G < K) phase_sum_set<K, SEG, G>(acc, vb, s, j + G, recv_rows);
+        }
+#pragma unroll
+        for (int e = 0; e < SEG; ++e)
+          if (i0 + e < HELD)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) held[i0 + e][q] = pack_bf16x2(acc[e][2 * q], acc[e][2 * q + 1]);
+        if (p == span) {
           p = 0;
           ++t;
         }
@@ -378,7 +452,7 @@ __global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __rest
     p = 0;
     c = c0 + rot;
 #pragma unroll
-    for (int i = 0; i < kHeld; ++i) {
+    for (int i = 0; i < HELD; ++i) {
       if (i < n_in) {
         const int col = c * kWave + lane;
         if (EVEN || col < row_vec) st16<true>(out + (int64_t)t * row_vec + col, held[i]);
@@ -395,15 +469,24 @@ __global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __rest
 using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int, int, int,
                          int);
 
-template <bool EVEN>
-PhaseFn pick_phase(int k) {
+template <int SEG, int G, int HELD, bool EVEN>
+PhaseFn pick_phase_k(int k) {
   switch (k) {
-    case 2: return combine_phase_kernel<2, EVEN>;
-    case 4: return combine_phase_kernel<4, EVEN>;
-    case 6: return combine_phase_kernel<6, EVEN>;
-    case 8: return combine_phase_kernel<8, EVEN>;
+    case 2: return combine_phase_kernel<2, SEG, G, HELD, EVEN>;
+    case 4: return combine_phase_kernel<4, SEG, G, HELD, EVEN>;
+    case 6: return combine_phase_kernel<6, SEG, G, HELD, EVEN>;
+    case 8: return combine_phase_kernel<8, SEG, G, HELD, EVEN>;
     default: return nullptr;
   }
+}
+
+// Register sets of 4 KiB per wave whatever the contiguous run: SEG x G = 4.
+// (Runs of 4 vectors do not fit: two sets plus 32 accumulators and the held
+// output spill at k >= 6.)
+template <bool EVEN>
+PhaseFn pick_phase(int seg_vec, int held, int k) {
+  if (seg_vec == 2) return held == 14 ? pick_phase_k<2, 2, 14, EVEN>(k) : pick_phase_k<2, 2, 16, EVEN>(k);
+  return held == 14 ? pick_phase_k<1, 4, 14, EVEN>(k) : pick_phase_k<1, 4, 16, EVEN>(k);
 }
 
 struct PhaseShape {
@@ -434,7 +517,15 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
                         const float* w, int T, int k, void* out, hipStream_t stream) {
   const bool even = row_vec % kWave == 0;
   const PhaseShape ps = phase_shape(row_vec);
-  PhaseFn fn = even ? pick_phase<true>(k) : pick_phase<false>(k);
+  // vectors per contiguous read: 1 by default (runs of 2 measured 5% slower
+  // at the train shape: fewer slots in flight); a requested slab of 2 takes
+  // runs of 2 where a step can; 14 held vectors when a unit never needs more
+  // (whole tokens at H = 7168), which frees registers for the reads
+  int seg_vec = 1;
+  if (b.slab_vpl >= 2 && (ps.tpu == 1 || ps.nv % 2 == 0)) seg_vec = 2;
+  const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
+  const int held = unit_vec <= 14 ? 14 : 16;
+  PhaseFn fn = even ? pick_phase<true>(seg_vec, held, k) : pick_phase<false>(seg_vec, held, k);
   if (!fn) return hipErrorInvalidValue;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   const size_t lds_bytes = b.num_cus > 0 ? kExclusiveLds : 0;
@@ -447,7 +538,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   // batches apart, which waves that loop over several units would not.
   const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
   const int64_t batch = ps.nseg == 1 ? wave_slots * ps.tpu : wave_slots / ps.nseg > 0 ? wave_slots / ps.nseg : 1;
-  for (int64_t t0 = 0; t0 < T; t0 += batch) {
+  for (int64_t t0 = 0; t0 < T;) {
     const int tb = (int)(T - t0 < batch ? T - t0 : batch);
     const int units = (int)phase_units(ps, tb);
     int grid = (units + kPhaseWpg - 1) / kPhaseWpg;
@@ -458,6 +549,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
                        ps.nv, tb, ps.tpu, ps.nseg, ps.seg, units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    t0 += tb;
   }
   return hipSuccess;
 }

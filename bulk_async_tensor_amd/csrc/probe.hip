@@ -116,6 +116,65 @@ __global__ __launch_bounds__(1024) void bw_mix_kernel(const u32x4* __restrict__ 
 // The 8:1 mix with burstier writes: a wave reads 64 KiB contiguous (8 rounds
 // of 8 KiB, folded into 8 accumulators) and then writes 8 KiB contiguous.
 // nvec counts the read side (multiple of 4096 vectors).
+// Arrival count and generation of the soft grid barrier (zero when the code
+// object loads).  Every workgroup of a launch arrives exactly once; the last
+// arrival resets the count and advances the generation.
+__device__ unsigned int g_probe_barrier[2];
+
+// Waits until every workgroup of the grid has arrived or `timeout` ticks of
+// the 100 MHz real-time clock have passed, whichever comes first.  The wait
+// orders nothing that correctness depends on: it only holds the grid's
+// writes back until its reads are done.  Called by all threads.
+__device__ void soft_grid_barrier(unsigned int* bar, uint64_t timeout) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned arrived = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    if (arrived == gridDim.x) {
+      __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen &&
+             __builtin_amdgcn_s_memrealtime() - t0 < timeout)
+        __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// Operation 7 with depth field 2: the 8:1 phases of operation 7 done once per
+// wave (the launch needs no more chunks than waves), with a soft grid
+// barrier (at most 20 us) between every wave's reads and its writes.
+__global__ __launch_bounds__(1024) void bw_phase_bar_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int64_t nvec) {
+  constexpr int kHeld = 16;
+  const int lane = lane_id();
+  const int64_t nchunk = nvec / (8 * kHeld * kWave);
+  const int64_t q = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_in_group();
+  const bool has = q < nchunk;
+  u32x4 acc[kHeld];
+  if (has) {
+    const u32x4* s = src + q * 8 * kHeld * kWave + lane;
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) acc[i] = ld16<true>(s + i * kWave);
+#pragma unroll
+    for (int g = 2; g < 16; ++g) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ld16<true>(s + (g * 8 + i) * kWave);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[(g & 1) * 8 + i] ^= v[i];
+    }
+  }
+  soft_grid_barrier(g_probe_barrier, 2000);
+  if (has) {
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) st16<true>(dst + q * kHeld * kWave + i * kWave + lane, acc[i]);
+  }
+}
+
 // Operation 7: the 8:1 mix in two phases per wave.  A wave reads 128 KiB
 // (eight 16 KiB blocks folded into 16 vectors per lane) before it writes its
 // 16 KiB.  Launched with one chunk per wave, every wave of the grid reads
@@ -145,6 +204,32 @@ __global__ __launch_bounds__(1024) void bw_phase_kernel(const u32x4* __restrict_
     }
 #pragma unroll
     for (int i = 0; i < kHeld; ++i) st16<true>(dst + q * kHeld * kWave + i * kWave + lane, acc[i]);
+  }
+}
+
+// Operation 7 with depth field 1: the 1:8 mix in two phases per wave.  A
+// wave reads 16 KiB and then writes it eight times (vector i of copy r with
+// r folded into its first word), 128 KiB.
+__global__ __launch_bounds__(1024) void bw_phase_out_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int64_t nvec) {
+  constexpr int kHeld = 16;
+  const int lane = lane_id();
+  const int64_t wpg = blockDim.x >> 6;
+  const int64_t nchunk = nvec / (8 * kHeld * kWave);
+  for (int64_t q = (int64_t)blockIdx.x * wpg + wave_in_group(); q < nchunk; q += (int64_t)gridDim.x * wpg) {
+    u32x4 v[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) v[i] = ld16<true>(src + (q * kHeld + i) * kWave + lane);
+    u32x4* d = dst + q * 8 * kHeld * kWave + lane;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+      for (int i = 0; i < kHeld; ++i) {
+        u32x4 o = v[i];
+        o[0] ^= (unsigned)r;
+        st16<true>(d + (r * kHeld + i) * kWave, o);
+      }
+    }
   }
 }
 
@@ -228,6 +313,8 @@ hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst
           : op == 4 ? (BwFn)bw_mix_kernel<0>
           : op == 5 ? (BwFn)bw_mix_kernel<1>
           : op == 6 ? (BwFn)bw_mix_burst_kernel
+          : depth_code == 1 ? (BwFn)bw_phase_out_kernel
+          : depth_code == 2 ? (BwFn)bw_phase_bar_kernel
                     : (BwFn)bw_phase_kernel;
   const size_t per_wave = op == 3 ? (size_t)depth * kWaveVecBytes : 0;
   int wpg, grid;
@@ -251,6 +338,8 @@ hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst
     lds = per_wave * wpg;
   }
   if (grid < 1) grid = 1;
+  // the barrier kernel handles one chunk per wave
+  if (op == 7 && depth_code == 2 && nvec / (8 * 16 * kWave) > (int64_t)grid * wpg) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = allow_dynamic_lds((const void*)fn, lds);
     if (e != hipSuccess) return e;

@@ -229,13 +229,19 @@ const char* ep_last_error(void);
  *               (each wave: 1 KiB in, 8 KiB out);
  *               6 mixed 8:1 in bursts -- as 4, but each wave reads 64 KiB
  *               and then writes 8 KiB;
- *               7 mixed 8:1 in phases -- as 4, but each wave reads 128 KiB
- *               and then writes 16 KiB, on one workgroup of 16 waves per
- *               CU whatever the budget; with bytes = 128 KiB x waves each
- *               wave does this once, so the grid reads first and writes
- *               last;
+ *               7 mixed in phases, on one workgroup of 16 waves per CU
+ *               whatever the budget: with depth field 0, 8:1 as 4, each
+ *               wave reading 128 KiB and then writing 16 KiB; with depth
+ *               field 1, 1:8 as 5, each wave reading 16 KiB and then
+ *               writing it 8 times (copy r has r xor-ed into the first
+ *               word of each 16-byte vector); with bytes = 128 KiB x waves
+ *               each wave does this once, so the grid reads first and
+ *               writes last; with depth field 2, the 8:1 form once per
+ *               wave with a bounded wait (at most 20 us) for every
+ *               workgroup's reads to finish before any writes (bytes above
+ *               128 KiB x waves fail with EP_ERR_HIP);
  *               4 and 5 need bytes % 8192 == 0, 6 bytes % 65536 == 0,
- *               7 bytes % 131072 == 0; they ignore depth and policy
+ *               7 bytes % 131072 == 0; 4-6 ignore depth, 4-7 policy
  *   bits [5:4]  depth: 16-byte vectors in flight per lane, 0 -> 8, 1 -> 16,
  *               2 -> 32 (3 is invalid)
  *   bits [10:8] cache policy of the loads of operations 1 and 3: 0 nt,

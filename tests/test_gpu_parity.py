@@ -297,7 +297,7 @@ def test_combine_phase_units(H, T, budget):
     assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2", "phase"])
 @pytest.mark.parametrize("slab", [1, 2, 4])
 @pytest.mark.parametrize("budget", [0, 24])
 def test_combine_slab_sizes(variant, slab, budget):
@@ -367,6 +367,19 @@ def test_bw_probe_mixed_ratios():
     b16 = big.view(-1, 8, 16, 64, 4).cpu().numpy()  # [chunk, block, i, lane, word]
     want = np.bitwise_xor.reduce(b16, axis=1).reshape(-1)
     assert np.array_equal(phase.cpu().numpy(), want)
+    phase.zero_()
+    ep.ep_bw_probe(0x27, big, phase, n)  # the same with the bounded grid-wide wait between reads and writes
+    torch.cuda.synchronize()
+    assert np.array_equal(phase.cpu().numpy(), want)
+    fan = torch.zeros_like(big)
+    ep.ep_bw_probe(0x17, small, fan, n)  # 1:8 in phases -- each 16 KiB in written 8 times, r in the first word
+    torch.cuda.synchronize()
+    f = fan.view(-1, 8, 16, 64, 4).cpu().numpy()  # [chunk, copy, i, lane, word]
+    s16 = small.view(-1, 16, 64, 4).cpu().numpy()
+    for r in range(8):
+        want = s16.copy()
+        want[..., 0] ^= r
+        assert np.array_equal(f[:, r], want)
     out = torch.zeros_like(big)
     ep.ep_bw_probe(5, small, out, n)  # 1:8 -- each 1 KiB chunk written 8 times (x ^ i in the first word)
     torch.cuda.synchronize()
