@@ -536,15 +536,21 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   // One launch per batch of tokens that gives every wave of the grid one
   // unit: the launch boundary keeps the read and write phases of the
   // batches apart, which waves that loop over several units would not.
+  // Batches are of equal size, and a batch spreads over every CU with as
+  // few waves per workgroup as it needs (a small last batch on a few full
+  // CUs measured 7% slower at 192 CUs).
   const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
-  const int64_t batch = ps.nseg == 1 ? wave_slots * ps.tpu : wave_slots / ps.nseg > 0 ? wave_slots / ps.nseg : 1;
+  const int64_t max_batch = ps.nseg == 1 ? wave_slots * ps.tpu : wave_slots / ps.nseg > 0 ? wave_slots / ps.nseg : 1;
+  const int64_t nbatch = (T + max_batch - 1) / max_batch;
+  int64_t batch = (T + nbatch - 1) / nbatch;
+  if (ps.nseg == 1) batch = (batch + ps.tpu - 1) / ps.tpu * ps.tpu;  // whole units
   for (int64_t t0 = 0; t0 < T;) {
     const int tb = (int)(T - t0 < batch ? T - t0 : batch);
     const int units = (int)phase_units(ps, tb);
-    int grid = (units + kPhaseWpg - 1) / kPhaseWpg;
-    if (grid > cus) grid = cus;
+    int grid = units < cus ? units : cus;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kPhaseWpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(y),
+    const int wpg = (units + grid - 1) / grid;  // <= kPhaseWpg
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(y),
                        static_cast<u32x4*>(out) + t0 * row_vec, dest_row + t0 * k, w + t0 * k, recv_rows, row_vec,
                        ps.nv, tb, ps.tpu, ps.nseg, ps.seg, units);
     hipError_t e = hipGetLastError();
@@ -554,14 +560,17 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   return hipSuccess;
 }
 
-// The phase kernel is the default on the whole device when a launch gives
-// most waves of the grid a unit (it reads all rows of its unit before its
-// first store, so a wave with little work gains nothing and a small batch
-// would sit on few CUs).
+// The phase kernel is the default on at least half the device when the
+// batch gives most waves of a full grid a unit: it reads all rows of its
+// unit before its first store, so a wave with little work gains nothing
+// (decode batches stay on the register kernel), and on fewer CUs the
+// per-CU read rate, not the read/write turnaround, is the bound.
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
-  if (b.num_cus > 0 || !(k == 2 || k == 4 || k == 6 || k == 8)) return false;
+  if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  if (2 * cus < b.device_cus) return false;
   const int64_t units = phase_units(phase_shape(row_vec), T);
-  return units * 4 >= (int64_t)b.device_cus * kPhaseWpg * 3;
+  return units * 4 >= (int64_t)cus * kPhaseWpg * 3;
 }
 
 using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);
