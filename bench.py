@@ -34,6 +34,10 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--cold", type=int, default=50,
+                   help="launches per kernel timed one by one after a 1 GiB cache flush (0: skip)")
+    p.add_argument("--cold-study", action="store_true",
+                   help="also time single launches with no flush and with write / read / write+read flushes")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="train")
     p.add_argument("--variant", default="auto")
@@ -162,6 +166,44 @@ class Setup:
             torch.cuda.synchronize()
             per[name] = e0.elapsed_time(e1) / steps
         return ms, per
+
+
+def cold_times(s, iters, flush_mode="write"):
+    """Per-launch times with cold caches: before each launch 1 GiB of other
+    memory is written (torch fill), read (the read probe) or both, which
+    evicts the L2s and the 256 MB Infinity Cache ("none": no flush, one launch
+    at a time); one launch sits between two HIP events on its stream.
+    Returns {kernel: [p10, median, p90]} in us."""
+    import bulk_async_tensor_amd as ep
+
+    torch = s.torch
+    stream = s.stream if s.stream is not None else torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    flush.fill_(1)
+    out = {}
+    for name, fn in (("layout", s.layout), ("dispatch", s.dispatch), ("combine", s.combine)):
+        if name == "dispatch" and not s.do_dispatch:
+            continue
+        fn()
+        evs = []
+        for i in range(iters):
+            if "write" in flush_mode:
+                with torch.cuda.stream(stream):
+                    flush.fill_(i)
+            if "read" in flush_mode:
+                ep.ep_bw_probe(1, flush, sink, flush.numel() * 4, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        pick = lambda q: us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))]
+        out[name] = [round(pick(0.1), 2), round(pick(0.5), 2), round(pick(0.9), 2)]
+    del flush
+    return out
 
 
 def read_traffic(kernel, workload):
@@ -539,6 +581,11 @@ def main():
         ms, per = s.run(args.steps, args.warmup)
         results[label] = (ms, per)
     ep.ep_set_num_cus(0)
+    cold = cold_times(s, args.cold) if args.cold > 0 else None
+    if args.cold_study:
+        for mode in ("none", "write", "read", "write_read"):
+            print(json.dumps({"kind": "cold_study", "workload": args.workload, "flush": mode,
+                              "us_p10_p50_p90": cold_times(s, args.cold or 50, mode)}), flush=True)
     if not args.only_all:
         # the same budget as a CU-masked stream with an ordinary grid
         mask_stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(args.budget)))
@@ -575,6 +622,9 @@ def main():
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "kernel_GBs": {k: round(s.bytes[k] / (per[k] * 1e6), 1) for k in per if per[k] > 0 and s.bytes[k]},
+        "cold_cache_us_p10_p50_p90": cold,
+        "cold_cache_GBs_p50": None if cold is None else {
+            k: round(s.bytes[k] / (v[1] * 1e3), 1) for k, v in cold.items() if s.bytes[k]},
         f"cu{args.budget}": None if f"cu{args.budget}" not in results else {
             "value": round(s.step_bytes / (ms_b * 1e-3) / 1e9, 2),
             "unit": "GB/s",

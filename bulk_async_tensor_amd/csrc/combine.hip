@@ -313,12 +313,6 @@ __global__ __launch_bounds__(1024) void combine_lds2_kernel(EP_COMBINE_ARGS) {
   }
 }
 
-// Phase kernel geometry: vectors (16 bytes per lane) of finished output a
-// wave holds before storing.  A unit is tpu whole tokens when a row has at
-// most kHeld vectors per lane (nseg == 1), else one of nseg segments of seg
-// vectors of one token.
-constexpr int kHeld = 16;
-
 // Loads slot j's SEG vectors at the given columns (row 0 when the slot's row
 // is out of range: those values are never summed).
 template <int K, int SEG>
@@ -367,7 +361,7 @@ __device__ __forceinline__ void phase_sum_set(float (&acc)[SEG][8], const u32x4 
     if (j0 + g < K) phase_sum<K, SEG>(acc, v[g], s, j0 + g, recv_rows);
 }
 
-// HELD <= kHeld output vectors held per wave; SEG vectors of a row are read
+// HELD <= kPhaseHeld output vectors held per wave; SEG vectors of a row are read
 // per source row and step (SEG KiB contiguous per row), G slots per register
 // set.  With several tokens per unit, SEG divides nv so that a step never
 // spans two tokens.
@@ -489,29 +483,6 @@ PhaseFn pick_phase(int seg_vec, int held, int k) {
   return held == 14 ? pick_phase_k<1, 4, 14, EVEN>(k) : pick_phase_k<1, 4, 16, EVEN>(k);
 }
 
-struct PhaseShape {
-  int nv, tpu, nseg, seg;
-};
-
-PhaseShape phase_shape(int row_vec) {
-  PhaseShape p;
-  p.nv = (row_vec + kWave - 1) / kWave;
-  p.tpu = 1;
-  p.nseg = 1;
-  p.seg = p.nv;
-  if (p.nv <= kHeld) {
-    p.tpu = kHeld / p.nv;
-  } else {
-    p.nseg = (p.nv + kHeld - 1) / kHeld;
-    p.seg = (p.nv + p.nseg - 1) / p.nseg;
-  }
-  return p;
-}
-
-int64_t phase_units(const PhaseShape& p, int64_t T) { return p.nseg == 1 ? (T + p.tpu - 1) / p.tpu : T * p.nseg; }
-
-// 16 waves per workgroup; at this register use a CU holds one such workgroup.
-constexpr int kPhaseWpg = 16;
 
 hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int row_vec, const int32_t* dest_row,
                         const float* w, int T, int k, void* out, hipStream_t stream) {
@@ -539,11 +510,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   // Batches are of equal size, and a batch spreads over every CU with as
   // few waves per workgroup as it needs (a small last batch on a few full
   // CUs measured 7% slower at 192 CUs).
-  const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
-  const int64_t max_batch = ps.nseg == 1 ? wave_slots * ps.tpu : wave_slots / ps.nseg > 0 ? wave_slots / ps.nseg : 1;
-  const int64_t nbatch = (T + max_batch - 1) / max_batch;
-  int64_t batch = (T + nbatch - 1) / nbatch;
-  if (ps.nseg == 1) batch = (batch + ps.tpu - 1) / ps.tpu * ps.tpu;  // whole units
+  const int64_t batch = phase_batch(ps, T, cus);
   for (int64_t t0 = 0; t0 < T;) {
     const int tb = (int)(T - t0 < batch ? T - t0 : batch);
     const int units = (int)phase_units(ps, tb);

@@ -324,16 +324,132 @@ RowsFn rows_pick(int vpl) {
   }
 }
 
+// The phased dispatch: a wave's unit is up to 16 KiB of source rows (one
+// token at H = 7168).  It reads them all into registers first, with every
+// load in flight together, and then writes the k copies.  With one unit per
+// wave on every CU, the whole grid reads x first and writes last, so the
+// reads never queue behind the writes: the dispatch costs the same whether
+// x is still in the caches or not (the staged kernels wait on each unit's
+// read under full write traffic and are twice as slow when x is not).
+template <int K, bool EVEN>
+__global__ __launch_bounds__(1024) void dispatch_phase_kernel(const u32x4* __restrict__ x, u32x4* __restrict__ recv,
+                                                              const int32_t* __restrict__ dest_row,
+                                                              int64_t recv_rows, int row_vec, int nv, int T, int tpu,
+                                                              int nseg, int seg, int units) {
+  constexpr int HELD = kPhaseHeld;
+  const int lane = lane_id();
+  const int stride = gridDim.x * (blockDim.x >> 6);
+  for (int u = blockIdx.x * (blockDim.x >> 6) + wave_in_group(); u < units; u += stride) {
+    int t0, c0, n_in;
+    if (nseg == 1) {
+      t0 = u * tpu;
+      c0 = 0;
+      n_in = (T - t0 < tpu ? T - t0 : tpu) * nv;
+    } else {
+      t0 = u / nseg;
+      c0 = (u - t0 * nseg) * seg;
+      n_in = nv - c0 < seg ? nv - c0 : seg;
+    }
+    const int span = nseg == 1 ? nv : n_in;
+    // rotated start per unit, as in the phased combine
+    const int rot = u % span;
+    // Straight-line loads: vectors past the unit re-read the unit's first
+    // vector, lanes past a ragged row end its last; neither is stored.
+    u32x4 held[HELD];
+    {
+      int t = t0, p = 0, c = c0 + rot;
+#pragma unroll
+      for (int i = 0; i < HELD; ++i) {
+        const bool in = i < n_in;
+        int col = (in ? c : c0 + rot) * kWave + lane;
+        if (!EVEN && col >= row_vec) col = row_vec - 1;
+        held[i] = ld16<false>(x + (int64_t)(in ? t : t0) * row_vec + col);
+        if (in) {
+          if (++c == c0 + span) c = c0;
+          if (++p == span) {
+            p = 0;
+            ++t;
+          }
+        }
+      }
+    }
+    int t = t0, p = 0, c = c0 + rot;
+    Dests<K> ds;
+    fetch_dests<K>(ds, dest_row + (int64_t)t * K);
+#pragma unroll
+    for (int i = 0; i < HELD; ++i) {
+      if (i < n_in) {
+        if (i > 0 && p == 0) fetch_dests<K>(ds, dest_row + (int64_t)t * K);
+        const int col = c * kWave + lane;
+        if (EVEN || col < row_vec) {
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            const int64_t d = ds.d[j];
+            if ((uint64_t)d < (uint64_t)recv_rows) st16<true>(recv + d * row_vec + col, held[i]);
+          }
+        }
+        if (++c == c0 + span) c = c0;
+        if (++p == span) {
+          p = 0;
+          ++t;
+        }
+      }
+    }
+  }
+}
+
+using PhaseDispatchFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, int, int, int, int, int, int);
+
+template <bool EVEN>
+PhaseDispatchFn pick_phase_dispatch(int k) {
+  switch (k) {
+    case 2: return dispatch_phase_kernel<2, EVEN>;
+    case 4: return dispatch_phase_kernel<4, EVEN>;
+    case 6: return dispatch_phase_kernel<6, EVEN>;
+    case 8: return dispatch_phase_kernel<8, EVEN>;
+    default: return nullptr;
+  }
+}
+
+hipError_t launch_dispatch_phase(const Budget& b, const void* x, int T, int row_vec, const int32_t* dest_row, int k,
+                                 void* recv, int64_t recv_rows, hipStream_t stream) {
+  const bool even = row_vec % kWave == 0;
+  const PhaseShape ps = phase_shape(row_vec);
+  PhaseDispatchFn fn = even ? pick_phase_dispatch<true>(k) : pick_phase_dispatch<false>(k);
+  if (!fn) return hipErrorInvalidValue;
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  const size_t lds_bytes = b.num_cus > 0 ? kExclusiveLds : 0;
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t batch = phase_batch(ps, T, cus);
+  for (int64_t t0 = 0; t0 < T;) {
+    const int tb = (int)(T - t0 < batch ? T - t0 : batch);
+    const int units = (int)phase_units(ps, tb);
+    int grid = units < cus ? units : cus;
+    if (grid < 1) grid = 1;
+    const int wpg = (units + grid - 1) / grid;  // <= kPhaseWpg
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x) + t0 * row_vec,
+                       static_cast<u32x4*>(recv), dest_row + t0 * k, recv_rows, row_vec, ps.nv, tb, ps.tpu, ps.nseg,
+                       ps.seg, units);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    t0 += tb;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {
   // direct-to-LDS staging measured fastest at every compute-unit budget
-  // ("phase" is a combine kernel; dispatch takes its default for it)
-  if (v == Variant::Auto || v == Variant::Phase) v = Variant::Lds1;
+  if (v == Variant::Auto) v = Variant::Lds1;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
-  if (v == Variant::Lds2 && !known_k) v = Variant::Lds1;
+  if ((v == Variant::Lds2 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;
+  if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
   // default slabs of at most 8 KiB (half rows at H = 7168); whole 14 KiB
   // rows per wave measured no faster.  A requested size may go to 16 for the

@@ -70,4 +70,45 @@ __device__ __forceinline__ void store_one(const u32x4 (&v)[VPL], u32x4* __restri
   }
 }
 
+// ---- phased units: a wave holds up to kPhaseHeld vectors per lane (16 KiB)
+// of rows in registers between reading and writing them.  A unit is tpu
+// whole rows when a row has at most kPhaseHeld vectors per lane (nseg == 1),
+// else one of nseg segments of seg vectors of one row.  Host-side geometry.
+constexpr int kPhaseHeld = 16;
+constexpr int kPhaseWpg = 16;  // waves per workgroup; one such workgroup fits a CU
+
+struct PhaseShape {
+  int nv, tpu, nseg, seg;
+};
+
+inline PhaseShape phase_shape(int row_vec) {
+  PhaseShape p;
+  p.nv = (row_vec + kWave - 1) / kWave;
+  p.tpu = 1;
+  p.nseg = 1;
+  p.seg = p.nv;
+  if (p.nv <= kPhaseHeld) {
+    p.tpu = kPhaseHeld / p.nv;
+  } else {
+    p.nseg = (p.nv + kPhaseHeld - 1) / kPhaseHeld;
+    p.seg = (p.nv + p.nseg - 1) / p.nseg;
+  }
+  return p;
+}
+
+inline int64_t phase_units(const PhaseShape& p, int64_t T) {
+  return p.nseg == 1 ? (T + p.tpu - 1) / p.tpu : T * p.nseg;
+}
+
+// Rows per launch so that every launch gives each wave of a grid of `cus`
+// workgroups at most one unit, in launches of equal size (whole units).
+inline int64_t phase_batch(const PhaseShape& p, int64_t T, int cus) {
+  const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
+  const int64_t max_batch = p.nseg == 1 ? wave_slots * p.tpu : (wave_slots / p.nseg > 0 ? wave_slots / p.nseg : 1);
+  const int64_t nbatch = (T + max_batch - 1) / max_batch;
+  int64_t batch = (T + nbatch - 1) / nbatch;
+  if (p.nseg == 1) batch = (batch + p.tpu - 1) / p.tpu * p.tpu;
+  return batch;
+}
+
 }  // namespace ep
