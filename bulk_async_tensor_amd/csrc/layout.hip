@@ -206,22 +206,42 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
 constexpr int kFusedChunk = 1024;   // entries per workgroup: 16 waves x 64
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
-constexpr int kFusedBatch = 4;  // tokens per thread whose ids are loaded together
 
-// Counts token t's k entries into the (chunk, expert) histogram and checks
-// them (runtime k).
+// Reads the k ids of token t, checks them and adds them to the (chunk,
+// expert) histogram.  KT > 0: k known at compile time, so the loads of a
+// token are independent and issued together.
+template <int KT>
 __device__ __forceinline__ void count_token(const int32_t* __restrict__ idx, int t, int k, int E, int32_t* cnt,
                                             int& bad) {
-  const int32_t* r = idx + (int64_t)t * k;
-  for (int j = 0; j < k; ++j) {
-    const int e = r[j];
-    const int i = t * k + j;
-    if ((unsigned)e < (unsigned)E) {
-      atomicAdd(&cnt[(i >> 10) * E + e], 1);
-      for (int j2 = 0; j2 < j; ++j2)
-        if (r[j2] == e) bad |= kStatusDuplicate;
-    } else {
-      bad |= kStatusOutOfRange;
+  constexpr int KA = KT > 0 ? KT : 1;
+  if constexpr (KT > 0) {
+    int e[KA];
+#pragma unroll
+    for (int j = 0; j < KA; ++j) e[j] = idx[(int64_t)t * KA + j];
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+      const int i = t * KA + j;
+      if ((unsigned)e[j] < (unsigned)E) {
+        atomicAdd(&cnt[(i >> 10) * E + e[j]], 1);
+#pragma unroll
+        for (int j2 = 0; j2 < j; ++j2)
+          if (e[j2] == e[j]) bad |= kStatusDuplicate;
+      } else {
+        bad |= kStatusOutOfRange;
+      }
+    }
+  } else {
+    const int32_t* r = idx + (int64_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      const int e = r[j];
+      const int i = t * k + j;
+      if ((unsigned)e < (unsigned)E) {
+        atomicAdd(&cnt[(i >> 10) * E + e], 1);
+        for (int j2 = 0; j2 < j; ++j2)
+          if (r[j2] == e) bad |= kStatusDuplicate;
+      } else {
+        bad |= kStatusOutOfRange;
+      }
     }
   }
 }
@@ -255,37 +275,11 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
 
   // Every workgroup histograms all tokens (thread per token) and validates
   // them, so each one knows the totals and the global status by itself.
+  // Two tokens per trip keep 2k loads in flight per thread.
   int bad = 0;
-  if constexpr (KT > 0) {
-    // kFusedBatch tokens per thread per trip, all their ids loaded before any
-    // is counted (a token past T re-reads the last one and counts nothing),
-    // so the trip waits for memory once instead of once per token.
-    for (int t0 = tid; t0 < T; t0 += kFusedBatch * kFusedThreads) {
-      int e[kFusedBatch][KT];
-#pragma unroll
-      for (int b = 0; b < kFusedBatch; ++b) {
-        const int t = min(t0 + b * kFusedThreads, T - 1);
-#pragma unroll
-        for (int j = 0; j < KT; ++j) e[b][j] = idx[(int64_t)t * KT + j];
-      }
-#pragma unroll
-      for (int b = 0; b < kFusedBatch; ++b) {
-        const int t = t0 + b * kFusedThreads;
-        if (t < T) {
-#pragma unroll
-          for (int j = 0; j < KT; ++j) {
-            const int i = t * KT + j;
-            const bool ok = (unsigned)e[b][j] < (unsigned)E;
-            if (ok) atomicAdd(&cnt[(i >> 10) * E + e[b][j]], 1);
-            bad |= ok ? 0 : kStatusOutOfRange;
-#pragma unroll
-            for (int j2 = 0; j2 < j; ++j2) bad |= (ok && e[b][j2] == e[b][j]) ? kStatusDuplicate : 0;
-          }
-        }
-      }
-    }
-  } else {
-    for (int t = tid; t < T; t += kFusedThreads) count_token(idx, t, k, E, cnt, bad);
+  for (int t = tid; t < T; t += 2 * kFusedThreads) {
+    count_token<KT>(idx, t, k, E, cnt, bad);
+    if (t + kFusedThreads < T) count_token<KT>(idx, t + kFusedThreads, k, E, cnt, bad);
   }
   if (bad) atomicOr(&s_status, bad);
   __syncthreads();
