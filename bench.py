@@ -57,6 +57,7 @@ def parse_args():
     p.add_argument("--kernels-only", action="store_true",
                    help="a few launches of each kernel and of a 256 MiB copy probe (for counter passes)")
     p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
+    p.add_argument("--no-reduce", action="store_true", help="skip timing the reduce-on-store combine")
     return p.parse_args()
 
 
@@ -204,6 +205,44 @@ def cold_times(s, iters, flush_mode="write"):
         out[name] = [round(pick(0.1), 2), round(pick(0.5), 2), round(pick(0.9), 2)]
     del flush
     return out
+
+
+def reduce_times(s, steps, budgets):
+    """ep_combine_reduce (zero fill, scatter-add with fp32 atomics, bf16
+    conversion: three launches) on the workload's expert outputs: `steps`
+    back-to-back calls between two HIP events on the launch stream, per CU
+    budget.  GB/s uses the combine's algorithmic bytes, so the figure compares
+    directly with ep_combine's."""
+    torch, ep = s.torch, s.ep
+    ws = torch.empty(max(16, ep.ep_combine_reduce_workspace_bytes(s.T, s.H)), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(s.out)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ep.ep_combine_reduce(s.y, s.src_token, s.dest_row, s.w, out, workspace=ws, stream=stream)
+
+    res = {}
+    for b in budgets:
+        ep.ep_set_num_cus(b)
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res["all" if b == 0 else f"cu{b}"] = {"ms": round(ms, 5), "GBs": round(s.bytes["combine"] / (ms * 1e6), 1)}
+    ep.ep_set_num_cus(0)
+    # the same inputs through ep_combine: the largest difference in bf16 ulps
+    s.combine()
+    torch.cuda.synchronize()
+    a = out.view(torch.int16).int()
+    b = s.out.view(torch.int16).int()
+    res["max_ulp_vs_ep_combine"] = int((a - b).abs().max().item()) if a.numel() else 0
+    del ws
+    return res
 
 
 def read_traffic(kernel, workload):
@@ -653,6 +692,9 @@ def main():
             "algorithmic_bytes": s.bytes[dom],
         },
     }
+    if not args.no_reduce:
+        line["combine_reduce"] = reduce_times(s, min(args.steps, 50),
+                                              [0] if args.only_all else [0, args.budget])
     if args.graph:
         ms_g, ms_e = graph_step(s, args.steps, args.warmup)
         line["graph_replay"] = {"ms_per_step": round(ms_g, 5), "eager_ms_per_step": round(ms_e, 5),

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "ep_layout_dispatch": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p,
                                     _c_i64, _p]),
     "ep_combine": (_c_int, [_p, _c_i64, _c_int, _p, _p, _c_int, _c_int, _p, _p]),
+    "ep_combine_reduce_workspace_bytes": (_c_sz, [_c_int, _c_int]),
+    "ep_combine_reduce": (_c_int, [_p, _c_i64, _c_int, _p, _p, _p, _c_int, _c_int, _p, _p, _c_sz, _p]),
     "ep_status_string": (ctypes.c_char_p, [_c_int]),
     "ep_last_error": (ctypes.c_char_p, []),
     "ep_bw_probe": (_c_int, [_c_int, _p, _p, _c_i64, _p]),
@@ -272,6 +274,38 @@ def ep_combine(y, dest_row, topk_w, out, stream=None):
     k = dest_row.shape[1]
     _check(lib().ep_combine(_ptr(y), y.shape[0], H, _ptr(dest_row), _ptr(topk_w), T, k, _ptr(out),
                             _stream(stream)), "ep_combine")
+    return out
+
+
+def ep_combine_reduce_workspace_bytes(T, H):
+    return lib().ep_combine_reduce_workspace_bytes(int(T), int(H))
+
+
+def ep_combine_reduce(y, src_token, dest_row, topk_w, out, workspace=None, stream=None):
+    """Reduce-on-store combine: out[t] = bf16(sum of w[t, j] * y[r] over the rows r
+    that src_token assigns to t and dest_row[t, j] lists), fp32 atomics into
+    ``workspace`` (float32 [T, H] worth of bytes; allocated when None)."""
+    import torch
+
+    _device_tensor(y, "y", torch.bfloat16)
+    _device_tensor(src_token, "src_token", torch.int32)
+    _device_tensor(dest_row, "dest_row", torch.int32)
+    _device_tensor(topk_w, "topk_w", torch.float32)
+    _device_tensor(out, "out", torch.bfloat16)
+    T, H = out.shape
+    if dest_row.dim() != 2 or dest_row.shape[0] != T or tuple(topk_w.shape) != tuple(dest_row.shape):
+        raise ValueError("dest_row and topk_w must both be [T, k]")
+    if y.dim() != 2 or y.shape[1] != H or src_token.numel() < y.shape[0]:
+        raise ValueError("y must be [R, H] and src_token hold at least R entries")
+    k = dest_row.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(ep_combine_reduce_workspace_bytes(T, H), 16), dtype=torch.uint8,
+                                device=out.device)
+    else:
+        _device_tensor(workspace, "workspace")
+    _check(lib().ep_combine_reduce(_ptr(y), y.shape[0], H, _ptr(src_token), _ptr(dest_row), _ptr(topk_w), T, k,
+                                   _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "ep_combine_reduce")
     return out
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libep.so")
-SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "decode.hip", "probe.hip"]
+SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "combine_reduce.hip", "decode.hip", "probe.hip"]
 ARCH = "gfx950"
 
 
@@ -26,6 +26,7 @@ KERNEL_SOURCES = {
     "layout": ["layout.hip", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
     "dispatch": ["dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
     "combine": ["combine.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
+    "combine_reduce": ["combine_reduce.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp", "ep_api.hip"],
 }
 
 

@@ -301,6 +301,40 @@ int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row,
   return EP_OK;
 }
 
+size_t ep_combine_reduce_workspace_bytes(int T, int H) {
+  if (T <= 0 || H <= 0 || H % 8 != 0) return 0;
+  return ep::combine_reduce_workspace_bytes(T, H);
+}
+
+int ep_combine_reduce(const void* y, int64_t recv_rows, int H, const int32_t* src_token, const int32_t* dest_row,
+                      const float* topk_w, int T, int k, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = check_common(T, k, H, "ep_combine_reduce");
+  if (rc) return rc;
+  rc = check_rows(H, recv_rows, "ep_combine_reduce");
+  if (rc) return rc;
+  if (T > 0 && (!dest_row || !topk_w || !out || (recv_rows > 0 && (!y || !src_token))))
+    return fail(EP_ERR_INVALID_ARG, "ep_combine_reduce: null y/src_token/dest_row/topk_w/out");
+  if ((y && !aligned(y, 16)) || (out && !aligned(out, 16)))
+    return fail(EP_ERR_ALIGNMENT, "ep_combine_reduce: bf16 tensor not 16-byte aligned");
+  if ((src_token && !aligned(src_token, 4)) || (dest_row && !aligned(dest_row, 4)) ||
+      (topk_w && !aligned(topk_w, 4)))
+    return fail(EP_ERR_ALIGNMENT, "ep_combine_reduce: src_token/dest_row/topk_w not 4-byte aligned");
+  if (T == 0) return EP_OK;
+  const size_t need = ep::combine_reduce_workspace_bytes(T, H);
+  if (!workspace || workspace_bytes < need)
+    return fail(EP_ERR_WORKSPACE, "ep_combine_reduce: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(EP_ERR_ALIGNMENT, "ep_combine_reduce: workspace not 16-byte aligned");
+  ep::Budget b;
+  rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_combine_reduce(b, y, recv_rows, H, src_token, dest_row, topk_w, T, k, out, workspace,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_combine_reduce launch");
+  return EP_OK;
+}
+
 const char* ep_status_string(int code) {
   switch (code) {
     case EP_OK: return "ok";

@@ -46,6 +46,12 @@ hipError_t launch_layout_dispatch(const Budget& b, const int32_t* idx, int T, in
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream);
 
+// ---- reduce-on-store combine (combine_reduce.hip)
+size_t combine_reduce_workspace_bytes(int T, int H);
+hipError_t launch_combine_reduce(const Budget& b, const void* y, int64_t recv_rows, int H, const int32_t* src_token,
+                                 const int32_t* dest_row, const float* w, int T, int k, void* out, void* acc,
+                                 hipStream_t stream);
+
 // ---- probes (probe.hip)
 hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes,
                            hipStream_t stream);

@@ -206,6 +206,40 @@ int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void
 int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row, const float* topk_w,
                int T, int k, void* out, void* stream);
 
+/*
+ * ep_combine_reduce -- the same combine computed from the expert side by
+ * reduce-on-store: the bulk store that adds element-wise into its global
+ * destination, described in "TMA study notes" (mkbk-pku.cn, cited as
+ * [TMA-notes]), section "TMA 的其他特性（单卡 / Cluster 内）", item 3.  gfx950 has no
+ * such store, so the addition is an fp32 atomic per element:
+ *   acc[t, :] = 0;  for r < recv_rows with t = src_token[r] in [0, T) and a
+ *   slot j with dest_row[t*k+j] == r:  acc[t, :] += w[t, j] * f32(y[r, :]);
+ *   out[t, :] = bf16_rne(acc[t, :])
+ * y is read once, as one sequential stream in receive-row order; each
+ * accumulator element takes k atomic additions.  The order of those
+ * additions is not fixed, so the result is the fp32 sum of the k products
+ * in SOME order (each product rounded separately, never fused), rounded
+ * once to bf16: within fp32 rounding of ep_combine's result, but not always
+ * bit-identical to it and not bit-reproducible from call to call.  Rows
+ * whose src_token is outside [0, T), or whose token does not list them in
+ * dest_row (entries of src_token beyond offsets[E] that ep_layout left
+ * unwritten), add nothing.
+ *   y          bf16 [recv_rows, H] expert outputs in the ep_layout order
+ *   src_token  int32 [recv_rows] from ep_layout
+ *   dest_row   int32 [T, k] from ep_layout
+ *   topk_w     float32 [T, k]
+ *   out        bf16 [T, H]
+ *   workspace  device scratch of at least ep_combine_reduce_workspace_bytes
+ *              (T, H) = 4*T*H bytes (the fp32 accumulator), 16-byte
+ *              aligned, owned by the caller, clobbered by the call
+ * Three launches on `stream` (zero, scatter-add, convert).  Limits as
+ * ep_combine; a missing or short workspace returns EP_ERR_WORKSPACE.
+ */
+size_t ep_combine_reduce_workspace_bytes(int T, int H);
+int ep_combine_reduce(const void* y, int64_t recv_rows, int H, const int32_t* src_token, const int32_t* dest_row,
+                      const float* topk_w, int T, int k, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Static text for a return code. */
 const char* ep_status_string(int code);
 /* Detail of the calling thread's last negative return ("" if none). */

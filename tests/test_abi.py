@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -161,6 +161,50 @@ def combine(lib, y=A16, rows=32, H=1024, dest=A4, w=A4, T=16, k=2, out=A16):
 )
 def test_combine_rejects(lib, kw, code):
     assert combine(lib, **kw) == code
+
+
+def combine_reduce(lib, y=A16, rows=32, H=1024, src=A4, dest=A4, w=A4, T=16, k=2, out=A16, ws=A16,
+                   wsb=16 * 1024 * 4):
+    return lib.ep_combine_reduce(y, rows, H, src, dest, w, T, k, out, ws, wsb, None)
+
+
+def test_combine_reduce_workspace_bytes(lib):
+    # the fp32 accumulator [T, H]
+    assert lib.ep_combine_reduce_workspace_bytes(4096, 7168) == 4096 * 7168 * 4
+    assert lib.ep_combine_reduce_workspace_bytes(1, 8) == 32
+    assert lib.ep_combine_reduce_workspace_bytes(0, 1024) == 0
+    assert lib.ep_combine_reduce_workspace_bytes(16, 12) == 0
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(H=12), ep.EP_ERR_INVALID_ARG),
+        (dict(k=0), ep.EP_ERR_INVALID_ARG),
+        (dict(k=33), ep.EP_ERR_INVALID_ARG),
+        (dict(rows=-5), ep.EP_ERR_INVALID_ARG),
+        (dict(y=None), ep.EP_ERR_INVALID_ARG),
+        (dict(src=None), ep.EP_ERR_INVALID_ARG),
+        (dict(dest=None), ep.EP_ERR_INVALID_ARG),
+        (dict(w=None), ep.EP_ERR_INVALID_ARG),
+        (dict(out=None), ep.EP_ERR_INVALID_ARG),
+        (dict(out=A16 + 4), ep.EP_ERR_ALIGNMENT),
+        (dict(y=A16 + 2), ep.EP_ERR_ALIGNMENT),
+        (dict(src=ODD), ep.EP_ERR_ALIGNMENT),
+        (dict(w=ODD), ep.EP_ERR_ALIGNMENT),
+        (dict(ws=None), ep.EP_ERR_WORKSPACE),
+        (dict(wsb=16 * 1024 * 4 - 1), ep.EP_ERR_WORKSPACE),
+        (dict(ws=A4), ep.EP_ERR_ALIGNMENT),
+    ],
+)
+def test_combine_reduce_rejects(lib, kw, code):
+    assert combine_reduce(lib, **kw) == code
+    assert lib.ep_last_error().decode() != ""
+
+
+def test_combine_reduce_empty_batch_is_a_host_no_op(lib):
+    assert combine_reduce(lib, T=0, y=None, src=None, dest=None, w=None, out=None, ws=None) == 0
 
 
 def test_layout_dispatch_rejects(lib):

@@ -121,24 +121,6 @@ def run_dispatch(wl, dest_row_np, recv_rows, fill=0x7E57):
     return from_dev_bf16(recv)
 
 
-# The phased dispatch's unit shapes (as for the phased combine), including a
-# duplicated destination row (-1: dropped) and several units per wave.
-@pytest.mark.parametrize("H", [8, 2048, 4104, 7168, 8712, 16384])
-@pytest.mark.parametrize("T", [1, 29, 300])
-@pytest.mark.parametrize("budget", [0, 1, 24])
-def test_dispatch_phase_units(H, T, budget):
-    ep.ep_set_variant("phase")
-    ep.ep_set_num_cus(budget)
-    k = 8 if H % 3 else 6
-    wl = make_workload("prefill", seed=H + T, T=T, H=H, E=32, k=k)
-    lay = oracle.layout(wl.topk_idx, 32)
-    dest = lay["dest_row"].copy()
-    dest[T // 2, k - 1] = -1  # a slot whose row is never written
-    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
-    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
-    np.testing.assert_array_equal(got, want)
-
-
 @pytest.mark.parametrize("name", DISPATCH_CONFIGS)
 def test_dispatch_full_size(name):
     wl = workload(name)
