@@ -224,6 +224,166 @@ __global__ __launch_bounds__(1024) void dispatch_lds2_kernel(EP_DISPATCH_ARGS) {
   }
 }
 
+// Three stages per wave: the fills of the next two units are in flight while
+// the current one is read out and stored.  A deeper ring costs LDS, so fewer
+// waves fit a CU (3 x 7 KiB per wave at H = 7168: 7 waves).  The wait for a
+// stage's fill lets the operations issued after it stay outstanding, up to
+// vmcnt's limit of 63 (past it the wait also retires the oldest stores,
+// which is still correct).  The ring is unrolled by three so that every stage
+// index is a compile-time constant and the per-stage state stays in
+// registers.
+template <int VPL, int K>
+struct Ring3 {
+  Unit un[3];
+  Dests<K> ds[3];
+  int after[3];  // vector-memory operations issued since the pending fill of each stage
+};
+
+template <int S, int VPL, int K, bool EVEN, bool NT>
+__device__ __forceinline__ bool lds3_step(Ring3<VPL, K>& r, int& u, char* ring, const u32x4* __restrict__ x,
+                                          u32x4* __restrict__ recv, const int32_t* __restrict__ dest_row,
+                                          int64_t recv_rows, int row_vec, int nslab, int units, int stride,
+                                          int lane) {
+  constexpr int kStage = VPL * kWaveVecBytes;
+  // steady state after a stage's fill: the stores of the two units before it
+  // and the fill of the unit after it
+  constexpr int kSteady = 2 * K * VPL + VPL;
+  constexpr int kCap = kSteady < 63 ? kSteady : 63;
+  constexpr int S1 = (S + 1) % 3, S2 = (S + 2) % 3;
+  if (r.after[S] >= kCap) wait_vmcnt<kCap>();
+  else wait_vmcnt<0>();
+  u32x4 v[VPL];
+  read_slab<VPL>(v, ring + S * kStage, lane);  // stage S is free again
+  const int u2 = u + 2 * stride;
+  const bool fill = u2 < units;
+  if (fill) {
+    r.un[S2] = unit_of<VPL>(u2, nslab, row_vec, lane);
+    fetch_dests<K>(r.ds[S2], dest_row + r.un[S2].t * K);
+    dma_slab<VPL, EVEN>(x + r.un[S2].t * row_vec, ring + S2 * kStage, r.un[S2], row_vec);
+    r.after[S1] += r.un[S2].nvec;  // the next stage's fill is older than this one
+    r.after[S2] = 0;
+  }
+  const int st = store_slab<VPL, K, EVEN, NT>(v, recv, r.ds[S], nullptr, K, recv_rows, r.un[S], row_vec);
+  r.after[S1] += st;
+  if (fill) r.after[S2] += st;
+  u += stride;
+  return u < units;
+}
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_lds3_kernel(EP_DISPATCH_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  static_assert(K > 0, "the three-stage ring needs a compile-time k for its wait counts");
+  constexpr int kStage = VPL * kWaveVecBytes;
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  char* ring = lds + wave * (3 * kStage);
+  int u = blockIdx.x * wpg + wave;
+  if (u >= units) return;
+  Ring3<VPL, K> r;
+  r.after[0] = r.after[1] = r.after[2] = 0;
+  r.un[0] = unit_of<VPL>(u, nslab, row_vec, lane);
+  fetch_dests<K>(r.ds[0], dest_row + r.un[0].t * K);
+  dma_slab<VPL, EVEN>(x + r.un[0].t * row_vec, ring, r.un[0], row_vec);
+  if (u + stride < units) {
+    r.un[1] = unit_of<VPL>(u + stride, nslab, row_vec, lane);
+    fetch_dests<K>(r.ds[1], dest_row + r.un[1].t * K);
+    dma_slab<VPL, EVEN>(x + r.un[1].t * row_vec, ring + kStage, r.un[1], row_vec);
+    r.after[0] = r.un[1].nvec;
+  }
+  for (;;) {
+    if (!lds3_step<0, VPL, K, EVEN, NT>(r, u, ring, x, recv, dest_row, recv_rows, row_vec, nslab, units, stride,
+                                        lane))
+      break;
+    if (!lds3_step<1, VPL, K, EVEN, NT>(r, u, ring, x, recv, dest_row, recv_rows, row_vec, nslab, units, stride,
+                                        lane))
+      break;
+    if (!lds3_step<2, VPL, K, EVEN, NT>(r, u, ring, x, recv, dest_row, recv_rows, row_vec, nslab, units, stride,
+                                        lane))
+      break;
+  }
+}
+
+// Producer/consumer specialisation: wave 0 of each workgroup only issues the
+// direct-to-LDS fills for the W consumer waves (the "elected" issuer of
+// [DeepEP-TMA] "Asynchronous Copy Primitives", made a whole wave because a
+// wave instruction is the unit of issue here); consumers only read their
+// slab out and store it k times.  Two slots of W slabs: the producer fills
+// slot (i + 1) & 1 while the consumers store round i.  Synchronisation is two
+// workgroup barriers per round and no polling: barrier A follows the
+// producer's wait for the round's fill, barrier B the consumers' reads of the
+// slot.  Every fill issues exactly W x VPL loads (units past the end re-read
+// unit 0, lanes past a ragged row end its last vector), so the producer's
+// wait for the older fill is exact.
+template <int VPL>
+constexpr int pc_consumers() {
+  return 63 / VPL < 8 ? 63 / VPL : 8;
+}
+
+inline int pc_consumers_host(int vpl) { return 63 / vpl < 8 ? 63 / vpl : 8; }
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_pc_kernel(EP_DISPATCH_ARGS) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int W = pc_consumers<VPL>();
+  constexpr int kSlot = W * VPL * kWaveVecBytes;
+  const int k = K > 0 ? K : k_rt;
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int G = gridDim.x;
+  const int per_round = G * W;
+  const int rounds = (units + per_round - 1) / per_round;
+  if (wave == 0) {
+    // producer
+    auto fill = [&](int i) {
+      char* slot = lds + (i & 1) * kSlot;
+#pragma unroll
+      for (int c = 0; c < W; ++c) {
+        const int uc = (i * G + (int)blockIdx.x) * W + c;
+        const Unit un = unit_of<VPL>(uc < units ? uc : 0, nslab, row_vec, lane);
+        const u32x4* src = x + un.t * row_vec;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          int col = un.c0 + v * kWave;
+          if (col >= row_vec) col = row_vec - 1;
+          dma16(src + col, (lds_void_t*)(slot + (c * VPL + v) * kWaveVecBytes));
+        }
+      }
+    };
+    if (rounds > 0) fill(0);
+    for (int i = 0; i < rounds; ++i) {
+      if (i + 1 < rounds) {
+        fill(i + 1);
+        wait_vmcnt<W * VPL>();  // fill i done; fill i + 1 stays in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      wg_barrier();  // A: slot i & 1 is full
+      wg_barrier();  // B: the consumers have read it
+    }
+    return;
+  }
+  // consumer c
+  const int c = wave - 1;
+  for (int i = 0; i < rounds; ++i) {
+    const int u = (i * G + (int)blockIdx.x) * W + c;
+    const bool ok = u < units;
+    const Unit un = unit_of<VPL>(ok ? u : 0, nslab, row_vec, lane);
+    const int32_t* dr = dest_row + un.t * k;
+    Dests<K> ds;
+    fetch_dests<K>(ds, dr);
+    wg_barrier();  // A
+    u32x4 v[VPL];
+    read_slab<VPL>(v, lds + (i & 1) * kSlot + c * VPL * kWaveVecBytes, lane);
+    wg_barrier();  // B
+    if (ok) store_slab<VPL, K, EVEN, NT>(v, recv, ds, dr, k, recv_rows, un, row_vec);
+  }
+}
+
 using DispatchFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, int, int, int);
 
 template <int VPL, int K, bool EVEN>
@@ -232,13 +392,17 @@ DispatchFn pick_kind(Variant v) {
     case Variant::Vgpr: return dispatch_vgpr_kernel<VPL, K, EVEN, true>;
     case Variant::VgprCached: return dispatch_vgpr_kernel<VPL, K, EVEN, false>;
     case Variant::Lds1: return dispatch_lds1_kernel<VPL, K, EVEN, true>;
+    case Variant::Pc: return dispatch_pc_kernel<VPL, K, EVEN, true>;
     default: break;
   }
-  // the double-buffered kernels hold two slabs: compiled up to 8 vectors per lane
+  // the double-buffered kernels hold two slabs (the three-stage one three):
+  // compiled up to 8 vectors per lane
   if constexpr (VPL <= 8) {
     if (v == Variant::Vgpr2) return dispatch_vgpr2_kernel<VPL, K, EVEN, true>;
-    if constexpr (K > 0)
+    if constexpr (K > 0) {
       if (v == Variant::Lds2) return dispatch_lds2_kernel<VPL, K, EVEN, true>;
+      if (v == Variant::Lds3) return dispatch_lds3_kernel<VPL, K, EVEN, true>;
+    }
   }
   return nullptr;
 }
@@ -247,6 +411,7 @@ template <int VPL, bool EVEN>
 DispatchFn pick_k(Variant v, int k) {
   switch (k) {
     case 2: return pick_kind<VPL, 2, EVEN>(v);
+    case 4: return pick_kind<VPL, 4, EVEN>(v);
     case 6: return pick_kind<VPL, 6, EVEN>(v);
     case 8: return pick_kind<VPL, 8, EVEN>(v);
     default: return pick_kind<VPL, 0, EVEN>(v);
@@ -447,14 +612,16 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // direct-to-LDS staging measured fastest at every compute-unit budget
   if (v == Variant::Auto) v = Variant::Lds1;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
-  if ((v == Variant::Lds2 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
+  if ((v == Variant::Lds2 || v == Variant::Lds3 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
   // default slabs of at most 8 KiB (half rows at H = 7168); whole 14 KiB
   // rows per wave measured no faster.  A requested size may go to 16 for the
-  // single-set kernels; the double-buffered ones hold two slabs, so 8.
-  const int cap = (v == Variant::Vgpr2 || v == Variant::Lds2 || b.slab_vpl == 0) ? 8 : 16;
+  // single-set kernels; the double-buffered ones hold two slabs (the
+  // three-stage one three), so 8.
+  const bool multi = v == Variant::Vgpr2 || v == Variant::Lds2 || v == Variant::Lds3;
+  const int cap = (multi || b.slab_vpl == 0) ? 8 : 16;
   const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
@@ -462,8 +629,9 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   DispatchFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
   if (!fn) return hipErrorInvalidValue;
 
-  const bool lds = (v == Variant::Lds1 || v == Variant::Lds2);
-  const size_t per_wave = lds ? (size_t)(v == Variant::Lds2 ? 2 : 1) * vpl * kWaveVecBytes : 0;
+  const bool lds = (v == Variant::Lds1 || v == Variant::Lds2 || v == Variant::Lds3);
+  const int stages = v == Variant::Lds3 ? 3 : v == Variant::Lds2 ? 2 : 1;
+  const size_t per_wave = lds ? (size_t)stages * vpl * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds_bytes;
   // With no budget set, a large dispatch still runs as a persistent grid on
@@ -473,7 +641,16 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // start-up is cheaper.
   int budget = b.num_cus;
   if (budget == 0 && units >= kWriteCus * 16 * 2) budget = kWriteCus;
-  if (budget > 0) {
+  if (v == Variant::Pc) {
+    // one producer and W consumer waves per workgroup, a two-slot ring of W
+    // slabs each; always a persistent grid (one workgroup per CU)
+    const int W = pc_consumers_host(vpl);
+    wpg = W + 1;
+    const int want = (units + W - 1) / W;
+    grid = budget > 0 ? (budget < b.device_cus ? budget : b.device_cus) : (want < b.device_cus ? want : b.device_cus);
+    lds_bytes = (size_t)2 * W * vpl * kWaveVecBytes;
+    if (lds_bytes < kExclusiveLds) lds_bytes = kExclusiveLds;
+  } else if (budget > 0) {
     // persistent: one workgroup per CU, as many waves as the LDS ring allows
     wpg = 16;
     if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
@@ -484,7 +661,10 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
     wpg = 4;
     int per_cu = per_wave ? (int)(kLdsPerCu / (per_wave * wpg)) : 8;
     if (per_cu > 8) per_cu = 8;
-    if (per_cu < 1) per_cu = 1;
+    if (per_cu < 1) {
+      per_cu = 1;
+      wpg = (int)(kLdsPerCu / per_wave);
+    }
     grid = (units + wpg - 1) / wpg;
     if (grid > b.device_cus * per_cu) grid = b.device_cus * per_cu;
     lds_bytes = per_wave * wpg;

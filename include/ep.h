@@ -95,7 +95,17 @@ int ep_get_num_cus(void);
  *           KiB of output rows in registers and stores them only after all
  *           their source rows are read: with one such unit per wave the
  *           whole grid reads first and writes last.  k must be 2, 4, 6 or 8,
- *           else the any-k register kernel runs.
+ *           else the any-k register kernel runs;
+ *   "lds3"  (dispatch; combine takes its default) three stages per wave:
+ *           the next two units' direct-to-LDS loads are in flight while the
+ *           current one is stored (fewer waves fit a CU);
+ *   "pc"    (dispatch; combine takes its default) producer/consumer: one
+ *           wave per workgroup issues every direct-to-LDS load into a
+ *           two-slot ring and 3 to 8 consumer waves store the slabs, in
+ *           step through workgroup barriers (the elected issuer of
+ *           [DeepEP-TMA] "Asynchronous Copy Primitives" as a whole wave);
+ *           always a persistent grid of one workgroup per CU.
+ * lds2, lds3 and phase need k in {2, 4, 6, 8}; for other k dispatch runs lds1.
  * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
  */
 int ep_set_variant(const char* name);

@@ -129,7 +129,7 @@ def test_dispatch_full_size(name):
     np.testing.assert_array_equal(got, oracle_recv(name))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached", "phase"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "vgpr_cached", "phase"])
 @pytest.mark.parametrize("budget", BUDGETS)
 def test_dispatch_variants_train(variant, budget):
     ep.ep_set_variant(variant)
@@ -139,9 +139,9 @@ def test_dispatch_variants_train(variant, budget):
     np.testing.assert_array_equal(got, oracle_recv("train"))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "phase"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "phase"])
 @pytest.mark.parametrize("H", [8, 520, 1024, 4104, 7168, 7176, 8712, 16384])
-@pytest.mark.parametrize("k", [2, 3, 6])
+@pytest.mark.parametrize("k", [2, 3, 4, 6])
 @pytest.mark.parametrize("budget", [0, 24])
 def test_dispatch_ragged_rows(variant, H, k, budget):
     ep.ep_set_variant(variant)
@@ -153,7 +153,7 @@ def test_dispatch_ragged_rows(variant, H, k, budget):
     np.testing.assert_array_equal(got, oracle.dispatch(wl.x, lay["dest_row"], T * k))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc"])
 @pytest.mark.parametrize("slab", [1, 2, 4, 7, 8, 14, 16])
 @pytest.mark.parametrize("budget", [0, 24])
 def test_dispatch_slab_sizes(variant, slab, budget):
@@ -333,6 +333,15 @@ def test_combine_slab_sizes(variant, slab, budget):
             assert_combine_close(got, oracle.combine(wr.y, lay["dest_row"], wr.topk_w))
     finally:
         ep.ep_set_slab(0)
+
+
+@pytest.mark.parametrize("variant", ["lds3", "pc"])
+def test_combine_under_dispatch_only_variants(variant):
+    # these name dispatch kernels only; combine runs its default
+    ep.ep_set_variant(variant)
+    wl = workload("train")
+    got = run_combine(wl, expert_outputs("train"), oracle_layout("train")["dest_row"])
+    assert_combine_close(got, oracle_out("train"))
 
 
 def test_combine_unnormalised_weights_and_signed_zero():
