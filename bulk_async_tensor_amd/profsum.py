@@ -23,6 +23,7 @@ KINDS = {
     "layout": ("layout_",),
     "dispatch": ("dispatch_",),
     "combine": ("combine_",),
+    "combine_reduce": ("reduce_zero", "reduce_scatter", "reduce_convert"),
     "copy_probe": ("bw_kernel<0",),
 }
 
