@@ -268,9 +268,11 @@ def read_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(name, seconds):
+def cpu_baseline(name, seconds, gpu=None):
     """The oracle as it stands, on the host, over the whole workload, repeated
-    until about `seconds` of CPU work; reported in the metric's unit."""
+    until about `seconds` of CPU work; reported in the metric's unit.  With
+    `gpu` (the Setup whose step was timed), the oracle's outputs of the last
+    pass are also compared with the GPU's outputs of the same inputs."""
     import oracle
     from synth import algorithmic_bytes, make_workload
 
@@ -295,13 +297,14 @@ def cpu_baseline(name, seconds):
         else:
             y = recv
         t2 = time.perf_counter()
-        oracle.combine(y, lay["dest_row"], wl.topk_w)
+        out = oracle.combine(y, lay["dest_row"], wl.topk_w)
         t3 = time.perf_counter()
         t_total += (t1 - t0) + (t3 - t2)
         passes += 1
         if time.perf_counter() - t_start >= seconds:
             break
     per_step = t_total / passes
+    parity = None if gpu is None else parity_against(gpu, lay, recv if c.ops != "combine" else None, out)
     b = algorithmic_bytes(c.T, c.H, c.k, c.E)
     step_bytes = b["layout"] + b["combine"] + (b["dispatch"] if c.ops != "combine" else 0)
     return {
@@ -313,7 +316,34 @@ def cpu_baseline(name, seconds):
         "kind": "oracle",
         "sample": f"whole {name} workload (T={c.T}), {passes} pass(es) of layout+dispatch+combine, "
                   f"single-threaded numpy/Python",
+        "parity_of_timed_gpu_outputs": parity,
     }
+
+
+def parity_against(s, lay, recv, out):
+    """The GPU outputs of the timed step (layout, dispatch, combine on the
+    workload's inputs) against the oracle's: bit-exact flags for layout and
+    dispatch; for combine the bit-identical fraction and the gate
+    abs(g - r) <= 1e-2 abs(r) + 1e-3."""
+    import numpy as np
+
+    import oracle
+
+    res = {}
+    n = int(lay["offsets"][-1])
+    got = {k: getattr(s, k).cpu().numpy().reshape(-1) for k in ("counts", "offsets", "dest_row", "src_token")}
+    res["layout_bit_exact"] = bool(
+        np.array_equal(got["counts"], lay["counts"]) and np.array_equal(got["offsets"], lay["offsets"])
+        and np.array_equal(got["dest_row"], lay["dest_row"].reshape(-1))
+        and np.array_equal(got["src_token"][:n], lay["src_token"][:n]))
+    if recv is not None:
+        g = s.recv.contiguous().view(s.torch.int16).cpu().numpy().view(np.uint16)
+        res["dispatch_bit_exact"] = bool(np.array_equal(g, recv))
+    go = oracle.bf16_to_f32(s.out.contiguous().view(s.torch.int16).cpu().numpy().view(np.uint16))
+    ro = oracle.bf16_to_f32(out)
+    res["combine_bit_identical_frac"] = round(float(np.mean(go == ro)), 6)
+    res["combine_within_gate"] = bool(np.all(np.abs(go.astype(np.float64) - ro) <= 1e-2 * np.abs(ro) + 1e-3))
+    return res
 
 
 def parse_budget(tok):
@@ -702,7 +732,7 @@ def main():
                                 "value": round(s.step_bytes / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
                                 "tokens_per_s": round(s.T / (ms_g * 1e-3), 1)}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, gpu=s)
     print(json.dumps(line), flush=True)
 
 

@@ -4,7 +4,7 @@
 // back.  Entries of one expert are placed in row-major (token, slot) order;
 // no atomic operation decides a row, so the result is deterministic.
 //
-// Fused path (one launch; used while the per-chunk histogram fits in LDS):
+// One-launch path (a few 1024-entry chunks, or up to 64 when E > 64):
 // workgroup c owns entries [1024 c, 1024 c + 1024), one 64-entry step per
 // wave.  Every workgroup reads all T*k ids (a few hundred KiB at most) and
 // builds the full (chunk, expert) histogram in LDS, so it knows each
@@ -15,10 +15,15 @@
 // sizes (written to LDS by the highest lane of each group) give each wave
 // the rows taken by the steps before it.
 //
-// Large path (three launches): count (LDS histogram per chunk of tokens),
-// scan (one workgroup: totals, offsets and the base row of every (chunk,
-// expert)), place (one wave per chunk walking its entries 64 at a time,
-// advancing per-expert cursors in LDS).
+// Two-launch path (larger batches, or few experts): count (an LDS histogram per chunk
+// of 1024 / k tokens, equal experts of a step aggregated into one atomic),
+// then scan and rank in one launch, each workgroup summing the small
+// (chunk, expert) table instead of all ids.
+//
+// Three-launch path (tables too large to read per workgroup): count, scan
+// (one workgroup: totals, offsets and the base row of every (chunk, expert)),
+// place (one wave per chunk walking its entries 64 at a time, advancing
+// per-expert cursors in LDS).
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -34,7 +39,7 @@ constexpr int kStatusOutOfRange = 1;
 constexpr int kStatusDuplicate = 2;
 
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(const int32_t* __restrict__ idx, int T,
-                                                                     int k, int E, int chunk_tokens,
+                                                                     int k, int E, int nbits, int chunk_tokens,
                                                                      int32_t* __restrict__ chunk_counts,
                                                                      int32_t* __restrict__ chunk_status) {
   extern __shared__ int32_t lds[];
@@ -50,14 +55,34 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(const int32
 
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   if (threadIdx.x == 0) s_status = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ent[i] = src[i];
+  // a chunk holds at most kChunkEntries = 4 x kCountThreads ids: every load
+  // is issued before the first LDS store waits on one
+  static_assert(kChunkEntries == 4 * kCountThreads, "four ids per thread");
+  int v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + q * kCountThreads;
+    v[q] = i < n ? src[i] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + q * kCountThreads;
+    if (i < n) ent[i] = v[q];
+  }
   __syncthreads();
 
+  // Lanes of one step that hold the same expert add their count with one
+  // atomic (the highest lane of the group): with a few hot experts the
+  // atomics of a step would otherwise serialise on one address.
   int bad = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int e = ent[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
-    else bad |= kStatusOutOfRange;
+  const int lane = lane_id();
+  for (int i0 = threadIdx.x - lane; i0 < n; i0 += blockDim.x) {  // uniform per wave
+    const int i = i0 + lane;
+    const int e = i < n ? ent[i] : -1;
+    const bool ok = (unsigned)e < (unsigned)E;
+    if (i < n && !ok) bad |= kStatusOutOfRange;
+    const uint64_t m = same_value_lanes(ok, e, nbits);
+    if (ok && (m >> lane) == 1ull) atomicAdd(&hist[e], __builtin_popcountll(m));
   }
   // repeated expert inside one token: thread per token, pairwise
   for (int tt = threadIdx.x; tt < nt; tt += blockDim.x) {
@@ -203,6 +228,114 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
   }
 }
 
+// Second launch of the two-launch path: scan and rank in one kernel, one
+// workgroup of 1024 threads per chunk of the count kernel (chunk_tokens
+// tokens, at most 1024 entries; thread j takes entry j of the chunk).  Each
+// workgroup reads the whole (chunk, expert) table written by the count
+// kernel -- nchunks x E counts, instead of the T*k ids that the one-launch
+// path histograms -- and sums it in G = 1024 / Epad groups of Epad lanes
+// (lane e an expert, group g a range of chunks): the totals give the
+// offsets, the chunks before its own the start of each expert's rows in this
+// chunk.  Ranks inside the chunk as in the one-launch path.
+__global__ __launch_bounds__(1024) void layout_rank_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                           int nbits, int epad, int chunk_tokens, int nchunks,
+                                                           const int32_t* __restrict__ chunk_counts,
+                                                           const int32_t* __restrict__ chunk_status,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ dest_row,
+                                                           int32_t* __restrict__ src_token,
+                                                           int32_t* __restrict__ status) {
+  constexpr int kWaves = 1024 / kWave;
+  extern __shared__ int32_t lds[];
+  const int G = 1024 / epad;
+  int32_t* part_tot = lds;                  // [G][epad]
+  int32_t* part_pre = part_tot + G * epad;  // [G][epad]
+  int32_t* stepc = part_pre + G * epad;     // [16][E] group sizes per 64-entry step of this chunk
+  int32_t* base = stepc + kWaves * E;       // [E] first row of each expert for this chunk
+  __shared__ int32_t s_wave[kWaves + 1];
+  __shared__ int32_t s_status;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int t0 = c * chunk_tokens;
+  const int nt = min(chunk_tokens, T - t0);
+  const int n = nt * k;
+  const int64_t i = (int64_t)t0 * k + tid;
+  const bool in_range = tid < n;
+  const int my_e = in_range ? idx[i] : -1;
+  if (tid == 0) s_status = 0;
+
+  int st = 0;
+  for (int cc = tid; cc < nchunks; cc += 1024) st |= chunk_status[cc];
+  const int g = tid / epad;
+  const int e = tid - g * epad;
+  const int cpg = (nchunks + G - 1) / G;
+  const int c0 = min(nchunks, g * cpg);
+  const int c1 = min(nchunks, c0 + cpg);
+  // up to 8 counts per trip, all loads issued before the first is used
+  int sum = 0, before = 0;
+  if (e < E) {
+    for (int cb = c0; cb < c1; cb += 8) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = cb + q < c1 ? chunk_counts[(int64_t)(cb + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        sum += v[q];
+        before += cb + q < c ? v[q] : 0;
+      }
+    }
+  }
+  part_tot[g * epad + e] = sum;
+  part_pre[g * epad + e] = before;
+  __syncthreads();
+  if (st) atomicOr(&s_status, st);
+
+  // expert totals and the part before this chunk; thread e of group 0 holds expert e
+  int tot = 0, pre = 0;
+  if (g == 0 && e < E) {
+    for (int g2 = 0; g2 < G; ++g2) {
+      tot += part_tot[g2 * epad + e];
+      pre += part_pre[g2 * epad + e];
+    }
+  }
+  int all = 0;
+  const int excl = block_excl_scan<kWaves>(tot, s_wave, &all);  // threads past E add 0
+  if (g == 0 && e < E) base[e] = excl + pre;
+  for (int x = tid; x < kWaves * E; x += 1024) stepc[x] = 0;
+  __syncthreads();
+  if (c == 0) {
+    if (g == 0 && e < E) {
+      counts[e] = tot;
+      offsets[e] = excl;
+    }
+    if (tid == 0) {
+      offsets[E] = all;
+      if (status) status[0] = s_status;
+    }
+  }
+
+  // ranks inside this wave's 64-entry step
+  const bool ok = in_range && (unsigned)my_e < (unsigned)E;
+  const uint64_t m = same_value_lanes(ok, my_e, nbits);
+  const int rank = mask_rank(m);
+  if (ok && (m >> lane) == 1ull) stepc[wave * E + my_e] = __builtin_popcountll(m);
+  __syncthreads();
+  if (in_range) {
+    int r = -1;
+    if (ok) {
+      r = base[my_e] + rank;
+      for (int w = 0; w < wave; ++w) r += stepc[w * E + my_e];
+      if (src_token) src_token[r] = t0 + tid / k;
+    }
+    dest_row[i] = r;
+  }
+}
+
+size_t rank_lds_bytes(int E, int epad) { return (size_t)(2 * 1024 + 16 * E + E) * sizeof(int32_t); }
+
 constexpr int kFusedChunk = 1024;   // entries per workgroup: 16 waves x 64
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
@@ -344,10 +477,37 @@ size_t fused_lds_bytes(int T, int k, int E) {
   return (size_t)(nchunks + kFusedWaves + 1) * E * sizeof(int32_t);
 }
 
-bool use_fused(int T, int k, int E) {
+// Path choice, from measurements on MI355X (one launch costs at least about
+// 4.5 us here, whatever it does):
+//  - the one-launch path, whose every workgroup histograms all T*k ids with
+//    LDS atomics, costs 4.6 us at 1 chunk, 8.6 us at 32 and 12.9 us at 64
+//    chunks of 1024 entries with E = 256, but 21.9 us at 96 chunks with
+//    E = 64 and skewed routing, where the atomics of a 64-lane step collide
+//    on a few addresses (with E <= 64 some always do);
+//  - the two-launch path costs 10.4 to 12.4 us over the same range.
+// So: one launch up to a few chunks, and up to 64 chunks when E > 64.
+#ifndef EP_LAYOUT_FUSED_MAX_CHUNKS
+#define EP_LAYOUT_FUSED_MAX_CHUNKS 64
+#endif
+constexpr int64_t kFusedFewChunks = 4;
+constexpr int kFusedMinExperts = 65;  // one launch past a few chunks only above this many experts
+// The two-launch path reads the whole (chunk, expert) table in every
+// workgroup; past this many counts the three-launch path scans it once.
+constexpr int64_t kRankTableMax = 64 * 1024;
+
+enum class Path { Fused, Two, Three };
+
+Path layout_path(int T, int k, int E) {
+  if (T <= 0) return Path::Fused;
   const int64_t N = (int64_t)T * k;
-  const int64_t nchunks = (N + kFusedChunk - 1) / kFusedChunk;
-  return nchunks <= 128 && fused_lds_bytes(T, k, E) <= 144 * 1024;
+  const int64_t nf = (N + kFusedChunk - 1) / kFusedChunk;
+  const bool fits = fused_lds_bytes(T, k, E) <= 144 * 1024;
+  if (fits && (nf <= kFusedFewChunks || (E >= kFusedMinExperts && nf <= EP_LAYOUT_FUSED_MAX_CHUNKS)))
+    return Path::Fused;
+  const int64_t ct = kChunkEntries / k;
+  const int64_t nch = (T + ct - 1) / ct;
+  if (nch * E <= kRankTableMax) return Path::Two;
+  return Path::Three;
 }
 
 }  // namespace
@@ -360,7 +520,7 @@ int layout_num_chunks(int T, int k) {
 }
 
 size_t layout_workspace_bytes(int T, int k, int E) {
-  if (T <= 0 || use_fused(T, k, E)) return 0;
+  if (T <= 0 || layout_path(T, k, E) == Path::Fused) return 0;
   const size_t nch = (size_t)layout_num_chunks(T, k);
   size_t counts = nch * (size_t)E * sizeof(int32_t);
   counts = (counts + 255) & ~(size_t)255;
@@ -374,7 +534,8 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
   while (epad < E) epad <<= 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  if (T == 0 || use_fused(T, k, E)) {
+  const Path path = layout_path(T, k, E);
+  if (path == Path::Fused) {
     const int N = T * k;
     const int nchunks = (N + kFusedChunk - 1) / kFusedChunk;
     const size_t lds = fused_lds_bytes(T, k, E);
@@ -388,19 +549,28 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
     return hipGetLastError();
   }
   const int ct = layout_chunk_tokens(k);
-  const int nch = T > 0 ? layout_num_chunks(T, k) : 0;
+  const int nch = layout_num_chunks(T, k);  // T > 0 here
 
   int32_t* chunk_counts = static_cast<int32_t*>(workspace);
-  int32_t* chunk_status = nullptr;
-  if (nch > 0) {
-    size_t cb = (size_t)nch * E * sizeof(int32_t);
-    cb = (cb + 255) & ~(size_t)255;
-    chunk_status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cb);
+  size_t cb = (size_t)nch * E * sizeof(int32_t);
+  cb = (cb + 255) & ~(size_t)255;
+  int32_t* chunk_status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cb);
+  {
     const size_t lds = (size_t)(E + ct * k) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(nch), dim3(kCountThreads), lds, stream, idx, T, k, E, ct,
+    hipLaunchKernelGGL(layout_count_kernel, dim3(nch), dim3(kCountThreads), lds, stream, idx, T, k, E, nbits, ct,
                        chunk_counts, chunk_status);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+  }
+  if (path == Path::Two) {
+    const size_t lds = rank_lds_bytes(E, epad);
+    if (lds > 64 * 1024) {
+      hipError_t e = allow_dynamic_lds((const void*)layout_rank_kernel, lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(nch), dim3(1024), lds, stream, idx, T, k, E, nbits, epad, ct, nch,
+                       chunk_counts, chunk_status, counts, offsets, dest_row, src_token, status);
+    return hipGetLastError();
   }
   {
     const int G = kScanThreads / epad;
@@ -410,7 +580,7 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (nch > 0) {
+  {
     const size_t lds = (size_t)E * sizeof(int32_t);
     hipLaunchKernelGGL(layout_place_kernel, dim3(nch), dim3(kWave), lds, stream, idx, T, k, E, nbits, ct,
                        chunk_counts, dest_row, src_token);

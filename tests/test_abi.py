@@ -69,10 +69,20 @@ def test_slab_setting(lib):
 
 
 def test_workspace_bytes(lib):
-    # shapes whose (chunk, expert) histogram fits in LDS use the one-launch path: no workspace
+    # the one-launch path needs no workspace: a few 1024-entry chunks, or up to 64 chunks with E > 64
+    assert lib.ep_layout_workspace_bytes(128, 8, 256) == 0
+    assert lib.ep_layout_workspace_bytes(128, 2, 8) == 0
     assert lib.ep_layout_workspace_bytes(4096, 8, 256) == 0
-    assert lib.ep_layout_workspace_bytes(16384, 6, 64) == 0
-    # larger ones: chunks of 1024 // k tokens; counts per (chunk, expert), 256-aligned, + one status per chunk
+    assert lib.ep_layout_workspace_bytes(8192, 8, 256) == 0
+    assert lib.ep_layout_workspace_bytes(512, 8, 64) == 0
+    # the two-launch path counts per chunk of 1024 // k tokens into a (chunk, expert) table,
+    # 256-aligned, followed by one status word per chunk.  E <= 64 past four chunks:
+    # 16384 x 6 -> 97 chunks of 170 tokens; 97 * 64 * 4 = 24,832 is already 256-aligned
+    assert lib.ep_layout_workspace_bytes(16384, 6, 64) == 97 * 64 * 4 + 97 * 4
+    # 513 x 8 = 4104 entries with E = 64: five chunks of 128 tokens
+    assert lib.ep_layout_workspace_bytes(513, 8, 64) == 5 * 64 * 4 + 5 * 4
+    # more than 64 chunks: 8193 x 8 -> 65 chunks of 128 tokens
+    assert lib.ep_layout_workspace_bytes(8193, 8, 256) == 65 * 256 * 4 + 65 * 4
     # T=131072, k=8 -> 1024 chunks; 1024*256*4 = 1 MiB
     assert lib.ep_layout_workspace_bytes(131072, 8, 256) == 1024 * 256 * 4 + 1024 * 4
     # T=40000, k=32, E=1024 -> 32 tokens per chunk -> 1250 chunks; 1250*1024*4 = 5,120,000 (256-aligned)
@@ -102,8 +112,10 @@ def layout(lib, idx=A4, T=16, k=2, E=8, counts=A4, offsets=A4, dest=A4, src=A4, 
         (dict(dest=ODD), ep.EP_ERR_ALIGNMENT),
         (dict(idx=ODD), ep.EP_ERR_ALIGNMENT),
         (dict(status=A4 + 2), ep.EP_ERR_ALIGNMENT),
-        # shapes on the three-launch path need a workspace
+        # shapes beyond the one-launch path need a workspace
         (dict(T=131072, k=8, E=256, ws=None), ep.EP_ERR_WORKSPACE),
+        (dict(T=16384, k=6, E=64, ws=None), ep.EP_ERR_WORKSPACE),
+        (dict(T=16384, k=6, E=64, wsb=97 * 64 * 4), ep.EP_ERR_WORKSPACE),
         (dict(T=131072, k=8, E=256, wsb=16), ep.EP_ERR_WORKSPACE),
         (dict(T=131072, k=8, E=256, ws=A4, wsb=1 << 24), ep.EP_ERR_ALIGNMENT),
     ],
