@@ -9,6 +9,8 @@
 
 #include <atomic>
 #include <mutex>
+#include <map>
+#include <utility>
 
 #include "ep.h"
 #include "ep_internal.hpp"
@@ -100,8 +102,22 @@ int check_rows(int H, int64_t recv_rows, const char* what) {
 
 namespace ep {
 
+// Raises a kernel's dynamic-LDS limit on the current device when a launch
+// needs more than was set before; launches within the limit already set only
+// look it up.  (The limit cannot simply be set to a CU's whole LDS: a kernel's
+// static LDS counts against it.)
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> limit;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = limit.find({dev, kernel});
+  if (it != limit.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) limit[{dev, kernel}] = bytes;
+  return e;
 }
 
 }  // namespace ep

@@ -417,7 +417,8 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
   if (bad) atomicOr(&s_status, bad);
   __syncthreads();
 
-  // expert totals, the part before this chunk, and the offsets
+  // expert totals, the part before this chunk, and the offsets (a plain loop
+  // per expert measured faster than spreading the sums over all threads)
   int tot = 0, pre = 0;
   if (tid < E) {
     for (int cc = 0; cc < nchunks; ++cc) {
