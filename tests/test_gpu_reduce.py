@@ -189,3 +189,41 @@ def test_reduce_unnormalised_weights_and_signed_zero():
     got = run_reduce(recv, lay["src_token"], lay["dest_row"], w, 16, 1024)
     assert_combine_close(got, oracle.combine(recv, lay["dest_row"], w), exact=False)
     assert_within_sum_bound(got, recv, lay["dest_row"], w)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill"])
+def test_reduce_graph_replay(name):
+    """The reduce-on-store combine captured in a HIP graph (its accumulator is
+    cleared by a fill kernel, not a memset node): every replay, with the
+    accumulator and the output clobbered eagerly in between, gives the exact
+    identity round trip."""
+    wl = workload(name)
+    c = wl.config
+    lay = oracle_layout(name)
+    y = to_dev_bf16(expert_outputs(name))
+    src = to_dev(lay["src_token"])
+    dest = to_dev(lay["dest_row"])
+    w = to_dev(wl.topk_w)
+    out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ep.ep_combine_reduce_workspace_bytes(c.T, c.H), dtype=torch.uint8, device=DEV)
+
+    def call():
+        ep.ep_combine_reduce(y, src, dest, w, out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    want = oracle.bf16_to_f32(wl.x)
+    for rep in range(4):
+        out.view(torch.int16).fill_(rep)
+        ws.view(torch.float32).fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(oracle.bf16_to_f32(from_dev_bf16(out)), want), f"replay {rep}"
