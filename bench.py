@@ -639,8 +639,8 @@ def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is a single-GPU kernel library with no collectives)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(a single-GPU kernel library with no collectives)", file=sys.stderr)
         sys.exit(2)
     import torch
 
