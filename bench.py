@@ -53,7 +53,9 @@ def parse_args():
     p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
     p.add_argument("--fused", action="store_true", help="layout and dispatch through ep_layout_dispatch")
     p.add_argument("--overlap", default=None,
-                   help="CU-partitioned overlap with a bf16 GEMM, JSONL to this file (budgets from --sweep-budgets)")
+                   help="CU-partitioned overlap with computation, JSONL to this file (budgets from --sweep-budgets)")
+    p.add_argument("--overlap-compute", default="gemm", choices=["gemm", "mfma"],
+                   help="the computation beside the copies: a torch bf16 GEMM or the matrix-core probe")
     p.add_argument("--kernels-only", action="store_true",
                    help="a few launches of each kernel and of a 256 MiB copy probe (for counter passes)")
     p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
@@ -545,22 +547,40 @@ def kernels_only(s, launches=5, copy_bytes=256 << 20):
                       "bytes": s.bytes}), flush=True)
 
 
-def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
-    """Row movement on a stream masked to n CUs beside a bf16 GEMM on a stream
+def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None, compute="gemm", mfma_iters=16384):
+    """Row movement on a stream masked to n CUs beside computation on a stream
     masked to the other CUs (the pages' premise: the copy kernels leave the
     remaining units to computation).  Each side alone and concurrently; also
-    both concurrently without a partition."""
+    both concurrently without a partition.  compute = "gemm": a bf16 GEMM
+    through torch (hipBLASLt, whose grid is sized for the whole device);
+    "mfma": ep_mfma_probe, a matrix-core loop sized to its share of CUs,
+    whose throughput follows the CUs it gets."""
     import torch
 
     import bulk_async_tensor_amd as ep
 
     s = Setup(name)
     dev = torch.device("cuda:0")
-    A = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
-    B = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
-    C = torch.empty((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
     n_all = torch.cuda.get_device_properties(0).multi_processor_count
-    flop = 2.0 * gemm_n ** 3
+    if compute == "mfma":
+        A = B = C = None
+        sink = torch.empty(256 * 8 * n_all, dtype=torch.float32, device=dev)
+    else:
+        A = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+        B = torch.randn((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+        C = torch.empty((gemm_n, gemm_n), device=dev, dtype=torch.bfloat16)
+    share = {"cus": n_all}  # CUs the computation is sized for
+
+    # the matrix-core probe runs 8 short workgroups per CU of its share, so
+    # that the dispatcher can even out a partition whose shader engines hold
+    # unequal numbers of CUs (with two long workgroups per CU the most loaded
+    # CU set the time: 1.5x on 240 of 256 CUs)
+    groups_per_cu, iters_per_group = 8, max(1, mfma_iters // 4)
+
+    def flop_per_call():
+        if compute == "mfma":
+            return 2.0 * share["cus"] * groups_per_cu * 4 * iters_per_group * 4 * 16384
+        return 2.0 * gemm_n ** 3
 
     def timed(jobs):
         """jobs: list of (stream, fn, reps); all start together; returns ms per stream."""
@@ -581,7 +601,10 @@ def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
         return [e0.elapsed_time(e1) for e0, e1 in evs]
 
     def gemm(st):
-        torch.matmul(A, B, out=C)
+        if compute == "mfma":
+            ep.ep_mfma_probe(groups_per_cu * share["cus"], iters_per_group, sink, stream=st)
+        else:
+            torch.matmul(A, B, out=C)
 
     def step(st):
         s.stream = st
@@ -598,8 +621,9 @@ def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
     reps_g = gemm_reps or max(4, int(round(steps * s_full / g_full)))
     recs = []
     with open(path, "a") as fh:
-        base = {"kind": "overlap_base", "workload": name, "gemm_n": gemm_n, "gemm_ms_all_cus": g_full,
-                "gemm_TFLOPs_all_cus": flop / g_full / 1e9, "step_ms_all_cus": s_full}
+        base = {"kind": "overlap_base", "workload": name, "compute": compute,
+                "gemm_n": gemm_n if compute == "gemm" else None, "gemm_ms_all_cus": g_full,
+                "gemm_TFLOPs_all_cus": flop_per_call() / g_full / 1e9, "step_ms_all_cus": s_full}
         fh.write(json.dumps(base) + "\n")
         print(json.dumps(base), flush=True)
         # no partition: both on ordinary streams at once
@@ -612,6 +636,7 @@ def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
         for n in comm_cus_list:
             comm = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n)))
             comp = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n, n_all)))
+            share["cus"] = n_all - n
             for _ in range(2):
                 step(comm)
                 with torch.cuda.stream(comp):
@@ -626,13 +651,15 @@ def overlap(path, name, comm_cus_list, steps, gemm_n=8192, gemm_reps=None):
                    "gemm_slowdown_vs_all_cus": (t_g / reps_g) / g_full,
                    "step_slowdown_vs_alone_on_n": (t_s / steps) / s_alone,
                    "step_GBs_concurrent": s.step_bytes / (t_s / steps) / 1e6,
-                   "gemm_TFLOPs_concurrent": flop / (t_g / reps_g) / 1e9}
+                   "gemm_TFLOPs_alone_on_rest": flop_per_call() / g_alone / 1e9,
+                   "gemm_TFLOPs_concurrent": flop_per_call() / (t_g / reps_g) / 1e9}
             fh.write(json.dumps(rec) + "\n")
             print(json.dumps(rec), flush=True)
             torch.cuda.synchronize()
             s.stream = None
             ep.ep_stream_destroy(comm)
             ep.ep_stream_destroy(comp)
+            share["cus"] = n_all
     s.stream = None
 
 
@@ -655,7 +682,8 @@ def main():
         probe_sweep(args.probe_sweep, [int(b) for b in budgets])
         return
     if args.overlap:
-        overlap(args.overlap, args.workload, [int(b) for b in budgets], max(20, args.steps // 4))
+        overlap(args.overlap, args.workload, [int(b) for b in budgets], max(20, args.steps // 4),
+                compute=args.overlap_compute)
         return
     if args.sweep:
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),

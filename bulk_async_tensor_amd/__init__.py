@@ -52,6 +52,7 @@ _SIGNATURES = {
     "ep_last_error": (ctypes.c_char_p, []),
     "ep_bw_probe": (_c_int, [_c_int, _p, _p, _c_i64, _p]),
     "ep_probe_placement": (_c_int, [_p, _c_int, _p]),
+    "ep_mfma_probe": (_c_int, [_c_int, _c_int, _p, _p]),
     "ep_stream_create_cu_masked": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, ctypes.POINTER(_p)]),
     "ep_stream_destroy": (_c_int, [_p]),
 }
@@ -323,6 +324,17 @@ def ep_probe_placement(out, n_groups, stream=None):
     if out.numel() < 4 * n_groups:
         raise ValueError("out must hold 4 * n_groups int32")
     return _check(lib().ep_probe_placement(_ptr(out), int(n_groups), _stream(stream)), "ep_probe_placement")
+
+
+def ep_mfma_probe(n_groups, iters, out, stream=None):
+    """Compute-bound matrix-core loop: n_groups workgroups of 4 waves, iters
+    rounds of 4 x 16384 flop per wave; out: float32 tensor of 256 * n_groups."""
+    import torch
+
+    _device_tensor(out, "out", torch.float32)
+    if out.numel() < 256 * int(n_groups):
+        raise ValueError("out must hold 256 * n_groups floats")
+    return _check(lib().ep_mfma_probe(int(n_groups), int(iters), _ptr(out), _stream(stream)), "ep_mfma_probe")
 
 
 # ------------------------------------------------------------------ CU-masked streams

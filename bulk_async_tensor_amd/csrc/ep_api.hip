@@ -401,6 +401,18 @@ int ep_probe_placement(int32_t* out, int n_groups, void* stream) {
   return launched;
 }
 
+int ep_mfma_probe(int n_groups, int iters, float* out, void* stream) {
+  if (!out || n_groups < 1 || n_groups > 65536 || iters < 0)
+    return fail(EP_ERR_INVALID_ARG, "ep_mfma_probe: bad output, n_groups or iters");
+  if (!aligned(out, 4)) return fail(EP_ERR_ALIGNMENT, "ep_mfma_probe: alignment");
+  ep::Budget b;
+  int rc = current_device(&b);
+  if (rc) return rc;
+  hipError_t e = ep::launch_mfma_probe(n_groups, iters, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_mfma_probe launch");
+  return EP_OK;
+}
+
 int ep_stream_create_cu_masked(const uint32_t* mask, int mask_words, void** stream) {
   if (!mask || !stream) return fail(EP_ERR_INVALID_ARG, "ep_stream_create_cu_masked: null pointer");
   if (mask_words < 1 || mask_words > 64)

@@ -56,6 +56,7 @@ hipError_t launch_combine_reduce(const Budget& b, const void* y, int64_t recv_ro
 hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes,
                            hipStream_t stream);
 hipError_t launch_placement(const Budget& b, int n_groups, int32_t* out, hipStream_t stream, int* launched);
+hipError_t launch_mfma_probe(int n_groups, int iters, float* out, hipStream_t stream);
 
 // Raise the dynamic-LDS limit of a kernel once (needed above 64 KiB).
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);

@@ -365,3 +365,45 @@ hipError_t launch_placement(const Budget& b, int n_groups, int32_t* out, hipStre
 }
 
 }  // namespace ep
+
+namespace ep {
+
+namespace {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// A compute-bound stand-in for the expert GEMM beside the copy kernels: each
+// wave runs `iters` rounds of four independent 32x32x8 bf16 matrix-core
+// products on register operands (no memory traffic).  The sum of the
+// accumulators is compared with a value it never takes, so the work stays
+// live without a store; out is written only in that impossible case.
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ out) {
+  const int lane = lane_id();
+  bf16x4_t a, b;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    a[q] = (short)(0x3F80 + ((lane + q) & 7));  // small positive bf16 values
+    b[q] = (short)(0x3F80 + ((lane * 3 + q) & 7));
+  }
+  f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s += c0[q] + c1[q] + c2[q] + c3[q];
+  if (s == -1.0f) out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(int n_groups, int iters, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(n_groups), dim3(256), 0, stream, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace ep

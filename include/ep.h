@@ -306,6 +306,20 @@ int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* strea
 int ep_probe_placement(int32_t* out, int n_groups, void* stream);
 
 /*
+ * ep_mfma_probe: a compute-bound kernel to run beside the copy kernels (the
+ * computation that [DeepEP-TMA] "Minimal SM Occupancy Configuration" keeps
+ * the remaining units free for).  n_groups workgroups of 4 waves; each wave
+ * runs `iters` rounds of four 32x32x8 bf16 matrix-core products on register
+ * operands, 4 x 16384 flop per round, with no memory traffic, so its
+ * throughput follows the compute units it gets.  out is device memory of
+ * 256 * n_groups floats that is written only if the products sum to an
+ * impossible value (it keeps the work live).  Returns EP_OK,
+ * EP_ERR_INVALID_ARG (null out, n_groups outside [1, 65536], iters < 0),
+ * EP_ERR_ALIGNMENT or EP_ERR_HIP.
+ */
+int ep_mfma_probe(int n_groups, int iters, float* out, void* stream);
+
+/*
  * CU-masked streams, for running the copy kernels on a chosen set of compute
  * units beside other work ([DeepEP-TMA] "Minimal SM Occupancy
  * Configuration": the communication kernels keep to a few units so that the

@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -268,6 +268,10 @@ def test_probe_rejects(lib):
     assert lib.ep_bw_probe(0, A16, A16, 0, None) == 0
     assert lib.ep_probe_placement(None, 4, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_probe_placement(A4, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_mfma_probe(4, 10, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_mfma_probe(0, 10, A4, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_mfma_probe(4, -1, A4, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_mfma_probe(4, 10, ODD, None) == ep.EP_ERR_ALIGNMENT
 
 
 def test_masked_stream_rejects(lib):

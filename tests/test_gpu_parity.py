@@ -436,6 +436,13 @@ def test_persistent_grid_gets_distinct_cus(budget):
     assert per_xcc.max() - per_xcc.min() <= 1
 
 
+def test_mfma_probe_runs_and_keeps_out_untouched():
+    out = torch.full((256 * 8,), 7.0, dtype=torch.float32, device=DEV)
+    ep.ep_mfma_probe(8, 100, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
 def test_cu_masked_stream_confines_work():
     n = 24
     stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n)))
