@@ -404,6 +404,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 ep.ep_set_num_cus(budget)
             s.stream = stream
             st = stream if stream is not None else torch.cuda.current_stream()
+            ceiling = {}  # probe GB/s at this budget, by probe name
             # operation 7 once per wave: 128 KiB read by each of 16 waves on every CU of the grid
             once = min(n, (budget if budget > 0 else ndev) * 16 * (128 << 10))
             for mode, label, nb in ([(0, "copy", n), (1, "read", n), (2, "write", n), (0x20 | 2, "write32", n),
@@ -424,6 +425,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                 moved = 2 * nb if mode == 0 else (nb + nb // 8) if mode in (4, 5, 6, 7, 0x17, 0x27) else nb
                 rec = {"kind": "probe", "mode": label, "num_cus": str(tok), "ms": ms, "GBs": moved / ms / 1e6,
                        "bytes": nb}
+                ceiling[label] = rec["GBs"]
                 fh.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), flush=True)
             for v in variants:
@@ -433,9 +435,15 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                     ep.ep_set_variant({"rows": "auto", "rows_nt": "vgpr_cached"}.get(v, v))
                     ep.ep_set_slab(slab)
                     ms, per = s.run(steps, warmup)
-                    rec = {"kind": "step", "workload": name, "variant": v, "slab": slab, "num_cus": str(tok),
-                           "ms_per_step": ms, "kernel_ms": per,
-                           "GBs": {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}}
+                    gbs = {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}
+                    # the probe whose read/write mix matches each kernel, measured at this budget
+                    ref = {"dispatch": ceiling.get("mix1to8"), "combine": ceiling.get("mix8to1_phase_once")}
+                    rec = {"kind": "step", "workload": name, "seed": s.wl.seed, "variant": v, "slab": slab,
+                           "num_cus": str(tok), "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3),
+                           "kernel_ms": per, "kernel_timing": getattr(s, "kernel_timing", None), "GBs": gbs,
+                           "frac_of_hbm_peak": {k: (g / HBM_PEAK_GBS if g else None) for k, g in gbs.items()},
+                           "frac_of_probe": {k: (gbs[k] / ref[k] if gbs.get(k) and ref.get(k) else None)
+                                             for k in ("dispatch", "combine")}}
                     fh.write(json.dumps(rec) + "\n")
                     print(json.dumps(rec), flush=True)
             ep.ep_set_slab(0)
