@@ -436,14 +436,18 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                     ep.ep_set_slab(slab)
                     ms, per = s.run(steps, warmup)
                     gbs = {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}
-                    # the probe whose read/write mix matches each kernel, measured at this budget
-                    ref = {"dispatch": ceiling.get("mix1to8"), "combine": ceiling.get("mix8to1_phase_once")}
+                    # streaming ceilings at this budget: dispatch (8/9 writes) against the
+                    # better write probe, combine against the probe with its phased 8:1 mix
+                    writes = [ceiling[m] for m in ("write", "write32") if m in ceiling]
+                    ref = {"dispatch": max(writes) if writes else None,
+                           "combine": ceiling.get("mix8to1_phase_once")}
                     rec = {"kind": "step", "workload": name, "seed": s.wl.seed, "variant": v, "slab": slab,
                            "num_cus": str(tok), "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3),
                            "kernel_ms": per, "kernel_timing": getattr(s, "kernel_timing", None), "GBs": gbs,
                            "frac_of_hbm_peak": {k: (g / HBM_PEAK_GBS if g else None) for k, g in gbs.items()},
                            "frac_of_probe": {k: (gbs[k] / ref[k] if gbs.get(k) and ref.get(k) else None)
-                                             for k in ("dispatch", "combine")}}
+                                             for k in ("dispatch", "combine")},
+                           "probe_ref": {"dispatch": "max(write, write32)", "combine": "mix8to1_phase_once"}}
                     fh.write(json.dumps(rec) + "\n")
                     print(json.dumps(rec), flush=True)
             ep.ep_set_slab(0)
