@@ -92,7 +92,25 @@ def build(verbose=False, jobs=None):
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_c_abi_test()
     return LIB
+
+
+C_TEST_SRC = os.path.join(ROOT, "tests", "c_abi_roundtrip.c")
+C_TEST_BIN = os.path.join(BUILD, "c_abi_roundtrip")
+
+
+def build_c_abi_test():
+    """The C program that calls the library from C (tests/c_abi_roundtrip.c),
+    compiled with gcc against the HIP runtime API and linked to libep.so."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(rocm, 'include')}",
+           f"-I{INCLUDE}", C_TEST_SRC, "-o", C_TEST_BIN, f"-L{PKG}", "-lep", f"-L{os.path.join(rocm, 'lib')}",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_TEST_SRC}:\n{res.stdout}\n{res.stderr}")
+    return C_TEST_BIN
 
 
 if __name__ == "__main__":
