@@ -189,7 +189,7 @@ class Setup:
         ms = (time.perf_counter() - t0) * 1e3 / steps
         per = {}
         for name, fn in (("layout", self.layout), ("dispatch", self.dispatch), ("combine", self.combine)):
-            if name == "dispatch" and not self.do_dispatch:
+            if name == "dispatch" and (not self.do_dispatch or self.fused):
                 per[name] = 0.0
                 continue
             per[name] = self.kernel_ms(fn, steps)
@@ -332,6 +332,18 @@ def cpu_baseline(name, seconds, gpu=None):
             break
     per_step = t_total / passes
     parity = None if gpu is None else parity_against(gpu, lay, recv if c.ops != "combine" else None, out)
+    parity_fused = None
+    if gpu is not None and c.ops != "combine":
+        # layout and dispatch once more through the one-launch entry point, on
+        # outputs overwritten with sentinels first
+        for t in (gpu.counts, gpu.offsets, gpu.dest_row, gpu.src_token):
+            t.fill_(-7)
+        gpu.recv.view(gpu.torch.int16).fill_(0x7E57)
+        gpu.fused = True
+        gpu.layout()
+        gpu.fused = False
+        gpu.torch.cuda.synchronize()
+        parity_fused = {k: v for k, v in parity_against(gpu, lay, recv, out).items() if not k.startswith("combine")}
     b = algorithmic_bytes(c.T, c.H, c.k, c.E)
     step_bytes = b["layout"] + b["combine"] + (b["dispatch"] if c.ops != "combine" else 0)
     return {
@@ -344,6 +356,7 @@ def cpu_baseline(name, seconds, gpu=None):
         "sample": f"whole {name} workload (T={c.T}), {passes} pass(es) of layout+dispatch+combine, "
                   f"single-threaded numpy/Python",
         "parity_of_timed_gpu_outputs": parity,
+        "parity_of_one_launch_layout_dispatch": parity_fused,
     }
 
 
@@ -716,6 +729,12 @@ def main():
         ms, per = s.run(args.steps, args.warmup)
         results[label] = (ms, per)
     ep.ep_set_num_cus(0)
+    fused = None
+    if s.do_dispatch and not args.fused:
+        # the same step with layout and dispatch in one launch (ep_layout_dispatch)
+        s.fused = True
+        fused = s.run(args.steps, args.warmup)
+        s.fused = False
     cold = cold_times(s, args.cold) if args.cold > 0 else None
     if args.cold_study:
         for mode in ("none", "write", "read", "write_read"):
@@ -777,6 +796,14 @@ def main():
             "kernel_ms": {k: round(v, 5) for k, v in results["mask"][1].items()},
             "kernel_GBs": {k: round(s.bytes[k] / (v * 1e6), 1) for k, v in results["mask"][1].items()
                            if v > 0 and s.bytes[k]},
+        },
+        "fused_step": None if fused is None else {
+            "step": "layout_dispatch+combine",
+            "value": round(s.step_bytes / (fused[0] * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(fused[0], 5),
+            "tokens_per_s": round(s.T / (fused[0] * 1e-3), 1),
+            "kernel_ms": {"layout_dispatch": round(fused[1]["layout"], 5), "combine": round(fused[1]["combine"], 5)},
         },
         "roofline": {
             "kernel": kname,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libep.so")
-SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "combine_reduce.hip", "decode.hip", "probe.hip"]
+SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "combine_reduce.hip", "layout_dispatch.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

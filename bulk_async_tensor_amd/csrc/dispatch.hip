@@ -134,32 +134,6 @@ __global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) 
   }
 }
 
-// Direct-to-LDS fill of one slab: instruction i moves vector i of every lane
-// into slice + i KiB.  Every instruction with i < nvec is issued.
-template <int VPL, bool EVEN>
-__device__ __forceinline__ void dma_slab(const u32x4* __restrict__ src, char* slice, const Unit& un, int row_vec) {
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i < un.nvec) {
-      const int c = un.c0 + i * kWave;
-      if (EVEN || c < row_vec) dma16(src + c, (lds_void_t*)(slice + i * kWaveVecBytes));
-    }
-  }
-}
-
-// Reads the whole slice (vectors past the slab hold stale bytes of this wave's
-// own slice and are never stored): unconditional reads keep the register
-// allocation simple.
-template <int VPL>
-__device__ __forceinline__ void read_slab(u32x4 (&v)[VPL], const char* slice, int lane) {
-  const uint32_t base = lds_addr_of(slice) + lane * kVecBytes;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) lds_read16_async(v[i], base + i * kWaveVecBytes);
-  lds_wait_all();
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) lds_fence_value(v[i]);
-}
-
 template <int VPL, int K, bool EVEN, bool NT>
 __global__ __launch_bounds__(1024) void dispatch_lds1_kernel(EP_DISPATCH_ARGS) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -431,7 +405,6 @@ DispatchFn pick_vpl(Variant v, int vpl, int k) {
 }
 
 constexpr int kSlabChoices[] = {2, 4, 7, 8, 14, 16};
-constexpr int kWriteCus = 64;
 
 // Vectors per lane per slab.  Default: the whole row when it is at most
 // `cap` vectors per lane (rows then leave a wave as one contiguous burst per
@@ -606,6 +579,8 @@ hipError_t launch_dispatch_phase(const Budget& b, const void* x, int T, int row_
 }
 
 }  // namespace
+
+int dispatch_slab_vpl(int row_vec, int cap, int requested) { return choose_vpl(row_vec, cap, requested); }
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {

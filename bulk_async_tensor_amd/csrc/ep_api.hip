@@ -261,17 +261,9 @@ int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void*
   ep::Budget b;
   rc = current_device(&b);
   if (rc) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (T > 0 && ep::layout_dispatch_fits(T, k, E)) {
-    e = ep::launch_layout_dispatch(b, topk_idx, T, k, E, x, H, counts, offsets, dest_row, src_token, status, recv,
-                                   recv_rows, s);
-  } else {
-    e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace, s);
-    if (e == hipSuccess && T > 0 && recv_rows > 0)
-      e = ep::launch_dispatch(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, dest_row, k, recv, recv_rows,
-                              s);
-  }
+  hipError_t e = ep::launch_layout_dispatch(static_cast<ep::Variant>(g_variant.load()), b, topk_idx, T, k, E, x, H,
+                                            counts, offsets, dest_row, src_token, status, workspace, recv, recv_rows,
+                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ep_layout_dispatch launch");
   return EP_OK;
 }

@@ -21,6 +21,11 @@ struct Budget {
 constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr size_t kExclusiveLds = 80 * 1024 + 1024;
 
+// A large dispatch runs as a persistent grid on this many CUs when no budget
+// is set: its traffic is 8/9 writes, and HBM write throughput was measured
+// highest with about a quarter of the CUs issuing them.
+constexpr int kWriteCus = 64;
+
 // ---- layout (layout.hip)
 int layout_chunk_tokens(int k);
 int layout_num_chunks(int T, int k);
@@ -36,11 +41,17 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
 hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* src_token,
                                 void* recv, int64_t recv_rows, hipStream_t stream);
 
-// ---- fused layout + dispatch for small batches (decode.hip)
-bool layout_dispatch_fits(int T, int k, int E);
-hipError_t launch_layout_dispatch(const Budget& b, const int32_t* idx, int T, int k, int E, const void* x, int H,
-                                  int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* src_token,
-                                  int32_t* status, void* recv, int64_t recv_rows, hipStream_t stream);
+// Vectors per lane of the default dispatch slab for a row of row_vec 16-byte
+// vectors, at most `cap` (a requested size is rounded down to a compiled one).
+int dispatch_slab_vpl(int row_vec, int cap, int requested);
+
+// ---- fused layout + dispatch (layout_dispatch.hip)
+// One launch for small batches and, with the lds1-style copy, for wide ones;
+// otherwise launch_layout then launch_dispatch (workspace as for the layout).
+hipError_t launch_layout_dispatch(Variant v, const Budget& b, const int32_t* idx, int T, int k, int E, const void* x,
+                                  int H, int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* src_token,
+                                  int32_t* status, void* workspace, void* recv, int64_t recv_rows,
+                                  hipStream_t stream);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,

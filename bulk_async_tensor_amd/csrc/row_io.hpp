@@ -70,6 +70,32 @@ __device__ __forceinline__ void store_one(const u32x4 (&v)[VPL], u32x4* __restri
   }
 }
 
+// Direct-to-LDS fill of one slab: instruction i moves vector i of every lane
+// into slice + i KiB.  Every instruction with i < nvec is issued.
+template <int VPL, bool EVEN>
+__device__ __forceinline__ void dma_slab(const u32x4* __restrict__ src, char* slice, const Unit& un, int row_vec) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (i < un.nvec) {
+      const int c = un.c0 + i * kWave;
+      if (EVEN || c < row_vec) dma16(src + c, (lds_void_t*)(slice + i * kWaveVecBytes));
+    }
+  }
+}
+
+// Reads the whole slice (vectors past the slab hold stale bytes of this wave's
+// own slice and are never stored): unconditional reads keep the register
+// allocation simple.
+template <int VPL>
+__device__ __forceinline__ void read_slab(u32x4 (&v)[VPL], const char* slice, int lane) {
+  const uint32_t base = lds_addr_of(slice) + lane * kVecBytes;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) lds_read16_async(v[i], base + i * kWaveVecBytes);
+  lds_wait_all();
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) lds_fence_value(v[i]);
+}
+
 // ---- phased units: a wave holds up to kPhaseHeld vectors per lane (16 KiB)
 // of rows in registers between reading and writing them.  A unit is tpu
 // whole rows when a row has at most kPhaseHeld vectors per lane (nseg == 1),

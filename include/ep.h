@@ -171,12 +171,19 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
 
 /*
  * ep_layout_dispatch -- ep_layout followed by ep_dispatch, with identical
- * outputs, in one launch when the batch is small (T*k <= 1024 entries): the
- * low-latency decode shape, where launches rather than bytes set the time
- * (the low-latency kernel family of [DeepEP-TMA], "TMA Implementation
- * Across Kernel Types").  Larger batches run the two calls in order.
+ * outputs, in one launch where that is faster (the low-latency kernel
+ * family of [DeepEP-TMA], "TMA Implementation Across Kernel Types", and its
+ * use for wide batches):
+ *   - T*k <= 1024 entries (the decode shape, where launches rather than
+ *     bytes set the time);
+ *   - up to 64 Ki entries with k in {2, 4, 6, 8} and 65 <= E <= 256, while
+ *     the dispatch variant is "auto" or "lds1": a persistent grid on the
+ *     dispatch's compute units in which every workgroup histograms all ids
+ *     and then ranks and copies its own range of tokens.
+ * Other batches run ep_layout and ep_dispatch in order on the stream.
  * Arguments as for ep_layout and ep_dispatch (x bf16 [T, H], recv bf16
- * [recv_rows, H]); the workspace is needed only when ep_layout needs one.
+ * [recv_rows, H]); the workspace must be given whenever ep_layout needs one
+ * for these sizes (ep_layout_workspace_bytes), whichever path runs.
  */
 int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void* x, int H, int32_t* counts,
                        int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,

@@ -558,3 +558,103 @@ def test_layout_dispatch_flags_bad_ids():
     check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, 100, 4)
     want = oracle.dispatch(x, ref["dest_row"], 400, recv=np.full((400, 64), 0x7E57, dtype=np.uint16))
     np.testing.assert_array_equal(from_dev_bf16(recv), want)
+
+
+# ------------------------------------------------- fused layout + dispatch, wide batches
+# Past 1024 entries, with k in {2, 4, 6, 8}, 65 <= E <= 256 and at most 64 Ki
+# entries, ep_layout_dispatch runs as one persistent launch in which every
+# workgroup histograms all ids and then ranks and copies its own token
+# range.  These cases put T off the grid size, rows off the slab size, E at
+# both ends of the range, the entry count at its limit, and several ranking
+# rounds in one workgroup (the 24-CU budget at the training shape: 171
+# tokens x 8 = 1368 entries per workgroup).  The last cases fall outside the
+# wide path (k = 1 or 3, E = 1 or 64 or 300, past 64 Ki entries) and take the
+# two separate launches.
+WIDE_CASES = [
+    ("train", {}),
+    ("train", dict(T=129)),
+    ("train", dict(T=5000, H=7176)),
+    ("train", dict(T=777, H=1032, E=65, k=2)),
+    ("train", dict(T=4096, k=6)),
+    ("train", dict(T=3000, H=512, E=256, k=4)),
+    ("train", dict(T=8192)),
+    ("prefill", dict(T=3001, H=4096, E=100, k=2)),
+    ("train", dict(T=8193)),
+    ("prefill", dict(T=6000, E=64, k=6)),
+    ("prefill", dict(T=2048, H=2056, E=1, k=1)),
+    ("prefill", dict(T=2000, H=1024, E=64, k=3)),
+    ("train", dict(T=400, H=1024, E=300, k=8)),
+]
+
+
+def run_layout_dispatch(wl):
+    c = wl.config
+    ref = oracle.layout(wl.topk_idx, c.E)
+    R = c.T * c.k
+    recv = torch.full((R, c.H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay = ep.ep_layout_dispatch(to_dev(wl.topk_idx), c.E, to_dev_bf16(wl.x), recv)
+    torch.cuda.synchronize()
+    check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+    np.testing.assert_array_equal(from_dev_bf16(recv), oracle.dispatch(wl.x, ref["dest_row"], R))
+
+
+@pytest.mark.parametrize("name,over", WIDE_CASES)
+@pytest.mark.parametrize("budget", [0, 24, 256])
+def test_layout_dispatch_wide(name, over, budget):
+    ep.ep_set_num_cus(budget)
+    run_layout_dispatch(make_workload(name, seed=8, **over))
+
+
+def test_layout_dispatch_wide_prefill_full_size():
+    run_layout_dispatch(workload("prefill"))
+
+
+@pytest.mark.parametrize("slab", [2, 4, 8])
+def test_layout_dispatch_wide_slabs(slab):
+    ep.ep_set_slab(slab)
+    try:
+        run_layout_dispatch(make_workload("train", seed=9, T=1500))
+    finally:
+        ep.ep_set_slab(0)
+
+
+@pytest.mark.parametrize("variant", ["vgpr", "lds2", "lds1"])
+def test_layout_dispatch_wide_under_variants(variant):
+    ep.ep_set_variant(variant)
+    run_layout_dispatch(make_workload("train", seed=10, T=1200))
+
+
+@pytest.mark.parametrize("E,k", [(96, 4), (256, 8)])
+def test_layout_dispatch_wide_flags_bad_ids(E, k):
+    rng = np.random.default_rng(12)
+    T, H = 2000, 1024
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32)
+    idx[3, 1] = E + 5
+    idx[1500, 0] = -1
+    idx[999, 2] = idx[999, 0]
+    x = rng.integers(0, 2**16, size=(T, H), dtype=np.uint32).astype(np.uint16)
+    ref = oracle.layout(idx, E)
+    assert ref["status"] == 3
+    R = T * k
+    recv = torch.full((R, H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay = ep.ep_layout_dispatch(to_dev(idx), E, to_dev_bf16(x), recv)
+    torch.cuda.synchronize()
+    check_layout({kk: v.cpu().numpy() for kk, v in lay.items()}, ref, T, k)
+    want = oracle.dispatch(x, ref["dest_row"], R, recv=np.full((R, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(from_dev_bf16(recv), want)
+
+
+def test_layout_dispatch_wide_is_deterministic():
+    wl = make_workload("train", seed=13, T=3000)
+    c = wl.config
+    idx, x = to_dev(wl.topk_idx), to_dev_bf16(wl.x)
+    outs = []
+    for _ in range(3):
+        recv = torch.zeros((c.T * c.k, c.H), dtype=torch.bfloat16, device=DEV)
+        lay = ep.ep_layout_dispatch(idx, c.E, x, recv)
+        torch.cuda.synchronize()
+        outs.append((lay["dest_row"].cpu().numpy(), lay["src_token"].cpu().numpy(), recv.view(torch.int16).cpu()))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o[0], outs[0][0])
+        np.testing.assert_array_equal(o[1], outs[0][1])
+        assert torch.equal(o[2], outs[0][2])
