@@ -563,6 +563,11 @@ def kernels_only(s, launches=5, copy_bytes=256 << 20):
         s.dispatch()
     for _ in range(launches):
         s.combine()
+    if s.do_dispatch:
+        s.fused = True
+        for _ in range(launches):
+            s.layout()
+        s.fused = False
     a = torch.empty(copy_bytes // 4, dtype=torch.int32, device="cuda:0")
     b = torch.empty_like(a)
     for _ in range(launches):

@@ -28,6 +28,7 @@ KERNEL_SOURCES = {
     "dispatch": ["dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
     "combine": ["combine.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
     "combine_reduce": ["combine_reduce.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "layout_dispatch": ["layout_dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
 }
 
 

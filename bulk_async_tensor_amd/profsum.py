@@ -5,7 +5,7 @@
       benchmark measured with HIP events in the same run.
 
   python -m bulk_async_tensor_amd.profsum hbm <fetch_counter_collection.csv> <write_counter_collection.csv>
-          --kernel dispatch|combine|layout --workload NAME --out FILE --command "..."
+          --kernel dispatch|combine|layout|layout_dispatch --workload NAME --out FILE --command "..."
       HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
       each scaled by what the same counter reads for the copy probe, which
       reads and writes exactly --copy-bytes (default 256 MiB).
@@ -19,7 +19,9 @@ import sys
 
 from .build import kernel_source_hash
 
+# first match wins: the one-launch layout + dispatch kernels before the layout ones
 KINDS = {
+    "layout_dispatch": ("layout_dispatch",),
     "layout": ("layout_",),
     "dispatch": ("dispatch_",),
     "combine": ("combine_",),
@@ -154,7 +156,7 @@ def main(argv=None):
     h = sub.add_parser("hbm")
     h.add_argument("fetch")
     h.add_argument("write")
-    h.add_argument("--kernel", required=True, choices=["layout", "dispatch", "combine"])
+    h.add_argument("--kernel", required=True, choices=["layout", "dispatch", "combine", "layout_dispatch"])
     h.add_argument("--workload", required=True)
     h.add_argument("--out", required=True)
     h.add_argument("--copy-bytes", type=int, default=256 << 20)
