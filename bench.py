@@ -360,6 +360,140 @@ def cpu_baseline(name, seconds, gpu=None):
     }
 
 
+_ORACLE_WORKER = {}
+
+
+def _oracle_worker_task(task):
+    """One token slice of dispatch or combine, by the oracle's own functions,
+    written into the shared output.  The worker maps the shared arrays (files
+    named in the task) on first use."""
+    import numpy as np
+
+    import oracle
+
+    spec, op, a, b = task
+    W = _ORACLE_WORKER
+    if W.get("spec") != spec:
+        W.clear()
+        for key, (path, shape, dtype) in spec.items():
+            W[key] = np.memmap(path, dtype=dtype, mode="r+", shape=tuple(shape))
+        W["spec"] = spec
+    if op == "dispatch":
+        oracle.dispatch(W["x"][a:b], W["dest"][a:b], W["recv"].shape[0], recv=W["recv"])
+    else:
+        W["out"][a:b] = oracle.combine(W["y"], W["dest"][a:b], W["w"][a:b])
+    return b - a
+
+
+def oracle_pool(workers):
+    """Processes for the all-cores oracle leg.  Started before this process
+    touches the GPU: they are new interpreters (spawn) that import no GPU
+    library."""
+    import multiprocessing as mp
+
+    return mp.get_context("spawn").Pool(workers)
+
+
+def cpu_baseline_parallel(name, seconds, pool, workers):
+    """The same oracle functions on `workers` host processes: the layout as
+    it stands in this process (its counting pass runs over the tokens in
+    order), then dispatch and combine over token slices in a process pool,
+    each slice writing its own rows of arrays shared through files
+    (`pool` from oracle_pool(workers)).  The expert op is computed once beforehand (it is not part of a step).
+    The last pass's outputs are compared with the one-process oracle's."""
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    import oracle
+    from synth import algorithmic_bytes, make_workload
+
+    wl = make_workload(name)
+    c = wl.config
+    R = c.T * c.k
+    dispatch_too = c.ops != "combine"
+    lay = oracle.layout(wl.topk_idx, c.E)
+    recv1 = oracle.dispatch(wl.x, lay["dest_row"], R) if dispatch_too else None
+    if not dispatch_too:
+        y1 = wl.y
+    elif c.expert == "scale":
+        y1 = oracle.expert_scale(recv1, lay["offsets"], wl.scales)
+    else:
+        y1 = None  # identity: combine reads the shared receive buffer itself
+    out1 = oracle.combine(y1 if y1 is not None else recv1, lay["dest_row"], wl.topk_w)
+
+    tmp = tempfile.mkdtemp(prefix="ep_oracle_")
+    try:
+        arrays = {}
+
+        def shared(key, shape, dtype, init=None):
+            path = os.path.join(tmp, key)
+            m = np.memmap(path, dtype=dtype, mode="w+", shape=shape)
+            if init is not None:
+                m[...] = init
+            m.flush()
+            arrays[key] = m
+            return (path, list(shape), np.dtype(dtype).str)
+
+        spec = {"dest": shared("dest", (c.T, c.k), np.int32, lay["dest_row"]),
+                "w": shared("w", (c.T, c.k), np.float32, wl.topk_w),
+                "out": shared("out", (c.T, c.H), np.uint16)}
+        if dispatch_too:
+            spec["x"] = shared("x", (c.T, c.H), np.uint16, wl.x)
+            spec["recv"] = shared("recv", (R, c.H), np.uint16)
+        if y1 is not None:
+            spec["y"] = shared("y", (R, c.H), np.uint16, y1)
+        else:
+            spec["y"] = spec["recv"]
+        chunks = max(1, workers * 4)
+        bounds = np.linspace(0, c.T, chunks + 1).astype(int)
+        slices = [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        passes = 0
+        t_total = 0.0
+        pool.map(_oracle_worker_task, [(spec, "combine", 0, 1)] * (4 * workers))  # arrays mapped
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            lay_p = oracle.layout(wl.topk_idx, c.E)
+            arrays["dest"][...] = lay_p["dest_row"]
+            if dispatch_too:
+                pool.map(_oracle_worker_task, [(spec, "dispatch", a, b) for a, b in slices])
+            pool.map(_oracle_worker_task, [(spec, "combine", a, b) for a, b in slices])
+            t_total += time.perf_counter() - t0
+            passes += 1
+            if time.perf_counter() - t_start >= seconds:
+                break
+        same = bool(np.array_equal(arrays["out"], out1) and
+                    (not dispatch_too or np.array_equal(arrays["recv"], recv1)))
+        arrays.clear()
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    per_step = t_total / passes
+    b = algorithmic_bytes(c.T, c.H, c.k, c.E)
+    step_bytes = b["layout"] + b["combine"] + (b["dispatch"] if dispatch_too else 0)
+    return {
+        "value": round(step_bytes / per_step / 1e9, 3),
+        "unit": "GB/s",
+        "tokens_per_s": round(c.T / per_step, 1),
+        "s_per_step": round(per_step, 4),
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"whole {name} workload (T={c.T}), {passes} pass(es); layout in one process, dispatch and "
+                  f"combine over {len(slices)} token slices on {workers} processes",
+        "matches_one_process_oracle": same,
+    }
+
+
+def host_threads(cap=16):
+    """Host cores this process may use, at most `cap` (the CPU share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
 def parity_against(s, lay, recv, out):
     """The GPU outputs of the timed step (layout, dispatch, combine on the
     workload's inputs) against the oracle's: bit-exact flags for layout and
@@ -699,6 +833,10 @@ def main():
         print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
               "(a single-GPU kernel library with no collectives)", file=sys.stderr)
         sys.exit(2)
+    # the all-cores oracle's processes start before anything touches the GPU
+    pool = None
+    if not args.no_cpu and not (args.probe_sweep or args.overlap or args.sweep or args.kernels_only):
+        pool = oracle_pool(host_threads())
     import torch
 
     import bulk_async_tensor_amd as ep
@@ -831,6 +969,10 @@ def main():
                                 "tokens_per_s": round(s.T / (ms_g * 1e-3), 1)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, gpu=s)
+        line["cpu_baseline"]["all_cores"] = cpu_baseline_parallel(args.workload, args.cpu_seconds / 2, pool,
+                                                                  host_threads())
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 
