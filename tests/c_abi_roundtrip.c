@@ -9,7 +9,9 @@
  *   - dispatch: recv[dest_row[t,j]] equals x[t] bit for bit;
  *   - combine with the identity expert and weights summing to 1 (here 1/k
  *     for k = 4, exact in fp32): combine(dispatch(x)) == x bit for bit, since
- *     each bf16 row times 1/4, four times added, is exact.
+ *     each bf16 row times 1/4, four times added, is exact;
+ *   - ep_layout_dispatch with NULL src_token and status gives the same
+ *     dest_row and receive rows as the two separate calls.
  * Prints "c_abi_roundtrip: ok" and exits 0 on success, prints the first
  * failure and exits 1 otherwise.
  */
@@ -23,7 +25,7 @@
 
 #define T 300
 #define K 4
-#define E 37
+#define E 80 /* 65..256 experts and 1200 entries: ep_layout_dispatch runs as one wide launch */
 #define H 1032 /* not a multiple of 512 elements: ragged slabs */
 
 static int fail(const char* what) {
@@ -52,7 +54,8 @@ static uint32_t lcg(uint32_t* s) {
 
 int main(void) {
   static int32_t idx[T * K], counts[E], offsets[E + 1], dest[T * K], src[T * K], status;
-  static uint16_t x[T * H], recv[T * K * H], out[T * H];
+  static uint16_t x[T * H], recv[T * K * H], out[T * H], recv2[T * K * H];
+  static int32_t dest2[T * K];
   static float w[T * K];
   uint32_t seed = 12345u;
 
@@ -130,6 +133,17 @@ int main(void) {
     for (int r = offsets[e] + 1; r < offsets[e + 1]; ++r)
       if (src[r] <= src[r - 1]) return fail("tokens do not ascend inside a segment");
   if (memcmp(out, x, sizeof out) != 0) return fail("combine(dispatch(x)) != x");
+
+  /* the one-call form, without the optional outputs, on fresh buffers */
+  HIP_OK(hipMemset(d_dest, 0xFF, sizeof dest));
+  HIP_OK(hipMemset(d_recv, 0, sizeof recv));
+  EP_CALL(ep_layout_dispatch(d_idx, T, K, E, d_x, H, d_counts, d_offsets, d_dest, NULL, NULL, d_ws, ws, d_recv,
+                             (int64_t)T * K, NULL));
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(dest2, d_dest, sizeof dest2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(recv2, d_recv, sizeof recv2, hipMemcpyDeviceToHost));
+  if (memcmp(dest2, dest, sizeof dest) != 0) return fail("ep_layout_dispatch dest_row differs");
+  if (memcmp(recv2, recv, sizeof recv) != 0) return fail("ep_layout_dispatch receive rows differ");
 
   hipFree(d_idx); hipFree(d_counts); hipFree(d_offsets); hipFree(d_dest); hipFree(d_src);
   hipFree(d_status); hipFree(d_w); hipFree(d_x); hipFree(d_recv); hipFree(d_out);

@@ -644,6 +644,20 @@ def test_layout_dispatch_wide_flags_bad_ids(E, k):
     np.testing.assert_array_equal(from_dev_bf16(recv), want)
 
 
+@pytest.mark.parametrize("rows", [0, 1, 4096, 20000])
+def test_layout_dispatch_wide_short_receive_buffer(rows):
+    # rows past the receive buffer are skipped, as in ep_dispatch
+    wl = make_workload("train", seed=14, T=3000, H=1024)
+    c = wl.config
+    ref = oracle.layout(wl.topk_idx, c.E)
+    recv = torch.full((rows, c.H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay = ep.ep_layout_dispatch(to_dev(wl.topk_idx), c.E, to_dev_bf16(wl.x), recv)
+    torch.cuda.synchronize()
+    check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+    want = oracle.dispatch(wl.x, ref["dest_row"], rows, recv=np.full((rows, c.H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(from_dev_bf16(recv), want)
+
+
 def test_layout_dispatch_wide_is_deterministic():
     wl = make_workload("train", seed=13, T=3000)
     c = wl.config
