@@ -274,8 +274,9 @@ def reduce_times(s, steps, budgets):
 
 
 def read_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, or None when it
-    is missing or was taken on different kernel sources."""
+    """HBM bytes per library call (one launch, or the several of a phased
+    combine) from the committed counter summary, or None when it is missing
+    or was taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
@@ -290,7 +291,7 @@ def read_traffic(kernel, workload):
     if fields.get("kernel_sources") != kernel_source_hash(kernel):
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields.get("hbm_bytes_per_call", fields["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
 

@@ -104,9 +104,14 @@ def hbm(args):
         f"hbm_write_bytes_per_launch: {write_b:.0f}",
         f"hbm_bytes_per_launch: {read_b + write_b:.0f}",
     ]
+    n = args.launches_per_call
+    if n > 1:
+        # one library call runs n launches of equal share (the phased combine on large batches)
+        lines.append(f"launches_per_call: {n}")
+        lines.append(f"hbm_bytes_per_call: {(read_b + write_b) * n:.0f}")
     if args.algorithmic:
-        lines.append(f"algorithmic_bytes_per_launch: {args.algorithmic}")
-        lines.append(f"traffic_over_algorithmic: {(read_b + write_b) / args.algorithmic:.4f}")
+        lines.append(f"algorithmic_bytes_per_call: {args.algorithmic}")
+        lines.append(f"traffic_over_algorithmic: {(read_b + write_b) * n / args.algorithmic:.4f}")
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -160,7 +165,8 @@ def main(argv=None):
     h.add_argument("--workload", required=True)
     h.add_argument("--out", required=True)
     h.add_argument("--copy-bytes", type=int, default=256 << 20)
-    h.add_argument("--algorithmic", type=int, default=0)
+    h.add_argument("--algorithmic", type=int, default=0, help="algorithmic bytes of one library call")
+    h.add_argument("--launches-per-call", type=int, default=1)
     h.add_argument("--command-fetch", default="")
     h.add_argument("--command-write", default="")
     q = sub.add_parser("sq")
