@@ -524,6 +524,54 @@ def test_graph_replay_matches_eager(name):
         assert np.array_equal(oracle.bf16_to_f32(from_dev_bf16(out)), oracle.bf16_to_f32(wl.x))
 
 
+@pytest.mark.parametrize("name,over", [("decode", {}), ("train", dict(T=1000)), ("train", {})])
+def test_graph_replay_one_launch_layout_dispatch(name, over):
+    """ep_layout_dispatch (the small and the wide one-launch kernels) and
+    ep_combine captured in a HIP graph: every replay, with the outputs
+    clobbered eagerly in between, equals the oracle."""
+    wl = make_workload(name, seed=15, **over)
+    c = wl.config
+    idx = to_dev(wl.topk_idx)
+    x = to_dev_bf16(wl.x)
+    w = to_dev(wl.topk_w)
+    R = c.T * c.k
+    i32 = dict(dtype=torch.int32, device=DEV)
+    lay = {"counts": torch.empty(c.E, **i32), "offsets": torch.empty(c.E + 1, **i32),
+           "dest_row": torch.empty((c.T, c.k), **i32), "src_token": torch.empty(R, **i32),
+           "status": torch.empty(1, **i32)}
+    ws = torch.empty(max(16, ep.ep_layout_workspace_bytes(c.T, c.k, c.E)), dtype=torch.uint8, device=DEV)
+    recv = torch.empty((R, c.H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        ep.ep_layout_dispatch(idx, c.E, x, recv, lay["counts"], lay["offsets"], lay["dest_row"], lay["src_token"],
+                              lay["status"], ws)
+        ep.ep_combine(recv, lay["dest_row"], w, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ref = oracle.layout(wl.topk_idx, c.E)
+    ref_recv = oracle.dispatch(wl.x, ref["dest_row"], R)
+    for rep in range(4):
+        recv.view(torch.int16).fill_(rep)
+        out.view(torch.int16).fill_(rep)
+        lay["dest_row"].fill_(-7)
+        lay["src_token"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+        np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
+        assert np.array_equal(oracle.bf16_to_f32(from_dev_bf16(out)), oracle.bf16_to_f32(wl.x))
+
+
 @pytest.mark.parametrize(
     "name,over",
     [("decode", {}), ("tiny", {}), ("prefill", dict(T=170, E=64, k=6)), ("prefill", dict(T=33, H=7176, E=16, k=3)),
