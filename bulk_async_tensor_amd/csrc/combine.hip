@@ -361,12 +361,13 @@ __device__ __forceinline__ void phase_sum_set(float (&acc)[SEG][8], const u32x4 
     if (j0 + g < K) phase_sum<K, SEG>(acc, v[g], s, j0 + g, recv_rows);
 }
 
-// HELD <= kPhaseHeld output vectors held per wave; SEG vectors of a row are read
-// per source row and step (SEG KiB contiguous per row), G slots per register
+// HELD output vectors held per wave; SEG vectors of a row are read per
+// source row and step (SEG KiB contiguous per row), G slots per register
 // set.  With several tokens per unit, SEG divides nv so that a step never
-// spans two tokens.
-template <int K, int SEG, int G, int HELD, bool EVEN>
-__global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __restrict__ y, u32x4* __restrict__ out,
+// spans two tokens.  MAXT: threads per workgroup at most (16 waves for the
+// 16-vector hold; 8 for the 28-vector one, which needs about 175 VGPRs).
+template <int K, int SEG, int G, int HELD, bool EVEN, int MAXT>
+__global__ __launch_bounds__(MAXT) void combine_phase_kernel(const u32x4* __restrict__ y, u32x4* __restrict__ out,
                                                              const int32_t* __restrict__ dest_row,
                                                              const float* __restrict__ w, int64_t recv_rows,
                                                              int row_vec, int nv, int T, int tpu, int nseg, int seg,
@@ -463,13 +464,13 @@ __global__ __launch_bounds__(1024) void combine_phase_kernel(const u32x4* __rest
 using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int, int, int,
                          int);
 
-template <int SEG, int G, int HELD, bool EVEN>
+template <int SEG, int G, int HELD, bool EVEN, int MAXT = kPhaseWpg * kWave>
 PhaseFn pick_phase_k(int k) {
   switch (k) {
-    case 2: return combine_phase_kernel<2, SEG, G, HELD, EVEN>;
-    case 4: return combine_phase_kernel<4, SEG, G, HELD, EVEN>;
-    case 6: return combine_phase_kernel<6, SEG, G, HELD, EVEN>;
-    case 8: return combine_phase_kernel<8, SEG, G, HELD, EVEN>;
+    case 2: return combine_phase_kernel<2, SEG, G, HELD, EVEN, MAXT>;
+    case 4: return combine_phase_kernel<4, SEG, G, HELD, EVEN, MAXT>;
+    case 6: return combine_phase_kernel<6, SEG, G, HELD, EVEN, MAXT>;
+    case 8: return combine_phase_kernel<8, SEG, G, HELD, EVEN, MAXT>;
     default: return nullptr;
   }
 }
@@ -479,23 +480,42 @@ PhaseFn pick_phase_k(int k) {
 // output spill at k >= 6.)
 template <bool EVEN>
 PhaseFn pick_phase(int seg_vec, int held, int k) {
+  if (held == kPhaseWideHeld) return pick_phase_k<1, 4, kPhaseWideHeld, EVEN, kPhaseWideWpg * kWave>(k);
   if (seg_vec == 2) return held == 14 ? pick_phase_k<2, 2, 14, EVEN>(k) : pick_phase_k<2, 2, 16, EVEN>(k);
   return held == 14 ? pick_phase_k<1, 4, 14, EVEN>(k) : pick_phase_k<1, 4, 16, EVEN>(k);
+}
+
+// Rows of 9 to 14 vectors per lane (H from 4104 to 7168) hold two or three
+// whole rows per wave in workgroups of 8 waves instead of one row in
+// workgroups of 16: as many rows per CU (or more, at 9 vectors), written as
+// one burst of two or three adjacent output rows per wave.  At the training
+// shape this took the combine from 84.2 to 82.5 us (E = 256) and from 88.6
+// to 80.8 us (E = 128), bit-identical.  Larger rows would drop to one row per
+// wave and smaller ones to fewer rows per CU.
+// Vectors per contiguous read of the phased combine: 1 by default (runs of
+// 2 measured 5% slower at the train shape: fewer slots in flight); a
+// requested slab of 2 takes runs of 2 where a step can.
+int combine_phase_seg(const Budget& b, int row_vec) {
+  const PhaseShape p16 = phase_shape(row_vec);
+  return (b.slab_vpl >= 2 && (p16.tpu == 1 || p16.nv % 2 == 0)) ? 2 : 1;
+}
+
+PhaseShape combine_phase_shape(int row_vec, int seg_vec) {
+  const int nv = (row_vec + kWave - 1) / kWave;
+  if (seg_vec == 1 && nv >= 9 && nv <= 14) return phase_shape(row_vec, kPhaseWideHeld, kPhaseWideWpg);
+  return phase_shape(row_vec);
 }
 
 
 hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int row_vec, const int32_t* dest_row,
                         const float* w, int T, int k, void* out, hipStream_t stream) {
   const bool even = row_vec % kWave == 0;
-  const PhaseShape ps = phase_shape(row_vec);
-  // vectors per contiguous read: 1 by default (runs of 2 measured 5% slower
-  // at the train shape: fewer slots in flight); a requested slab of 2 takes
-  // runs of 2 where a step can; 14 held vectors when a unit never needs more
-  // (whole tokens at H = 7168), which frees registers for the reads
-  int seg_vec = 1;
-  if (b.slab_vpl >= 2 && (ps.tpu == 1 || ps.nv % 2 == 0)) seg_vec = 2;
+  // 14 held vectors when a unit never needs more (whole tokens at H = 7168
+  // in the 16-wave shape), which frees registers for the reads
+  const int seg_vec = combine_phase_seg(b, row_vec);
+  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec);
   const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
-  const int held = unit_vec <= 14 ? 14 : 16;
+  const int held = ps.held == kPhaseWideHeld ? kPhaseWideHeld : unit_vec <= 14 ? 14 : 16;
   PhaseFn fn = even ? pick_phase<true>(seg_vec, held, k) : pick_phase<false>(seg_vec, held, k);
   if (!fn) return hipErrorInvalidValue;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
@@ -516,7 +536,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
     const int units = (int)phase_units(ps, tb);
     int grid = units < cus ? units : cus;
     if (grid < 1) grid = 1;
-    const int wpg = (units + grid - 1) / grid;  // <= kPhaseWpg
+    const int wpg = (units + grid - 1) / grid;  // <= ps.wpg
     hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(y),
                        static_cast<u32x4*>(out) + t0 * row_vec, dest_row + t0 * k, w + t0 * k, recv_rows, row_vec,
                        ps.nv, tb, ps.tpu, ps.nseg, ps.seg, units);
@@ -535,9 +555,10 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-  if (2 * cus < b.device_cus) return false;
-  const int64_t units = phase_units(phase_shape(row_vec), T);
-  return units * 4 >= (int64_t)cus * kPhaseWpg * 3;
+  if (2 * cus < b.all_cus) return false;
+  const PhaseShape ps = combine_phase_shape(row_vec, combine_phase_seg(b, row_vec));
+  const int64_t units = phase_units(ps, T);
+  return units * 4 >= (int64_t)cus * ps.wpg * 3;
 }
 
 using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);

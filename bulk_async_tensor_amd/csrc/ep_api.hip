@@ -58,8 +58,32 @@ constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
-// Device of the calling thread, checked once: gfx950 and its CU count.
-int current_device(ep::Budget* b) {
+// Compute units a launch on `stream` may use: the stream's CU mask (a
+// stream made by ep_stream_create_cu_masked, or any other masked stream)
+// narrows b->device_cus, so that grids, persistent budgets and the kernel
+// choices that depend on the CU count follow the mask.  A stream whose mask
+// cannot be read counts as unmasked; the failed query's error is cleared so
+// that the launch checks after it do not see it.
+void apply_stream_mask(hipStream_t stream, ep::Budget* b) {
+  uint32_t mask[64];
+  if (hipExtStreamGetCUMask(stream, 64, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  const int words = (b->all_cus + 31) / 32;
+  int n = 0;
+  for (int i = 0; i < words && i < 64; ++i) {
+    uint32_t m = mask[i];
+    const int bits = b->all_cus - 32 * i;
+    if (bits < 32) m &= (1u << bits) - 1u;
+    n += __builtin_popcount(m);
+  }
+  if (n > 0 && n < b->device_cus) b->device_cus = n;
+}
+
+// Device of the calling thread, checked once: gfx950 and its CU count; then
+// the CU count that `stream` may use.
+int current_device(ep::Budget* b, void* stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -76,8 +100,10 @@ int current_device(ep::Budget* b) {
   }
   if (!d.gfx950) return fail(EP_ERR_UNSUPPORTED, "libep is built for gfx950 only");
   b->device_cus = d.cus;
+  b->all_cus = d.cus;
   b->num_cus = num_cus_setting();
   b->slab_vpl = g_slab.load();
+  apply_stream_mask(static_cast<hipStream_t>(stream), b);
   return EP_OK;
 }
 
@@ -217,7 +243,7 @@ int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int
                              workspace_bytes, "ep_layout");
   if (rc) return rc;
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
                                    static_cast<hipStream_t>(stream));
@@ -238,7 +264,7 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
   if (dest_row && !aligned(dest_row, 4)) return fail(EP_ERR_ALIGNMENT, "ep_dispatch: dest_row not 4-byte aligned");
   if (T == 0 || recv_rows == 0) return EP_OK;
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_dispatch(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, dest_row, k, recv,
                                      recv_rows, static_cast<hipStream_t>(stream));
@@ -259,7 +285,7 @@ int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void*
   if ((x && !aligned(x, 16)) || (recv && !aligned(recv, 16)))
     return fail(EP_ERR_ALIGNMENT, "ep_layout_dispatch: bf16 tensor not 16-byte aligned");
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_layout_dispatch(static_cast<ep::Variant>(g_variant.load()), b, topk_idx, T, k, E, x, H,
                                             counts, offsets, dest_row, src_token, status, workspace, recv, recv_rows,
@@ -281,7 +307,7 @@ int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void
     return fail(EP_ERR_ALIGNMENT, "ep_dispatch_rows: src_token not 4-byte aligned");
   if (T == 0 || recv_rows == 0) return EP_OK;
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_dispatch_rows(static_cast<ep::Variant>(g_variant.load()), b, x, T, H, src_token, recv,
                                           recv_rows, static_cast<hipStream_t>(stream));
@@ -303,7 +329,7 @@ int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row,
     return fail(EP_ERR_ALIGNMENT, "ep_combine: dest_row/topk_w not 4-byte aligned");
   if (T == 0) return EP_OK;
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_combine(static_cast<ep::Variant>(g_variant.load()), b, y, recv_rows, H, dest_row, topk_w,
                                     T, k, out, static_cast<hipStream_t>(stream));
@@ -337,7 +363,7 @@ int ep_combine_reduce(const void* y, int64_t recv_rows, int H, const int32_t* sr
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(EP_ERR_ALIGNMENT, "ep_combine_reduce: workspace not 16-byte aligned");
   ep::Budget b;
-  rc = current_device(&b);
+  rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_combine_reduce(b, y, recv_rows, H, src_token, dest_row, topk_w, T, k, out, workspace,
                                            static_cast<hipStream_t>(stream));
@@ -373,7 +399,7 @@ int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* strea
   if ((src && !aligned(src, 16)) || !aligned(dst, 16)) return fail(EP_ERR_ALIGNMENT, "ep_bw_probe: alignment");
   if (bytes == 0) return EP_OK;
   ep::Budget b;
-  int rc = current_device(&b);
+  int rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_bw_probe(b, mode, src, dst, bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ep_bw_probe launch");
@@ -385,7 +411,7 @@ int ep_probe_placement(int32_t* out, int n_groups, void* stream) {
     return fail(EP_ERR_INVALID_ARG, "ep_probe_placement: bad output or n_groups");
   if (!aligned(out, 4)) return fail(EP_ERR_ALIGNMENT, "ep_probe_placement: alignment");
   ep::Budget b;
-  int rc = current_device(&b);
+  int rc = current_device(&b, stream);
   if (rc) return rc;
   int launched = 0;
   hipError_t e = ep::launch_placement(b, n_groups, out, static_cast<hipStream_t>(stream), &launched);
@@ -398,7 +424,7 @@ int ep_mfma_probe(int n_groups, int iters, float* out, void* stream) {
     return fail(EP_ERR_INVALID_ARG, "ep_mfma_probe: bad output, n_groups or iters");
   if (!aligned(out, 4)) return fail(EP_ERR_ALIGNMENT, "ep_mfma_probe: alignment");
   ep::Budget b;
-  int rc = current_device(&b);
+  int rc = current_device(&b, stream);
   if (rc) return rc;
   hipError_t e = ep::launch_mfma_probe(n_groups, iters, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ep_mfma_probe launch");

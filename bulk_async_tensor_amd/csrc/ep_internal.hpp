@@ -12,7 +12,8 @@ enum class Variant : int { Auto = 0, Vgpr = 1, Vgpr2 = 2, Lds1 = 3, Lds2 = 4, Vg
 // Launch geometry chosen by the host for the row-movement kernels.
 struct Budget {
   int num_cus;     // > 0: persistent grid of this many workgroups, one per CU
-  int device_cus;  // compute units of the current device
+  int device_cus;  // compute units the launch may use: the device's, or fewer on a CU-masked stream
+  int all_cus;     // compute units of the current device
   int slab_vpl;    // 16-byte vectors per lane per row slab (0: the kernel's default)
 };
 

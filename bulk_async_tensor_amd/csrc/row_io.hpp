@@ -96,27 +96,35 @@ __device__ __forceinline__ void read_slab(u32x4 (&v)[VPL], const char* slice, in
   for (int i = 0; i < VPL; ++i) lds_fence_value(v[i]);
 }
 
-// ---- phased units: a wave holds up to kPhaseHeld vectors per lane (16 KiB)
-// of rows in registers between reading and writing them.  A unit is tpu
-// whole rows when a row has at most kPhaseHeld vectors per lane (nseg == 1),
-// else one of nseg segments of seg vectors of one row.  Host-side geometry.
+// ---- phased units: a wave holds up to `held` vectors per lane of rows in
+// registers between reading and writing them: kPhaseHeld (16 KiB) in
+// workgroups of kPhaseWpg waves, or kPhaseWideHeld (28 KiB) in workgroups of
+// kPhaseWideWpg waves, which leaves each wave the registers for it.  A unit
+// is tpu whole rows when a row has at most `held` vectors per lane
+// (nseg == 1), else one of nseg segments of seg vectors of one row.
+// Host-side geometry.
 constexpr int kPhaseHeld = 16;
 constexpr int kPhaseWpg = 16;  // waves per workgroup; one such workgroup fits a CU
+constexpr int kPhaseWideHeld = 28;
+constexpr int kPhaseWideWpg = 8;
 
 struct PhaseShape {
   int nv, tpu, nseg, seg;
+  int held = kPhaseHeld, wpg = kPhaseWpg;
 };
 
-inline PhaseShape phase_shape(int row_vec) {
+inline PhaseShape phase_shape(int row_vec, int held = kPhaseHeld, int wpg = kPhaseWpg) {
   PhaseShape p;
+  p.held = held;
+  p.wpg = wpg;
   p.nv = (row_vec + kWave - 1) / kWave;
   p.tpu = 1;
   p.nseg = 1;
   p.seg = p.nv;
-  if (p.nv <= kPhaseHeld) {
-    p.tpu = kPhaseHeld / p.nv;
+  if (p.nv <= held) {
+    p.tpu = held / p.nv;
   } else {
-    p.nseg = (p.nv + kPhaseHeld - 1) / kPhaseHeld;
+    p.nseg = (p.nv + held - 1) / held;
     p.seg = (p.nv + p.nseg - 1) / p.nseg;
   }
   return p;
@@ -129,7 +137,7 @@ inline int64_t phase_units(const PhaseShape& p, int64_t T) {
 // Rows per launch so that every launch gives each wave of a grid of `cus`
 // workgroups at most one unit, in launches of equal size (whole units).
 inline int64_t phase_batch(const PhaseShape& p, int64_t T, int cus) {
-  const int64_t wave_slots = (int64_t)cus * kPhaseWpg;
+  const int64_t wave_slots = (int64_t)cus * p.wpg;
   const int64_t max_batch = p.nseg == 1 ? wave_slots * p.tpu : (wave_slots / p.nseg > 0 ? wave_slots / p.nseg : 1);
   const int64_t nbatch = (T + max_batch - 1) / max_batch;
   int64_t batch = (T + nbatch - 1) / nbatch;

@@ -300,11 +300,13 @@ def test_combine_ragged_rows(variant, H, k, budget):
     assert_combine_close(got, ref)
 
 
-# The phase kernel's unit shapes: several tokens per unit (H = 8, 2048, 4104
-# ragged), one token (7168), a row split into segments (8712 ragged: 18
-# vectors per lane in two segments of 9; 16384: two of 16), a last unit that
-# is only partly filled, and several units per wave (budget 1: 16 waves).
-@pytest.mark.parametrize("H", [8, 2048, 4104, 7168, 8712, 16384])
+# The phase kernel's unit shapes: several tokens per unit in 16-wave
+# workgroups (H = 8, 2048), two or three whole rows per wave in 8-wave
+# workgroups (4104 ragged: 9 vectors per lane, three rows; 5000 ragged, 6144
+# and 7168: two rows), a row split into segments (8712 ragged: 18 vectors per
+# lane in two segments of 9; 16384: two of 16), a last unit that is only
+# partly filled, and several units per wave (budget 1: one workgroup).
+@pytest.mark.parametrize("H", [8, 2048, 4104, 5000, 6144, 7168, 8712, 16384])
 @pytest.mark.parametrize("T", [1, 29, 300])
 @pytest.mark.parametrize("budget", [0, 1, 24])
 def test_combine_phase_units(H, T, budget):
@@ -317,6 +319,19 @@ def test_combine_phase_units(H, T, budget):
     dest[T // 2, k - 1] = -1  # a slot that contributes nothing
     got = run_combine(wl, wl.y, dest)
     assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
+
+
+# Several launches per call: batches of whole two-row units on 256 or 128 CUs
+# (4096 or 2048 tokens per launch at H = 7168), with a ragged last batch.
+@pytest.mark.parametrize("T,budget", [(4097, 0), (8193, 0), (5000, 128), (2049, 192)])
+@pytest.mark.parametrize("k", [6, 8])
+def test_combine_phase_batches(T, budget, k):
+    ep.ep_set_variant("phase")
+    ep.ep_set_num_cus(budget)
+    wl = make_workload("combine_stress", seed=T + k, T=T, H=7168, E=256, k=k)
+    lay = oracle.layout(wl.topk_idx, 256)
+    got = run_combine(wl, wl.y, lay["dest_row"])
+    assert_combine_close(got, oracle.combine(wl.y, lay["dest_row"], wl.topk_w))
 
 
 @pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2", "phase"])
@@ -468,6 +483,32 @@ def test_cu_masked_stream_confines_work():
             ep.ep_dispatch(x, dest, recv, stream=stream)
             stream.synchronize()
             np.testing.assert_array_equal(from_dev_bf16(recv), oracle_recv("train"))
+    finally:
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(stream)
+
+
+@pytest.mark.parametrize("n", [24, 128])
+def test_step_on_masked_stream(n):
+    """Layout, dispatch (in one launch) and combine on a stream masked to n
+    CUs with no budget set: the library reads the stream's mask and sizes its
+    grids and kernel choices for n CUs.  Outputs equal the oracle's."""
+    stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(n)))
+    try:
+        wl = workload("train")
+        c = wl.config
+        ref = oracle_layout("train")
+        recv = torch.empty((c.T * c.k, c.H), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+        idx, x, w = to_dev(wl.topk_idx), to_dev_bf16(wl.x), to_dev(wl.topk_w)
+        y = to_dev_bf16(expert_outputs("train"))
+        torch.cuda.synchronize()
+        lay = ep.ep_layout_dispatch(idx, c.E, x, recv, stream=stream)
+        ep.ep_combine(y, lay["dest_row"], w, out, stream=stream)
+        stream.synchronize()
+        check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+        np.testing.assert_array_equal(from_dev_bf16(recv), oracle_recv("train"))
+        assert_combine_close(from_dev_bf16(out), oracle_out("train"))
     finally:
         torch.cuda.synchronize()
         ep.ep_stream_destroy(stream)
