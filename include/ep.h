@@ -75,6 +75,11 @@ enum {
  * writes, and HBM write throughput peaks with about a quarter of the CUs
  * issuing them).  The initial value comes from the environment variable
  * EP_NUM_CUS (default 0).
+ * On a CU-masked stream (ep_stream_create_cu_masked, or any stream whose
+ * mask hipExtStreamGetCUMask reports) every launch counts only the CUs of
+ * the mask: n and the 64-CU dispatch budget are clamped to them, ordinary
+ * grids are sized for them, and the kernel choices that depend on the CU
+ * count (the phased combine needs at least half the device) use them.
  * Returns EP_OK, or EP_ERR_INVALID_ARG for n < 0 or n > 4096.
  */
 int ep_set_num_cus(int n);
