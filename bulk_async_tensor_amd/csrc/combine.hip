@@ -485,13 +485,6 @@ PhaseFn pick_phase(int seg_vec, int held, int k) {
   return held == 14 ? pick_phase_k<1, 4, 14, EVEN>(k) : pick_phase_k<1, 4, 16, EVEN>(k);
 }
 
-// Rows of 9 to 14 vectors per lane (H from 4104 to 7168) hold two or three
-// whole rows per wave in workgroups of 8 waves instead of one row in
-// workgroups of 16: as many rows per CU (or more, at 9 vectors), written as
-// one burst of two or three adjacent output rows per wave.  At the training
-// shape this took the combine from 84.2 to 82.5 us (E = 256) and from 88.6
-// to 80.8 us (E = 128), bit-identical.  Larger rows would drop to one row per
-// wave and smaller ones to fewer rows per CU.
 // Vectors per contiguous read of the phased combine: 1 by default (runs of
 // 2 measured 5% slower at the train shape: fewer slots in flight); a
 // requested slab of 2 takes runs of 2 where a step can.
@@ -500,9 +493,20 @@ int combine_phase_seg(const Budget& b, int row_vec) {
   return (b.slab_vpl >= 2 && (p16.tpu == 1 || p16.nv % 2 == 0)) ? 2 : 1;
 }
 
-PhaseShape combine_phase_shape(int row_vec, int seg_vec) {
+// With every CU of the device, rows of 9 to 14 vectors per lane (H from
+// 4104 to 7168) hold two or three whole rows per wave in workgroups of 8
+// waves instead of one row in workgroups of 16: as many rows per CU (or
+// more, at 9 vectors), written as one burst of two or three adjacent output
+// rows per wave.  At the training shape this took the combine from 84.2 to
+// 82.5 us (E = 256) and from 88.6 to 80.8 us (E = 128), bit-identical.  On
+// fewer CUs the per-CU read rate is the bound and half the waves keep half
+// the reads in flight: 4.2 against 5.1 TB/s on 128 CUs, 4.3 against 5.8 on
+// 192, so there the 16-wave shape stays.  Larger rows would drop to one row
+// per wave and smaller ones to fewer rows per CU.
+PhaseShape combine_phase_shape(int row_vec, int seg_vec, int cus, int all_cus) {
   const int nv = (row_vec + kWave - 1) / kWave;
-  if (seg_vec == 1 && nv >= 9 && nv <= 14) return phase_shape(row_vec, kPhaseWideHeld, kPhaseWideWpg);
+  if (seg_vec == 1 && nv >= 9 && nv <= 14 && cus >= all_cus)
+    return phase_shape(row_vec, kPhaseWideHeld, kPhaseWideWpg);
   return phase_shape(row_vec);
 }
 
@@ -513,12 +517,12 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   // 14 held vectors when a unit never needs more (whole tokens at H = 7168
   // in the 16-wave shape), which frees registers for the reads
   const int seg_vec = combine_phase_seg(b, row_vec);
-  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec);
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
   const int held = ps.held == kPhaseWideHeld ? kPhaseWideHeld : unit_vec <= 14 ? 14 : 16;
   PhaseFn fn = even ? pick_phase<true>(seg_vec, held, k) : pick_phase<false>(seg_vec, held, k);
   if (!fn) return hipErrorInvalidValue;
-  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   const size_t lds_bytes = b.num_cus > 0 ? kExclusiveLds : 0;
   if (lds_bytes > 64 * 1024) {
     hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
@@ -556,7 +560,7 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (2 * cus < b.all_cus) return false;
-  const PhaseShape ps = combine_phase_shape(row_vec, combine_phase_seg(b, row_vec));
+  const PhaseShape ps = combine_phase_shape(row_vec, combine_phase_seg(b, row_vec), cus, b.all_cus);
   const int64_t units = phase_units(ps, T);
   return units * 4 >= (int64_t)cus * ps.wpg * 3;
 }
