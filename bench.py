@@ -498,8 +498,9 @@ def host_threads(cap=16):
 def parity_against(s, lay, recv, out):
     """The GPU outputs of the timed step (layout, dispatch, combine on the
     workload's inputs) against the oracle's: bit-exact flags for layout and
-    dispatch; for combine the bit-identical fraction and the gate
-    abs(g - r) <= 1e-2 abs(r) + 1e-3."""
+    dispatch; for combine the bit-identical fraction, the gate
+    abs(g - r) <= 1e-2 abs(r) + 1e-3 and the norm-relative error
+    ||g - r|| / ||r||."""
     import numpy as np
 
     import oracle
@@ -518,6 +519,9 @@ def parity_against(s, lay, recv, out):
     ro = oracle.bf16_to_f32(out)
     res["combine_bit_identical_frac"] = round(float(np.mean(go == ro)), 6)
     res["combine_within_gate"] = bool(np.all(np.abs(go.astype(np.float64) - ro) <= 1e-2 * np.abs(ro) + 1e-3))
+    rn = float(np.linalg.norm(ro.astype(np.float64)))
+    dn = float(np.linalg.norm(go.astype(np.float64) - ro))
+    res["combine_norm_rel_err"] = dn / rn if rn > 0 else dn
     return res
 
 

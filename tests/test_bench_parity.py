@@ -33,7 +33,7 @@ def test_parity_check_passes_and_catches_planted_mistakes():
 
     ok = bench.parity_against(fake_setup(lay, recv, out), lay, recv, out)
     assert ok == {"layout_bit_exact": True, "dispatch_bit_exact": True,
-                  "combine_bit_identical_frac": 1.0, "combine_within_gate": True}
+                  "combine_bit_identical_frac": 1.0, "combine_within_gate": True, "combine_norm_rel_err": 0.0}
 
     s = fake_setup(lay, recv, out)
     s.dest_row.view(-1)[5] += 1
@@ -48,6 +48,7 @@ def test_parity_check_passes_and_catches_planted_mistakes():
     s.out.view(torch.int16)[0, 0] += 1
     res = bench.parity_against(s, lay, recv, out)
     assert res["combine_bit_identical_frac"] < 1.0 and res["combine_within_gate"] is True
+    assert 0.0 < res["combine_norm_rel_err"] < 1e-2
 
     # a sign flip on a sizeable element: outside the gate
     s = fake_setup(lay, recv, out)
