@@ -1,0 +1,64 @@
+"""The rocprofv3 summariser (bulk_async_tensor_amd/profsum.py) on small
+hand-made counter files: kernel classification, the copy-probe scaling of
+FETCH_SIZE and WRITE_SIZE, the per-call sum of a multi-launch kernel, and
+the source hash that bench.py checks before it reports the traffic."""
+
+import csv
+
+from bulk_async_tensor_amd import profsum
+from bulk_async_tensor_amd.build import kernel_source_hash
+
+import bench
+
+COLS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def write_counters(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=COLS)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_kind_of_classifies_our_kernels():
+    k = profsum.kind_of
+    assert k("void ep::(anonymous namespace)::layout_fused_kernel<8>(int const*)") == "layout"
+    assert k("void ep::(anonymous namespace)::layout_dispatch_wide_kernel<7, 8, true>(int const*)") == "layout_dispatch"
+    assert k("void ep::(anonymous namespace)::layout_dispatch_kernel<2, 8, true>(int const*)") == "layout_dispatch"
+    assert k("void ep::(anonymous namespace)::dispatch_lds1_kernel<7, 8, true, true>(x)") == "dispatch"
+    assert k("void ep::(anonymous namespace)::combine_phase_kernel<8, 1, 4, 28, true, 512>(x)") == "combine"
+    assert k("void ep::(anonymous namespace)::reduce_scatter_kernel<8, true>(x)") == "combine_reduce"
+    assert k("void ep::(anonymous namespace)::bw_kernel<0, 8, 0>(x)") == "copy_probe"
+    assert k("void at::native::vectorized_elementwise_kernel<4>(x)") is None
+
+
+def test_hbm_scales_by_the_copy_probe_and_sums_launches(tmp_path):
+    comb = "void ep::(anonymous namespace)::combine_phase_kernel<6, 1, 4, 28, true, 512>(x)"
+    probe = "void ep::(anonymous namespace)::bw_kernel<0, 8, 0>(x)"
+    copy = 256 << 20
+    # FETCH_SIZE reads half the true bytes, WRITE_SIZE all of them (KiB per dispatch)
+    write_counters(tmp_path / "f.csv", "FETCH_SIZE", [(comb, 1000.0), (comb, 1002.0), (comb, 998.0), (probe, copy / 2048)])
+    write_counters(tmp_path / "w.csv", "WRITE_SIZE", [(comb, 100.0), (comb, 100.0), (comb, 100.0), (probe, copy / 1024)])
+    out = tmp_path / "combine_x_hbm_counters.txt"
+    profsum.main(["hbm", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "--kernel", "combine", "--workload", "x",
+                  "--out", str(out), "--algorithmic", str(4 * 2200 * 1024), "--launches-per-call", "4"])
+    fields = dict(line.split(": ", 1) for line in out.read_text().splitlines() if not line.startswith("#"))
+    assert float(fields["fetch_scale"]) == 2.0 and float(fields["write_scale"]) == 1.0
+    assert int(fields["hbm_bytes_per_launch"]) == (1000 * 2 + 100) * 1024  # medians, scaled
+    assert int(fields["hbm_bytes_per_call"]) == 4 * (1000 * 2 + 100) * 1024
+    assert abs(float(fields["traffic_over_algorithmic"]) - 2100 / 2200) < 1e-4
+    assert fields["kernel_sources"] == kernel_source_hash("combine")
+
+
+def test_bench_reads_traffic_per_call_and_checks_the_source_hash(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    good = prof / "combine_w_hbm_counters.txt"
+    good.write_text(f"kernel_sources: {kernel_source_hash('combine')}\nhbm_bytes_per_launch: 10\n"
+                    f"hbm_bytes_per_call: 40\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.read_traffic("combine", "w") == 40.0
+    good.write_text("kernel_sources: 0000000000000000\nhbm_bytes_per_launch: 10\n")
+    assert bench.read_traffic("combine", "w") is None
+    assert bench.read_traffic("dispatch", "w") is None
