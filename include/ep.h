@@ -179,12 +179,13 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
  * outputs, in one launch where that is faster (the low-latency kernel
  * family of [DeepEP-TMA], "TMA Implementation Across Kernel Types", and its
  * use for wide batches):
- *   - T*k <= 1024 entries (the decode shape, where launches rather than
- *     bytes set the time);
  *   - up to 64 Ki entries with k in {2, 4, 6, 8} and 65 <= E <= 256, while
  *     the dispatch variant is "auto" or "lds1": a persistent grid on the
  *     dispatch's compute units in which every workgroup histograms all ids
- *     and then ranks and copies its own range of tokens.
+ *     and then ranks and copies its own range of tokens (decode batches
+ *     included, where launches rather than bytes set the time);
+ *   - other batches of T*k <= 1024 entries: a grid in which every
+ *     workgroup lays out all the entries and copies its share.
  * Other batches run ep_layout and ep_dispatch in order on the stream.
  * Arguments as for ep_layout and ep_dispatch (x bf16 [T, H], recv bf16
  * [recv_rows, H]); the workspace must be given whenever ep_layout needs one

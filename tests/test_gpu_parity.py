@@ -650,10 +650,9 @@ def test_layout_dispatch_flags_bad_ids():
 
 
 # ------------------------------------------------- fused layout + dispatch, wide batches
-# Past 1024 entries, with k in {2, 4, 6, 8}, 65 <= E <= 256 and at most 64 Ki
-# entries, ep_layout_dispatch runs as one persistent launch in which every
-# workgroup histograms all ids and then ranks and copies its own token
-# range.  These cases put T off the grid size, rows off the slab size, E at
+# With k in {2, 4, 6, 8}, 65 <= E <= 256 and at most 64 Ki entries,
+# ep_layout_dispatch runs as one persistent launch in which every workgroup
+# histograms all ids and then ranks and copies its own token range.  These cases put T off the grid size, rows off the slab size, E at
 # both ends of the range, the entry count at its limit, and several ranking
 # rounds in one workgroup (the 24-CU budget at the training shape: 171
 # tokens x 8 = 1368 entries per workgroup).  The last cases fall outside the
@@ -685,6 +684,18 @@ def run_layout_dispatch(wl):
     torch.cuda.synchronize()
     check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
     np.testing.assert_array_equal(from_dev_bf16(recv), oracle.dispatch(wl.x, ref["dest_row"], R))
+
+
+# Decode-size batches (T*k <= 1024): the wide kernel where it applies, the
+# small one (every workgroup lays out all entries) under another variant.
+@pytest.mark.parametrize("name,over", [("decode", {}), ("decode", dict(T=1)), ("decode", dict(T=33)),
+                                       ("train", dict(T=128, H=1032)), ("train", dict(T=100, E=65, k=6))])
+@pytest.mark.parametrize("variant", ["auto", "vgpr"])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_layout_dispatch_decode_sizes(name, over, variant, budget):
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    run_layout_dispatch(make_workload(name, seed=16, **over))
 
 
 @pytest.mark.parametrize("name,over", WIDE_CASES)
