@@ -197,7 +197,8 @@ def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, s
 
 def ep_layout_dispatch(topk_idx, num_experts, x, recv, counts=None, offsets=None, dest_row=None, src_token=None,
                        status=None, workspace=None, stream=None):
-    """ep_layout then ep_dispatch (one launch for small batches).  Returns the layout dict."""
+    """ep_layout then ep_dispatch, in one launch where the library can (see include/ep.h).  Returns the
+    layout dict."""
     import torch
 
     _device_tensor(topk_idx, "topk_idx", torch.int32)

@@ -17,10 +17,11 @@
 //
 // Batches of up to 64 Ki entries with 65 to 256 experts and k in
 // {2, 4, 6, 8}, decode batches included: a persistent grid (one workgroup
-// of 16 waves per CU, on the dispatch's CU count) in which workgroup g owns
-// a contiguous range of tokens.  Each workgroup histograms all T*k ids into two LDS histograms,
-// the tokens before its range and the rest, so that it knows every expert's
-// total (hence the offsets) and the rows that earlier workgroups take,
+// of 16 waves per CU: the budget, or 64 CUs for large batches and 128 below
+// that) in which workgroup g owns a contiguous range of tokens.  Each
+// workgroup histograms all T*k ids into two LDS histograms, the tokens
+// before its range and the rest, so that it knows every expert's total
+// (hence the offsets) and the rows that earlier workgroups take,
 // without any communication between workgroups.  It then ranks only its own
 // entries, writes their dest_row and src_token, and copies its own rows
 // through per-wave LDS slices filled by direct-to-LDS loads, as the lds1
