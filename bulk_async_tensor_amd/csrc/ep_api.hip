@@ -15,6 +15,8 @@
 #include "ep.h"
 #include "ep_internal.hpp"
 
+static_assert(EP_MAX_TOPK == ep::kMaxK, "the kernels' largest k is the ABI's");
+
 namespace {
 
 thread_local char g_err[512] = "";

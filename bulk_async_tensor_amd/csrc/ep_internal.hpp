@@ -27,6 +27,9 @@ constexpr size_t kExclusiveLds = 80 * 1024 + 1024;
 // highest with about a quarter of the CUs issuing them.
 constexpr int kWriteCus = 64;
 
+// Largest k the kernels accept (the ABI's EP_MAX_TOPK).
+constexpr int kMaxK = 32;
+
 // ---- layout (layout.hip)
 int layout_chunk_tokens(int k);
 int layout_num_chunks(int T, int k);

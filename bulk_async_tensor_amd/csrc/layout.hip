@@ -84,15 +84,14 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(const int32
     const uint64_t m = same_value_lanes(ok, e, nbits);
     if (ok && (m >> lane) == 1ull) atomicAdd(&hist[e], __builtin_popcountll(m));
   }
-  // repeated expert inside one token: thread per token, pairwise
-  for (int tt = threadIdx.x; tt < nt; tt += blockDim.x) {
-    const int32_t* r = ent + tt * k;
-    for (int j = 1; j < k; ++j) {
-      const int e = r[j];
-      if ((unsigned)e >= (unsigned)E) continue;
-      for (int j2 = 0; j2 < j; ++j2)
-        if (r[j2] == e) bad |= kStatusDuplicate;
-    }
+  // repeated expert inside one token: every entry is compared with the
+  // earlier entries of its token, entries spread over all threads (a thread
+  // per token would leave most threads idle and walk k^2 / 2 pairs each)
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = ent[i];
+    if ((unsigned)e >= (unsigned)E) continue;
+    for (int i2 = i - i % k; i2 < i; ++i2)
+      if (ent[i2] == e) bad |= kStatusDuplicate;
   }
   if (bad) atomicOr(&s_status, bad);
   __syncthreads();
@@ -340,41 +339,28 @@ constexpr int kFusedChunk = 1024;   // entries per workgroup: 16 waves x 64
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 
-// Reads the k ids of token t, checks them and adds them to the (chunk,
-// expert) histogram.  KT > 0: k known at compile time, so the loads of a
-// token are independent and issued together.
+// Reads the KT ids of token t (KT known at compile time, so its loads are
+// independent and issued together), keeps them in registers and adds them
+// to the (chunk, expert) histogram.  check_dups: compare every id with the
+// earlier ids of its token (only the workgroup that reports the status does).
 template <int KT>
-__device__ __forceinline__ void count_token(const int32_t* __restrict__ idx, int t, int k, int E, int32_t* cnt,
-                                            int& bad) {
-  constexpr int KA = KT > 0 ? KT : 1;
-  if constexpr (KT > 0) {
-    int e[KA];
+__device__ __forceinline__ void count_token(const int32_t* __restrict__ idx, int t, int E, int32_t* cnt, int& bad,
+                                            bool check_dups) {
+  int e[KT];
 #pragma unroll
-    for (int j = 0; j < KA; ++j) e[j] = idx[(int64_t)t * KA + j];
+  for (int j = 0; j < KT; ++j) e[j] = idx[(int64_t)t * KT + j];
 #pragma unroll
-    for (int j = 0; j < KA; ++j) {
-      const int i = t * KA + j;
-      if ((unsigned)e[j] < (unsigned)E) {
-        atomicAdd(&cnt[(i >> 10) * E + e[j]], 1);
+  for (int j = 0; j < KT; ++j) {
+    const int i = t * KT + j;
+    if ((unsigned)e[j] < (unsigned)E) {
+      atomicAdd(&cnt[(i >> 10) * E + e[j]], 1);
+      if (check_dups) {
 #pragma unroll
         for (int j2 = 0; j2 < j; ++j2)
           if (e[j2] == e[j]) bad |= kStatusDuplicate;
-      } else {
-        bad |= kStatusOutOfRange;
       }
-    }
-  } else {
-    const int32_t* r = idx + (int64_t)t * k;
-    for (int j = 0; j < k; ++j) {
-      const int e = r[j];
-      const int i = t * k + j;
-      if ((unsigned)e < (unsigned)E) {
-        atomicAdd(&cnt[(i >> 10) * E + e], 1);
-        for (int j2 = 0; j2 < j; ++j2)
-          if (r[j2] == e) bad |= kStatusDuplicate;
-      } else {
-        bad |= kStatusOutOfRange;
-      }
+    } else {
+      bad |= kStatusOutOfRange;
     }
   }
 }
@@ -406,13 +392,15 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
   const int my_e = my_i < N ? idx[my_i] : -1;
   __syncthreads();
 
-  // Every workgroup histograms all tokens (thread per token) and validates
-  // them, so each one knows the totals and the global status by itself.
-  // Two tokens per trip keep 2k loads in flight per thread.
+  // Every workgroup histograms all tokens (thread per token), so each one
+  // knows the totals by itself; workgroup 0, which reports the status, also
+  // looks for repeated experts.  Two tokens per trip keep 2k loads in flight
+  // per thread.
   int bad = 0;
+  const bool dups = c == 0;
   for (int t = tid; t < T; t += 2 * kFusedThreads) {
-    count_token<KT>(idx, t, k, E, cnt, bad);
-    if (t + kFusedThreads < T) count_token<KT>(idx, t + kFusedThreads, k, E, cnt, bad);
+    count_token<KT>(idx, t, E, cnt, bad, dups);
+    if (t + kFusedThreads < T) count_token<KT>(idx, t + kFusedThreads, E, cnt, bad, dups);
   }
   if (bad) atomicOr(&s_status, bad);
   __syncthreads();
@@ -461,6 +449,12 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
 
 using FusedFn = void (*)(const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*);
 
+// The one-launch kernel exists for these k only: with k known at run time a
+// token's ids could not stay in registers, and the kernel measured 30-40 us
+// at 32 Ki entries (k = 3, 7, 16, 32) against 8.5 us for k = 8.  Other k take
+// the count kernel, whose chunk of ids sits in LDS.
+bool fused_k(int k) { return k == 1 || k == 2 || k == 4 || k == 6 || k == 8; }
+
 FusedFn fused_for(int k) {
   switch (k) {
     case 1: return layout_fused_kernel<1>;
@@ -468,7 +462,7 @@ FusedFn fused_for(int k) {
     case 4: return layout_fused_kernel<4>;
     case 6: return layout_fused_kernel<6>;
     case 8: return layout_fused_kernel<8>;
-    default: return layout_fused_kernel<0>;
+    default: return nullptr;
   }
 }
 
@@ -503,7 +497,7 @@ Path layout_path(int T, int k, int E) {
   const int64_t N = (int64_t)T * k;
   const int64_t nf = (N + kFusedChunk - 1) / kFusedChunk;
   const bool fits = fused_lds_bytes(T, k, E) <= 144 * 1024;
-  if (fits && (nf <= kFusedFewChunks || (E >= kFusedMinExperts && nf <= EP_LAYOUT_FUSED_MAX_CHUNKS)))
+  if (fused_k(k) && fits && (nf <= kFusedFewChunks || (E >= kFusedMinExperts && nf <= EP_LAYOUT_FUSED_MAX_CHUNKS)))
     return Path::Fused;
   const int64_t ct = kChunkEntries / k;
   const int64_t nch = (T + ct - 1) / ct;
@@ -540,7 +534,9 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
     const int N = T * k;
     const int nchunks = (N + kFusedChunk - 1) / kFusedChunk;
     const size_t lds = fused_lds_bytes(T, k, E);
-    FusedFn fn = fused_for(k);
+    // an empty batch only writes zero counts and offsets: any instance does
+    FusedFn fn = fused_for(T > 0 ? k : 1);
+    if (!fn) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
       hipError_t e = allow_dynamic_lds((const void*)fn, lds);
       if (e != hipSuccess) return e;

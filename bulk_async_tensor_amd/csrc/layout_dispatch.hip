@@ -99,14 +99,13 @@ __global__ __launch_bounds__(kLdThreads) void layout_dispatch_kernel(
     }
   }
   if (blockIdx.x == 0) {
-    for (int t = tid; t < T; t += kLdThreads) {
-      const int32_t* r = ids + t * k;
-      for (int j = 1; j < k; ++j) {
-        const int v = r[j];
-        if ((unsigned)v >= (unsigned)E) continue;
-        for (int j2 = 0; j2 < j; ++j2)
-          if (r[j2] == v) bad |= kStatusDuplicate;
-      }
+    // repeated expert inside one token: every entry against the earlier
+    // entries of its token, entries spread over all threads
+    for (int i = tid; i < N; i += kLdThreads) {
+      const int v = ids[i];
+      if ((unsigned)v >= (unsigned)E) continue;
+      for (int i2 = i - i % k; i2 < i; ++i2)
+        if (ids[i2] == v) bad |= kStatusDuplicate;
     }
   }
   if (bad) atomicOr(&s_status, bad);
