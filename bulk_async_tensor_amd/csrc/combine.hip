@@ -551,17 +551,22 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   return hipSuccess;
 }
 
-// The phase kernel is the default on at least half the device when the
-// batch gives most waves of a full grid a unit: it reads all rows of its
-// unit before its first store, so a wave with little work gains nothing
-// (decode batches stay on the register kernel), and on fewer CUs the
-// per-CU read rate, not the read/write turnaround, is the bound.
+// The phase kernel is the default at k = 6 and 8 on at least half the
+// device when each of its launches gives most waves of a full grid a unit:
+// it reads all rows of its unit before its first store, so a wave with
+// little work gains nothing (decode batches stay on the register kernel),
+// and on fewer CUs the per-CU read rate, not the read/write turnaround, is
+// the bound.  At k = 2 and 4 a unit holds too few rows to keep the reads in
+// flight: measured at H = 7168 on 256 CUs, the register kernel is 11-20%
+// faster there (k = 4, T = 8192: 5.49 against 4.89 TB/s), and at k = 6 too
+// when the batch splits into launches of under three quarters of the grid
+// (T = 5461: 5.50 against 4.42).
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
-  if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
+  if (!(k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (2 * cus < b.all_cus) return false;
   const PhaseShape ps = combine_phase_shape(row_vec, combine_phase_seg(b, row_vec), cus, b.all_cus);
-  const int64_t units = phase_units(ps, T);
+  const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
   return units * 4 >= (int64_t)cus * ps.wpg * 3;
 }
 

@@ -610,12 +610,14 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   int wpg, grid;
   size_t lds_bytes;
   // With no budget set, a large dispatch still runs as a persistent grid on
-  // kWriteCus CUs: its traffic is 8/9 writes, and HBM write throughput was
-  // measured highest with about a quarter of the CUs issuing them (more add
-  // contention, not bandwidth).  Small batches keep the ordinary grid, whose
+  // dispatch_write_cus(k) CUs: at k = 8 its traffic is 8/9 writes, and HBM
+  // write throughput was measured highest with about a quarter of the CUs
+  // issuing them (more add contention, not bandwidth); smaller k carry more
+  // reads and take more CUs.  Small batches keep the ordinary grid, whose
   // start-up is cheaper.
   int budget = b.num_cus;
-  if (budget == 0 && units >= kWriteCus * 16 * 2) budget = kWriteCus;
+  const int write_cus = dispatch_write_cus(k);
+  if (budget == 0 && units >= write_cus * 16 * 2) budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W
     // slabs each; always a persistent grid (one workgroup per CU)

@@ -23,9 +23,15 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr size_t kExclusiveLds = 80 * 1024 + 1024;
 
 // A large dispatch runs as a persistent grid on this many CUs when no budget
-// is set: its traffic is 8/9 writes, and HBM write throughput was measured
-// highest with about a quarter of the CUs issuing them.
+// is set: at k = 8 its traffic is 8/9 writes, and HBM write throughput was
+// measured highest with about a quarter of the CUs issuing them.
 constexpr int kWriteCus = 64;
+
+// The default persistent budget by k.  The share of reads grows as k falls
+// (1/(1+k) of the bytes), and reads need more CUs in flight to hide their
+// latency: measured at H = 7168, 64 CUs stay best for k >= 5, 96 for
+// k = 2..4 (k = 2: 7.0 against 5.7 TB/s on 64) and 128 for k = 1.
+inline int dispatch_write_cus(int k) { return k >= 5 ? kWriteCus : k >= 2 ? 96 : 128; }
 
 // Largest k the kernels accept (the ABI's EP_MAX_TOPK).
 constexpr int kMaxK = 32;

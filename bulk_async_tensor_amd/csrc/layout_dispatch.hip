@@ -450,12 +450,14 @@ WidePlan wide_plan(const Budget& b, int T, int k, int E, int H) {
   const int row_vec = H / 8;
   p.vpl = dispatch_slab_vpl(row_vec, 8, b.slab_vpl);
   p.nslab = (row_vec + p.vpl * kWave - 1) / (p.vpl * kWave);
-  // With no budget: the dispatch's 64 CUs for large batches (its traffic is
-  // mostly writes, which peak there); smaller batches spread over 128 CUs,
-  // where a copy phase of a few microseconds gains from more CUs (T = 128 at
-  // H = 7168: 7.2 against 8.4 us on 64 CUs; T = 1024: 27.1 against 28.0 us).
+  // With no budget: the dispatch's CUs for large batches (64 at k >= 6,
+  // whose traffic is mostly writes, which peak there; 96 at k = 2 and 4);
+  // smaller batches spread over 128 CUs, where a copy phase of a few
+  // microseconds gains from more CUs (T = 128 at H = 7168: 7.2 against
+  // 8.4 us on 64 CUs; T = 1024: 27.1 against 28.0 us).
   const int64_t units = (int64_t)T * p.nslab;
-  int cus = b.num_cus > 0 ? b.num_cus : (units >= (int64_t)kWriteCus * 16 * 4 ? kWriteCus : 2 * kWriteCus);
+  const int write_cus = dispatch_write_cus(k);
+  int cus = b.num_cus > 0 ? b.num_cus : (units >= (int64_t)write_cus * 16 * 4 ? write_cus : 2 * kWriteCus);
   if (cus > b.device_cus) cus = b.device_cus;
   p.tpg = (T + cus - 1) / cus;
   p.grid = (T + p.tpg - 1) / p.tpg;  // every workgroup owns at least one token

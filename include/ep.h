@@ -71,13 +71,15 @@ enum {
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
  * launch.  n == 0: no budget; the library picks the launch per kernel --
  * an ordinary grid over the whole device, except that a dispatch of at
- * least 2048 work units runs persistent on 64 CUs (its traffic is 8/9
- * writes, and HBM write throughput peaks with about a quarter of the CUs
- * issuing them).  The initial value comes from the environment variable
- * EP_NUM_CUS (default 0).
+ * least 32 work units per CU of its default budget runs persistent on
+ * that budget: 64 CUs for k >= 5 (at k = 8 its traffic is 8/9 writes, and
+ * HBM write throughput peaks with about a quarter of the CUs issuing
+ * them), 96 for k = 2..4 and 128 for k = 1, whose larger read share needs
+ * more CUs in flight.  The initial value comes from the environment
+ * variable EP_NUM_CUS (default 0).
  * On a CU-masked stream (ep_stream_create_cu_masked, or any stream whose
  * mask hipExtStreamGetCUMask reports) every launch counts only the CUs of
- * the mask: n and the 64-CU dispatch budget are clamped to them, ordinary
+ * the mask: n and the default dispatch budget are clamped to them, ordinary
  * grids are sized for them, and the kernel choices that depend on the CU
  * count (the phased combine needs at least half the device) use them.
  * Returns EP_OK, or EP_ERR_INVALID_ARG for n < 0 or n > 4096.
@@ -96,11 +98,16 @@ int ep_get_num_cus(void);
  *           one stage;
  *   "lds2"  the same with two stages per wave: the next unit's
  *           direct-to-LDS load is in flight while the current one is stored;
- *   "phase" (combine; dispatch takes its default) each wave sums up to 16
- *           KiB of output rows in registers and stores them only after all
- *           their source rows are read: with one such unit per wave the
- *           whole grid reads first and writes last.  k must be 2, 4, 6 or 8,
- *           else the any-k register kernel runs;
+ *   "phase" reads before writes, per wave: for combine each wave sums up
+ *           to 16 KiB of output rows (28 KiB in 8-wave workgroups) in
+ *           registers and stores them only after all their source rows are
+ *           read; for dispatch each wave loads up to 16 KiB of x rows into
+ *           registers, then writes their k copies.  With one such unit per
+ *           wave the whole grid reads first and writes last.  k must be 2,
+ *           4, 6 or 8, else combine runs the any-k register kernel and
+ *           dispatch lds1.  "auto" picks it for combine at k = 6 and 8 on at
+ *           least half the device when each launch fills three quarters of
+ *           a full grid;
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
  *           the next two units' direct-to-LDS loads are in flight while the
  *           current one is stored (fewer waves fit a CU);
