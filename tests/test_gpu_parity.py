@@ -251,6 +251,22 @@ def run_combine(wl, y_u16, dest_row_np):
     return from_dev_bf16(out)
 
 
+# The default launches depend on k: the dispatch's persistent budget (128 CUs
+# at k = 1, 96 at k = 2..4, 64 from k = 5) and the combine's choice between
+# the phased and the register kernel (by k and by how full each phased launch
+# would be).  Each k runs once at a size that takes the persistent dispatch,
+# with the per-expert scale as the expert.
+@pytest.mark.parametrize("k,T", [(1, 4500), (2, 3100), (3, 3000), (4, 2500), (5, 2100), (6, 5461), (8, 4500)])
+def test_default_launch_across_k(k, T):
+    wl = make_workload("train", seed=40 + k, T=T, k=k)
+    lay = oracle.layout(wl.topk_idx, wl.config.E)
+    R = T * k
+    ref_recv = oracle.dispatch(wl.x, lay["dest_row"], R)
+    np.testing.assert_array_equal(run_dispatch(wl, lay["dest_row"], R), ref_recv)
+    y = oracle.expert_scale(ref_recv, lay["offsets"], wl.scales)
+    assert_combine_close(run_combine(wl, y, lay["dest_row"]), oracle.combine(y, lay["dest_row"], wl.topk_w))
+
+
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_combine_full_size(name):
     wl = workload(name)
@@ -657,7 +673,8 @@ def test_layout_dispatch_flags_bad_ids():
 # rounds in one workgroup (the 24-CU budget at the training shape: 171
 # tokens x 8 = 1368 entries per workgroup).  The last cases fall outside the
 # wide path (k = 1 or 3, E = 1 or 64 or 300, past 64 Ki entries) and take the
-# two separate launches.
+# two separate launches.  The two after them are large enough at k = 2 and 4
+# for the default budget of those k (96 CUs).
 WIDE_CASES = [
     ("train", {}),
     ("train", dict(T=129)),
@@ -672,6 +689,8 @@ WIDE_CASES = [
     ("prefill", dict(T=2048, H=2056, E=1, k=1)),
     ("prefill", dict(T=2000, H=1024, E=64, k=3)),
     ("train", dict(T=400, H=1024, E=300, k=8)),
+    ("train", dict(T=6200, k=2)),
+    ("train", dict(T=4000, k=4)),
 ]
 
 
