@@ -48,6 +48,8 @@ def parse_args():
     p.add_argument("--sweep-budgets", default="16,24,32,64,128,256,0")
     p.add_argument("--sweep-variants", default="vgpr,vgpr2,lds1,lds2,vgpr_cached")
     p.add_argument("--sweep-slabs", default="0", help="slab sizes (vectors per lane) to sweep; 0 = default")
+    p.add_argument("--shape", default=None,
+                   help="sweep only: override the workload's sizes, e.g. k=2,T=16384 (keys T, H, E, k)")
     p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
     p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
     p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
@@ -66,7 +68,7 @@ def parse_args():
 class Setup:
     """Device buffers of one workload and the step that runs on them."""
 
-    def __init__(self, name, stream=None):
+    def __init__(self, name, stream=None, shape=None):
         import numpy as np
         import torch
 
@@ -79,7 +81,7 @@ class Setup:
         self.gather = False  # True: dispatch through ep_dispatch_rows (gather form)
         self.fused = False   # True: layout and dispatch through ep_layout_dispatch
         dev = torch.device("cuda:0")
-        wl = make_workload(name)
+        wl = make_workload(name, **(shape or {}))
         self.wl = wl
         c = self.cfg = wl.config
         self.T, self.H, self.E, self.k = c.T, c.H, c.E, c.k
@@ -574,13 +576,26 @@ def parse_budget(tok):
     return "grid", int(tok)
 
 
-def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
+def parse_shape(text):
+    """"k=2,T=16384" -> {"k": 2, "T": 16384}: size overrides of a named workload."""
+    if not text:
+        return {}
+    out = {}
+    for item in text.split(","):
+        key, _, val = item.partition("=")
+        if key not in ("T", "H", "E", "k") or not val.isdigit():
+            raise SystemExit(f"bench.py: bad --shape item {item!r} (keys T, H, E, k with integer values)")
+        out[key] = int(val)
+    return out
+
+
+def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True, shape=None):
     """CU budget x variant x slab over the workload, plus the streaming-probe ceilings."""
     import torch
 
     import bulk_async_tensor_amd as ep
 
-    s = Setup(name)
+    s = Setup(name, shape=shape)
     n = 1 << 30
     ndev = torch.cuda.get_device_properties(0).multi_processor_count
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
@@ -633,7 +648,8 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True):
                     writes = [ceiling[m] for m in ("write", "write32") if m in ceiling]
                     ref = {"dispatch": max(writes) if writes else None,
                            "combine": ceiling.get("mix8to1_phase_once")}
-                    rec = {"kind": "step", "workload": name, "seed": s.wl.seed, "variant": v, "slab": slab,
+                    rec = {"kind": "step", "workload": name, "seed": s.wl.seed,
+                           "shape": {"T": s.T, "H": s.H, "E": s.E, "k": s.k}, "variant": v, "slab": slab,
                            "num_cus": str(tok), "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3),
                            "kernel_ms": per, "kernel_timing": getattr(s, "kernel_timing", None), "GBs": gbs,
                            "frac_of_hbm_peak": {k: (g / HBM_PEAK_GBS if g else None) for k, g in gbs.items()},
@@ -900,8 +916,10 @@ def main():
         return
     if args.sweep:
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
-              [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes)
+              [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes, shape=parse_shape(args.shape))
         return
+    if args.shape:
+        raise SystemExit("bench.py: --shape applies to --sweep only; the benchmark line runs the named workload")
 
     ep.ep_set_variant(args.variant)
     s = Setup(args.workload)

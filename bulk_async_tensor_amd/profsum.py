@@ -4,6 +4,10 @@
       kernel-trace statistics of our kernels beside the per-launch times the
       benchmark measured with HIP events in the same run.
 
+  python -m bulk_async_tensor_amd.profsum sweep <sweep.jsonl>... --title "..." --command "..."
+      the step records of bench.py --sweep files as one table (dispatch and
+      combine GB/s per shape, variant and CU budget).
+
   python -m bulk_async_tensor_amd.profsum hbm <fetch_counter_collection.csv> <write_counter_collection.csv>
           --kernel dispatch|combine|layout|layout_dispatch --workload NAME --out FILE --command "..."
       HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
@@ -150,6 +154,27 @@ def sq(args):
     sys.stdout.write("\n".join(out) + "\n")
 
 
+def sweep_table(args):
+    """Step records of `bench.py --sweep` files as one table: dispatch and
+    combine GB/s per shape, variant and CU budget (0: the default launch)."""
+    out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [
+        "# GB/s are algorithmic bytes over the HIP-event time per launch; CUs 0 = the library's default launch", "",
+        f"{'k':>2s} {'T':>6s} {'H':>5s} {'E':>4s} {'variant':<8s} {'CUs':>4s} {'dispatch GB/s':>14s} "
+        f"{'combine GB/s':>13s}"]
+    for path in args.jsonl:
+        for line in open(path):
+            r = json.loads(line)
+            if r.get("kind") != "step":
+                continue
+            sh = r.get("shape") or {}
+            g = r.get("GBs") or {}
+            cell = lambda v, w: f"{v:{w}.0f}" if v else f"{'-':>{w}s}"
+            out.append(f"{sh.get('k', 0):2d} {sh.get('T', 0):6d} {sh.get('H', 0):5d} {sh.get('E', 0):4d} "
+                       f"{r['variant']:<8s} {r['num_cus']:>4s} {cell(g.get('dispatch'), 14)} "
+                       f"{cell(g.get('combine'), 13)}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="mode", required=True)
@@ -175,8 +200,12 @@ def main(argv=None):
     q.add_argument("--command", default="")
     q.add_argument("--xcds", type=int, default=8)
     q.add_argument("--cus", type=int, default=256)
+    w = sub.add_parser("sweep")
+    w.add_argument("jsonl", nargs="+")
+    w.add_argument("--title", default="")
+    w.add_argument("--command", action="append", default=[])
     args = p.parse_args(argv)
-    {"trace": trace, "hbm": hbm, "sq": sq}[args.mode](args)
+    {"trace": trace, "hbm": hbm, "sq": sq, "sweep": sweep_table}[args.mode](args)
 
 
 if __name__ == "__main__":
