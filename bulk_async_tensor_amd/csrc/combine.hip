@@ -464,25 +464,29 @@ __global__ __launch_bounds__(MAXT) void combine_phase_kernel(const u32x4* __rest
 using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int, int, int,
                          int);
 
-template <int SEG, int G, int HELD, bool EVEN, int MAXT = kPhaseWpg * kWave>
+// Slots per register set: with single-vector runs, two equal sets of k/2
+// (k = 6 in sets of 4 and 2 ran 6-10% slower than in two sets of 3 at
+// H = 7168: 139.9 against 129.3 us at T = 8192); with 2-vector runs, sets of
+// 2 slots (4 KiB per wave).  (Runs of 4 vectors do not fit: two sets plus 32
+// accumulators and the held output spill at k >= 6.)
+constexpr int phase_set_slots(int k, int seg) { return seg == 1 ? k / 2 : 2; }
+
+template <int SEG, int HELD, bool EVEN, int MAXT = kPhaseWpg * kWave>
 PhaseFn pick_phase_k(int k) {
   switch (k) {
-    case 2: return combine_phase_kernel<2, SEG, G, HELD, EVEN, MAXT>;
-    case 4: return combine_phase_kernel<4, SEG, G, HELD, EVEN, MAXT>;
-    case 6: return combine_phase_kernel<6, SEG, G, HELD, EVEN, MAXT>;
-    case 8: return combine_phase_kernel<8, SEG, G, HELD, EVEN, MAXT>;
+    case 2: return combine_phase_kernel<2, SEG, phase_set_slots(2, SEG), HELD, EVEN, MAXT>;
+    case 4: return combine_phase_kernel<4, SEG, phase_set_slots(4, SEG), HELD, EVEN, MAXT>;
+    case 6: return combine_phase_kernel<6, SEG, phase_set_slots(6, SEG), HELD, EVEN, MAXT>;
+    case 8: return combine_phase_kernel<8, SEG, phase_set_slots(8, SEG), HELD, EVEN, MAXT>;
     default: return nullptr;
   }
 }
 
-// Register sets of 4 KiB per wave whatever the contiguous run: SEG x G = 4.
-// (Runs of 4 vectors do not fit: two sets plus 32 accumulators and the held
-// output spill at k >= 6.)
 template <bool EVEN>
 PhaseFn pick_phase(int seg_vec, int held, int k) {
-  if (held == kPhaseWideHeld) return pick_phase_k<1, 4, kPhaseWideHeld, EVEN, kPhaseWideWpg * kWave>(k);
-  if (seg_vec == 2) return held == 14 ? pick_phase_k<2, 2, 14, EVEN>(k) : pick_phase_k<2, 2, 16, EVEN>(k);
-  return held == 14 ? pick_phase_k<1, 4, 14, EVEN>(k) : pick_phase_k<1, 4, 16, EVEN>(k);
+  if (held == kPhaseWideHeld) return pick_phase_k<1, kPhaseWideHeld, EVEN, kPhaseWideWpg * kWave>(k);
+  if (seg_vec == 2) return held == 14 ? pick_phase_k<2, 14, EVEN>(k) : pick_phase_k<2, 16, EVEN>(k);
+  return held == 14 ? pick_phase_k<1, 14, EVEN>(k) : pick_phase_k<1, 16, EVEN>(k);
 }
 
 // Vectors per contiguous read of the phased combine: 1 by default (runs of
