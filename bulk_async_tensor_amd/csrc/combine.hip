@@ -489,12 +489,18 @@ PhaseFn pick_phase(int seg_vec, int held, int k) {
   return held == 14 ? pick_phase_k<1, 14, EVEN>(k) : pick_phase_k<1, 16, EVEN>(k);
 }
 
-// Vectors per contiguous read of the phased combine: 1 by default (runs of
-// 2 measured 5% slower at the train shape: fewer slots in flight); a
-// requested slab of 2 takes runs of 2 where a step can.
-int combine_phase_seg(const Budget& b, int row_vec) {
+// Vectors per contiguous read of the phased combine, where a step can take
+// runs of 2 (one row per unit, or an even row length): by default 1 at
+// k >= 6 (runs of 2 measured 5% slower at the train shape: fewer slots in
+// flight) and 2 at k <= 4, where a step of single vectors has too few loads
+// to keep in flight (H = 7168, T k = 32 Ki: 5.82 against 4.91 TB/s at
+// k = 4, 5.73 against 4.87 at k = 2); a requested slab of 1 or of 2 and
+// more takes 1 or 2.
+int combine_phase_seg(const Budget& b, int row_vec, int k) {
   const PhaseShape p16 = phase_shape(row_vec);
-  return (b.slab_vpl >= 2 && (p16.tpu == 1 || p16.nv % 2 == 0)) ? 2 : 1;
+  const bool can2 = p16.tpu == 1 || p16.nv % 2 == 0;
+  const bool want2 = b.slab_vpl >= 2 || (b.slab_vpl == 0 && k <= 4);
+  return want2 && can2 ? 2 : 1;
 }
 
 // With every CU of the device, rows of 9 to 14 vectors per lane (H from
@@ -520,7 +526,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   const bool even = row_vec % kWave == 0;
   // 14 held vectors when a unit never needs more (whole tokens at H = 7168
   // in the 16-wave shape), which frees registers for the reads
-  const int seg_vec = combine_phase_seg(b, row_vec);
+  const int seg_vec = combine_phase_seg(b, row_vec, k);
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
@@ -555,21 +561,23 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   return hipSuccess;
 }
 
-// The phase kernel is the default at k = 6 and 8 on at least half the
-// device when each of its launches gives most waves of a full grid a unit:
-// it reads all rows of its unit before its first store, so a wave with
-// little work gains nothing (decode batches stay on the register kernel),
-// and on fewer CUs the per-CU read rate, not the read/write turnaround, is
-// the bound.  At k = 2 and 4 a unit holds too few rows to keep the reads in
-// flight: measured at H = 7168 on 256 CUs, the register kernel is 11-20%
-// faster there (k = 4, T = 8192: 5.49 against 4.89 TB/s), and at k = 6 too
-// when the batch splits into launches of under three quarters of the grid
-// (T = 5461: 5.50 against 4.42).
+// The phase kernel is the default on at least half the device when each
+// of its launches gives most waves of a full grid a unit: it reads all rows
+// of its unit before its first store, so a wave with little work gains
+// nothing (decode batches stay on the register kernel), and on fewer CUs
+// the per-CU read rate, not the read/write turnaround, is the bound.  At
+// k = 6 a batch that splits into launches of under three quarters of the
+// grid ran slower than the register kernel (T = 5461 at H = 7168: 4.42
+// against 5.50 TB/s).  At k = 2 and 4 it needs runs of 2 vectors per read
+// (see combine_phase_seg): with single vectors the register kernel was
+// 11-20% faster there.
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
-  if (!(k == 6 || k == 8)) return false;
+  if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (2 * cus < b.all_cus) return false;
-  const PhaseShape ps = combine_phase_shape(row_vec, combine_phase_seg(b, row_vec), cus, b.all_cus);
+  const int seg_vec = combine_phase_seg(b, row_vec, k);
+  if (k <= 4 && seg_vec != 2) return false;
+  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
   return units * 4 >= (int64_t)cus * ps.wpg * 3;
 }

@@ -156,10 +156,12 @@ def sq(args):
 
 def sweep_table(args):
     """Step records of `bench.py --sweep` files as one table: dispatch and
-    combine GB/s per shape, variant and CU budget (0: the default launch)."""
+    combine GB/s per shape, variant, slab setting (0: the kernels' default)
+    and CU budget (0: the default launch)."""
     out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [
-        "# GB/s are algorithmic bytes over the HIP-event time per launch; CUs 0 = the library's default launch", "",
-        f"{'k':>2s} {'T':>6s} {'H':>5s} {'E':>4s} {'variant':<8s} {'CUs':>4s} {'dispatch GB/s':>14s} "
+        "# GB/s are algorithmic bytes over the HIP-event time per launch; slab 0 = the kernels' default; "
+        "CUs 0 = the library's default launch", "",
+        f"{'k':>2s} {'T':>6s} {'H':>5s} {'E':>4s} {'variant':<8s} {'slab':>4s} {'CUs':>4s} {'dispatch GB/s':>14s} "
         f"{'combine GB/s':>13s}"]
     for path in args.jsonl:
         for line in open(path):
@@ -170,7 +172,7 @@ def sweep_table(args):
             g = r.get("GBs") or {}
             cell = lambda v, w: f"{v:{w}.0f}" if v else f"{'-':>{w}s}"
             out.append(f"{sh.get('k', 0):2d} {sh.get('T', 0):6d} {sh.get('H', 0):5d} {sh.get('E', 0):4d} "
-                       f"{r['variant']:<8s} {r['num_cus']:>4s} {cell(g.get('dispatch'), 14)} "
+                       f"{r['variant']:<8s} {r.get('slab', 0):4d} {r['num_cus']:>4s} {cell(g.get('dispatch'), 14)} "
                        f"{cell(g.get('combine'), 13)}")
     sys.stdout.write("\n".join(out) + "\n")
 

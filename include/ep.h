@@ -105,9 +105,10 @@ int ep_get_num_cus(void);
  *           registers, then writes their k copies.  With one such unit per
  *           wave the whole grid reads first and writes last.  k must be 2,
  *           4, 6 or 8, else combine runs the any-k register kernel and
- *           dispatch lds1.  "auto" picks it for combine at k = 6 and 8 on at
- *           least half the device when each launch fills three quarters of
- *           a full grid;
+ *           dispatch lds1.  "auto" picks it for combine on at least half
+ *           the device when each launch fills three quarters of a full grid
+ *           (at k = 2 and 4 reading runs of 2 vectors per source row, where
+ *           the row allows them);
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
  *           the next two units' direct-to-LDS loads are in flight while the
  *           current one is stored (fewer waves fit a CU);

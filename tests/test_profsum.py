@@ -69,17 +69,17 @@ def test_sweep_table_lists_step_records(tmp_path, capsys):
 
     path = tmp_path / "s.jsonl"
     recs = [{"kind": "probe", "mode": "write", "GBs": 5000.0},
-            {"kind": "step", "shape": {"T": 16384, "H": 7168, "E": 256, "k": 2}, "variant": "lds1", "num_cus": "96",
+            {"kind": "step", "shape": {"T": 16384, "H": 7168, "E": 256, "k": 2}, "variant": "lds1", "slab": 0, "num_cus": "96",
              "GBs": {"layout": 40.0, "dispatch": 7012.4, "combine": 5401.0}},
-            {"kind": "step", "shape": {"T": 128, "H": 7168, "E": 256, "k": 8}, "variant": "vgpr", "num_cus": "0",
+            {"kind": "step", "shape": {"T": 128, "H": 7168, "E": 256, "k": 8}, "variant": "vgpr", "slab": 2, "num_cus": "0",
              "GBs": {"layout": 40.0, "dispatch": None, "combine": 812.0}}]
     path.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
     profsum.main(["sweep", str(path), "--title", "t", "--command", "c1", "--command", "c2"])
     out = capsys.readouterr().out.splitlines()
     assert out[:3] == ["# t", "# command: c1", "# command: c2"]
     rows = [line.split() for line in out if line and line[0] != "#" and not line.lstrip().startswith("k ")]
-    assert rows == [["2", "16384", "7168", "256", "lds1", "96", "7012", "5401"],
-                    ["8", "128", "7168", "256", "vgpr", "0", "-", "812"]]
+    assert rows == [["2", "16384", "7168", "256", "lds1", "0", "96", "7012", "5401"],
+                    ["8", "128", "7168", "256", "vgpr", "2", "0", "-", "812"]]
 
 
 def test_bench_shape_overrides():
