@@ -638,6 +638,13 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   const bool single = (v == Variant::Vgpr || v == Variant::VgprCached);
   int vpl = single ? 2 : 1;
   if (single && b.slab_vpl > 0) vpl = b.slab_vpl >= 4 ? 4 : b.slab_vpl >= 2 ? 2 : 1;
+  // A batch too small to give every CU of an ordinary grid four waves at 2
+  // vectors per lane (decode) takes 1-vector slabs: twice the waves, each
+  // with half the work (T = 128, H = 7168, k = 8: 4.08 against 3.71 TB/s;
+  // at T = 1024 the 2-vector slabs stay ahead, 6.02 against 5.81).
+  if (single && b.slab_vpl == 0 && b.num_cus == 0 &&
+      (int64_t)T * ((row_vec + 2 * kWave - 1) / (2 * kWave)) < 4 * (int64_t)b.device_cus)
+    vpl = 1;
   if (row_vec <= kWave) vpl = 1;
   const int max_wpg = (single && vpl >= 4) ? 8 : 16;
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
