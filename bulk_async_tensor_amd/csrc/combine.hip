@@ -562,15 +562,15 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
 }
 
 // The phase kernel is the default on at least half the device when each
-// of its launches gives most waves of a full grid a unit: it reads all rows
-// of its unit before its first store, so a wave with little work gains
-// nothing (decode batches stay on the register kernel), and on fewer CUs
-// the per-CU read rate, not the read/write turnaround, is the bound.  At
-// k = 6 a batch that splits into launches of under three quarters of the
-// grid ran slower than the register kernel (T = 5461 at H = 7168: 4.42
-// against 5.50 TB/s).  At k = 2 and 4 it needs runs of 2 vectors per read
-// (see combine_phase_seg): with single vectors the register kernel was
-// 11-20% faster there.
+// of its launches gives at least two thirds of the waves of a full grid a
+// unit: it reads all rows of its unit before its first store, so a wave
+// with little work gains nothing (decode batches stay on the register
+// kernel), and on fewer CUs the per-CU read rate, not the read/write
+// turnaround, is the bound.  Measured at H = 7168 on 256 CUs: launches of
+// 61-63% of the grid ran 7-10% slower than the register kernel at k = 2, 6
+// and 8, and of 67-73% 2-4% faster at k = 4, 6 and 8.  At k = 2 and 4 it
+// needs runs of 2 vectors per read (see combine_phase_seg): with single
+// vectors the register kernel was 11-20% faster there.
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
@@ -579,7 +579,7 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (k <= 4 && seg_vec != 2) return false;
   const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
-  return units * 4 >= (int64_t)cus * ps.wpg * 3;
+  return units * 3 >= (int64_t)cus * ps.wpg * 2;
 }
 
 using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);

@@ -106,7 +106,7 @@ int ep_get_num_cus(void);
  *           wave the whole grid reads first and writes last.  k must be 2,
  *           4, 6 or 8, else combine runs the any-k register kernel and
  *           dispatch lds1.  "auto" picks it for combine on at least half
- *           the device when each launch fills three quarters of a full grid
+ *           the device when each launch fills two thirds of a full grid
  *           (at k = 2 and 4 reading runs of 2 vectors per source row, where
  *           the row allows them);
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
