@@ -645,6 +645,11 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   if (single && b.slab_vpl == 0 && b.num_cus == 0 &&
       (int64_t)T * ((row_vec + 2 * kWave - 1) / (2 * kWave)) < 4 * (int64_t)b.device_cus)
     vpl = 1;
+  // On a CU budget, k = 2..7 read 4 vectors per lane per slot (8 waves per
+  // CU): H = 7168, k = 3 and 5 on 24 CUs 1.25 and 1.30 against 1.14 and
+  // 1.17 TB/s, k = 4 on 64 CUs 3.15 against 3.00; k = 1 and 8 keep 2
+  // (4-vector slabs cost them 3-10%).
+  if (single && b.slab_vpl == 0 && b.num_cus > 0 && k >= 2 && k <= 7) vpl = 4;
   if (row_vec <= kWave) vpl = 1;
   const int max_wpg = (single && vpl >= 4) ? 8 : 16;
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
