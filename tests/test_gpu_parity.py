@@ -337,6 +337,26 @@ def test_combine_phase_units(H, T, budget):
     assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
 
 
+# At k = 2 and 4 the phase kernel reads runs of 2 vectors per source row
+# where a step allows them: several tokens per unit (H = 2048), one row per
+# unit with an odd vector count (4104 ragged: 9 vectors, the last step half
+# used), a row split into segments of odd length (8712 ragged: 2 x 9) or
+# even length (16384: 2 x 16), and single vectors where neither fits (H = 8).
+@pytest.mark.parametrize("H", [8, 2048, 4104, 7168, 8712, 16384])
+@pytest.mark.parametrize("T", [29, 300])
+@pytest.mark.parametrize("k", [2, 4])
+@pytest.mark.parametrize("budget", [0, 24])
+def test_combine_phase_runs_of_two(H, T, k, budget):
+    ep.ep_set_variant("phase")
+    ep.ep_set_num_cus(budget)
+    wl = make_workload("combine_stress", seed=H + T + k, T=T, H=H, E=32, k=k)
+    lay = oracle.layout(wl.topk_idx, 32)
+    dest = lay["dest_row"].copy()
+    dest[T // 3, k - 1] = -1  # a slot that contributes nothing
+    got = run_combine(wl, wl.y, dest)
+    assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
+
+
 # Several launches per call: batches of whole two-row units on 256 or 128 CUs
 # (4096 or 2048 tokens per launch at H = 7168), with a ragged last batch.
 @pytest.mark.parametrize("T,budget", [(4097, 0), (8193, 0), (5000, 128), (2049, 192)])
