@@ -465,9 +465,9 @@ using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int
                          int);
 
 // Slots per register set: with single-vector runs, two equal sets of k/2
-// (k = 6 in sets of 4 and 2 ran 6-10% slower than in two sets of 3 at
-// H = 7168: 139.9 against 129.3 us at T = 8192); with 2-vector runs, sets of
-// 2 slots (4 KiB per wave).  (Runs of 4 vectors do not fit: two sets plus 32
+// (k = 6 in sets of 4 and 2 ran 3-10% slower than in two sets of 3 at
+// H = 7168, T = 8192: 139.5 against 135.0 us and 139.9 against 129.3 us in
+// two runs); with 2-vector runs, sets of 2 slots (4 KiB per wave).  (Runs of 4 vectors do not fit: two sets plus 32
 // accumulators and the held output spill at k >= 6.)
 constexpr int phase_set_slots(int k, int seg) { return seg == 1 ? k / 2 : 2; }
 
