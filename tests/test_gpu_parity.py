@@ -550,6 +550,33 @@ def test_step_on_masked_stream(n):
         ep.ep_stream_destroy(stream)
 
 
+def test_k4_step_on_masked_stream():
+    """k = 4 on a stream masked to 192 CUs: the one-launch layout + dispatch
+    on k = 4's default budget and the phased combine with 2-vector runs, in
+    launches sized for the mask.  Outputs equal the oracle's."""
+    stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(192)))
+    try:
+        wl = make_workload("train", seed=44, T=8192, k=4)
+        c = wl.config
+        ref = oracle.layout(wl.topk_idx, c.E)
+        R = c.T * c.k
+        ref_recv = oracle.dispatch(wl.x, ref["dest_row"], R)
+        y_np = oracle.expert_scale(ref_recv, ref["offsets"], wl.scales)
+        recv = torch.empty((R, c.H), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+        idx, x, w, y = to_dev(wl.topk_idx), to_dev_bf16(wl.x), to_dev(wl.topk_w), to_dev_bf16(y_np)
+        torch.cuda.synchronize()
+        lay = ep.ep_layout_dispatch(idx, c.E, x, recv, stream=stream)
+        ep.ep_combine(y, lay["dest_row"], w, out, stream=stream)
+        stream.synchronize()
+        check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+        np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
+        assert_combine_close(from_dev_bf16(out), oracle.combine(y_np, ref["dest_row"], wl.topk_w))
+    finally:
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(stream)
+
+
 @pytest.mark.parametrize("name", ["decode", "tiny"])
 def test_graph_replay_matches_eager(name):
     """The whole step captured in a HIP graph: every replay, with eager work
