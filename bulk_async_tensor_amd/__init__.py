@@ -99,17 +99,30 @@ def _check(rc, what):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it (NULL for None)
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
+def _stream(stream, t=None):
+    """The raw HIP stream: the given torch stream, else the current stream of
+    t's device (of the current device when t is None).  The raw accessor
+    skips building a torch.cuda.Stream object per call."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
 
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    dev = t.get_device() if t is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(dev)
 
 
 def _device_tensor(t, name, dtype=None):
+    # fast path for a valid argument (torch dtypes are singletons); the checks
+    # below give the error for anything else
+    try:
+        if t.is_cuda and t.is_contiguous() and (dtype is None or t.dtype is dtype):
+            return t
+    except (AttributeError, TypeError):
+        pass
     import torch
 
     if not isinstance(t, torch.Tensor):
@@ -183,13 +196,13 @@ def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, s
     else:
         _device_tensor(src_token, "src_token", torch.int32)
     status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
-    need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
     if workspace is None:
+        need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(
         lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
-                        _ptr(status), _ptr(workspace), ws_bytes, _stream(stream)),
+                        _ptr(status), _ptr(workspace), ws_bytes, _stream(stream, topk_idx)),
         "ep_layout",
     )
     return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
@@ -217,13 +230,13 @@ def ep_layout_dispatch(topk_idx, num_experts, x, recv, counts=None, offsets=None
     src_token = torch.empty(T * k, **i32) if src_token is None else _device_tensor(src_token, "src_token",
                                                                                    torch.int32)
     status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
-    need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
     if workspace is None:
+        need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(lib().ep_layout_dispatch(_ptr(topk_idx), T, k, E, _ptr(x), H, _ptr(counts), _ptr(offsets),
                                     _ptr(dest_row), _ptr(src_token), _ptr(status), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(recv), recv.shape[0],
-                                    _stream(stream)), "ep_layout_dispatch")
+                                    _stream(stream, x)), "ep_layout_dispatch")
     return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
 
 
@@ -240,7 +253,7 @@ def ep_dispatch(x, dest_row, recv, stream=None):
     if recv.dim() != 2 or recv.shape[1] != H:
         raise ValueError("recv must be [R, H]")
     k = dest_row.shape[1]
-    _check(lib().ep_dispatch(_ptr(x), T, H, _ptr(dest_row), k, _ptr(recv), recv.shape[0], _stream(stream)),
+    _check(lib().ep_dispatch(_ptr(x), T, H, _ptr(dest_row), k, _ptr(recv), recv.shape[0], _stream(stream, x)),
            "ep_dispatch")
     return recv
 
@@ -255,7 +268,7 @@ def ep_dispatch_rows(x, src_token, recv, stream=None):
     T, H = x.shape
     if recv.dim() != 2 or recv.shape[1] != H or src_token.numel() < recv.shape[0]:
         raise ValueError("recv must be [R, H] and src_token hold at least R entries")
-    _check(lib().ep_dispatch_rows(_ptr(x), T, H, _ptr(src_token), _ptr(recv), recv.shape[0], _stream(stream)),
+    _check(lib().ep_dispatch_rows(_ptr(x), T, H, _ptr(src_token), _ptr(recv), recv.shape[0], _stream(stream, x)),
            "ep_dispatch_rows")
     return recv
 
@@ -275,7 +288,7 @@ def ep_combine(y, dest_row, topk_w, out, stream=None):
         raise ValueError("y must be [R, H]")
     k = dest_row.shape[1]
     _check(lib().ep_combine(_ptr(y), y.shape[0], H, _ptr(dest_row), _ptr(topk_w), T, k, _ptr(out),
-                            _stream(stream)), "ep_combine")
+                            _stream(stream, out)), "ep_combine")
     return out
 
 
@@ -307,7 +320,7 @@ def ep_combine_reduce(y, src_token, dest_row, topk_w, out, workspace=None, strea
         _device_tensor(workspace, "workspace")
     _check(lib().ep_combine_reduce(_ptr(y), y.shape[0], H, _ptr(src_token), _ptr(dest_row), _ptr(topk_w), T, k,
                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _stream(stream)), "ep_combine_reduce")
+                                   _stream(stream, out)), "ep_combine_reduce")
     return out
 
 

@@ -838,3 +838,29 @@ def test_layout_dispatch_wide_is_deterministic():
         np.testing.assert_array_equal(o[0], outs[0][0])
         np.testing.assert_array_equal(o[1], outs[0][1])
         assert torch.equal(o[2], outs[0][2])
+
+
+def test_binding_rejects_bad_device_tensors():
+    """The binding's checks on device tensors: wrong dtype, non-contiguous
+    views and mismatched shapes raise before anything is launched."""
+    x = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    dest = torch.zeros((8, 2), dtype=torch.int32, device=DEV)
+    recv = torch.zeros((16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        ep.ep_dispatch(x.float(), dest, recv)
+    with pytest.raises(TypeError):
+        ep.ep_dispatch(x, dest.long(), recv)
+    with pytest.raises(ValueError):
+        ep.ep_dispatch(torch.zeros((64, 8), dtype=torch.bfloat16, device=DEV).t(), dest, recv)
+    with pytest.raises(ValueError):
+        ep.ep_dispatch(x, dest[:4], recv)
+    w = torch.zeros((8, 2), dtype=torch.float32, device=DEV)
+    out = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        ep.ep_combine(recv, dest, w.double(), out)
+    with pytest.raises(ValueError):
+        ep.ep_combine(recv, dest, w[:, :1], out)
+    with pytest.raises(ValueError):
+        ep.ep_layout(torch.zeros((2, 8), dtype=torch.int32, device=DEV).t(), 16)
+    ep.ep_dispatch(x, dest, recv)  # the valid call still works
+    torch.cuda.synchronize()
