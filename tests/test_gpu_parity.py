@@ -864,3 +864,50 @@ def test_binding_rejects_bad_device_tensors():
         ep.ep_layout(torch.zeros((2, 8), dtype=torch.int32, device=DEV).t(), 16)
     ep.ep_dispatch(x, dest, recv)  # the valid call still works
     torch.cuda.synchronize()
+
+
+def _random_cases(n, seed=2026):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        k = int(rng.integers(1, 11)) if rng.random() < 0.8 else int(rng.integers(11, 33))
+        E = int(rng.integers(max(k, 2), 300)) if rng.random() < 0.8 else int(rng.integers(max(k, 2), 1025))
+        H = 8 * int(rng.integers(1, 1125))
+        T = int(rng.integers(1, 3000))
+        if T * k * H * 2 > 96 << 20:  # keep the oracle to a few seconds
+            continue
+        cases.append(dict(name=str(rng.choice(["train", "prefill"])), T=T, H=H, E=E, k=k,
+                          budget=int(rng.choice([0, 0, 24, 64, 200])),
+                          variant=str(rng.choice(["auto", "auto", "lds1", "vgpr", "phase"])),
+                          one_launch=bool(rng.integers(0, 2))))
+    return cases
+
+
+# Seeded random shapes through the default and forced launches: layout and
+# dispatch bit-exact, combine against the oracle, with and without the
+# one-launch layout + dispatch.
+@pytest.mark.parametrize("case", _random_cases(100), ids=lambda c: "{name}-T{T}-H{H}-E{E}-k{k}-b{budget}-{variant}"
+                         .format(**c) + ("-one" if c["one_launch"] else ""))
+def test_random_shapes(case):
+    ep.ep_set_num_cus(case["budget"])
+    ep.ep_set_variant(case["variant"])
+    wl = make_workload(case["name"], seed=case["T"] + case["H"], T=case["T"], H=case["H"], E=case["E"],
+                       k=case["k"])
+    c = wl.config
+    ref = oracle.layout(wl.topk_idx, c.E)
+    R = c.T * c.k
+    ref_recv = oracle.dispatch(wl.x, ref["dest_row"], R)
+    recv = torch.full((R, c.H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    idx, x = to_dev(wl.topk_idx), to_dev_bf16(wl.x)
+    if case["one_launch"]:
+        lay = ep.ep_layout_dispatch(idx, c.E, x, recv)
+    else:
+        lay = ep.ep_layout(idx, c.E)
+        ep.ep_dispatch(x, lay["dest_row"], recv)
+    torch.cuda.synchronize()
+    check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+    np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
+    y = oracle.expert_identity(ref_recv) if wl.config.expert != "scale" else \
+        oracle.expert_scale(ref_recv, ref["offsets"], wl.scales)
+    got = run_combine(wl, y, ref["dest_row"])
+    assert_combine_close(got, oracle.combine(y, ref["dest_row"], wl.topk_w))
