@@ -907,6 +907,11 @@ def test_random_shapes(case):
     torch.cuda.synchronize()
     check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
     np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
+    # the gather form on the library's own src_token
+    recv.view(torch.int16).fill_(0x7E57)
+    ep.ep_dispatch_rows(x, lay["src_token"], recv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(from_dev_bf16(recv), ref_recv)
     y = oracle.expert_identity(ref_recv) if wl.config.expert != "scale" else \
         oracle.expert_scale(ref_recv, ref["offsets"], wl.scales)
     got = run_combine(wl, y, ref["dest_row"])
