@@ -49,7 +49,7 @@ def parse_args():
     p.add_argument("--sweep-variants", default="vgpr,vgpr2,lds1,lds2,vgpr_cached")
     p.add_argument("--sweep-slabs", default="0", help="slab sizes (vectors per lane) to sweep; 0 = default")
     p.add_argument("--shape", default=None,
-                   help="sweep only: override the workload's sizes, e.g. k=2,T=16384 (keys T, H, E, k)")
+                   help="--sweep and --kernels-only: override the workload's sizes, e.g. k=2,T=16384 (keys T, H, E, k)")
     p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
     p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
     p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
@@ -918,11 +918,12 @@ def main():
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
               [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes, shape=parse_shape(args.shape))
         return
-    if args.shape:
-        raise SystemExit("bench.py: --shape applies to --sweep only; the benchmark line runs the named workload")
+    if args.shape and not args.kernels_only:
+        raise SystemExit("bench.py: --shape applies to --sweep and --kernels-only; the benchmark line runs the "
+                         "named workload")
 
     ep.ep_set_variant(args.variant)
-    s = Setup(args.workload)
+    s = Setup(args.workload, shape=parse_shape(args.shape))
     s.fused = args.fused
     if args.kernels_only:
         kernels_only(s)
