@@ -735,6 +735,24 @@ def graph_step(s, steps, warmup):
         g.replay()
     torch.cuda.synchronize()
     ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+    # many steps per graph (a decode loop reusing its buffers): the graph
+    # launch is paid once per `per_graph` steps
+    per_graph = 16
+    gm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gm):
+        for _ in range(per_graph):
+            s.layout()
+            s.dispatch()
+            s.combine()
+    reps = max(1, steps // per_graph)
+    for _ in range(max(1, warmup // per_graph)):
+        gm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gm.replay()
+    torch.cuda.synchronize()
+    ms_graph_many = (time.perf_counter() - t0) * 1e3 / (reps * per_graph)
     t0 = time.perf_counter()
     for _ in range(steps):
         s.layout()
@@ -742,7 +760,7 @@ def graph_step(s, steps, warmup):
         s.combine()
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / steps
-    return ms_graph, ms_eager
+    return ms_graph, ms_eager, ms_graph_many, per_graph
 
 
 def kernels_only(s, launches=5, copy_bytes=256 << 20):
@@ -1036,10 +1054,12 @@ def main():
         line["combine_reduce"] = reduce_times(s, min(args.steps, 50),
                                               [0] if args.only_all else [0, args.budget])
     if args.graph:
-        ms_g, ms_e = graph_step(s, args.steps, args.warmup)
+        ms_g, ms_e, ms_m, per_graph = graph_step(s, args.steps, args.warmup)
         line["graph_replay"] = {"ms_per_step": round(ms_g, 5), "eager_ms_per_step": round(ms_e, 5),
                                 "value": round(s.step_bytes / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
-                                "tokens_per_s": round(s.T / (ms_g * 1e-3), 1)}
+                                "tokens_per_s": round(s.T / (ms_g * 1e-3), 1),
+                                "steps_per_graph": {"steps": per_graph, "ms_per_step": round(ms_m, 5),
+                                                    "tokens_per_s": round(s.T / (ms_m * 1e-3), 1)}}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, gpu=s)
         line["cpu_baseline"]["all_cores"] = cpu_baseline_parallel(args.workload, args.cpu_seconds / 2, pool,
