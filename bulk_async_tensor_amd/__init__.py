@@ -136,6 +136,32 @@ def _device_tensor(t, name, dtype=None):
     return t
 
 
+def _layout_outputs(T, k, E, dev, counts, offsets, dest_row, src_token, status):
+    """The layout's output tensors: the caller's, checked for dtype and for
+    room (the C ABI takes bare pointers and cannot), or new ones."""
+    import torch
+
+    i32 = dict(dtype=torch.int32, device=dev)
+
+    def given(t, name, need):
+        _device_tensor(t, name, torch.int32)
+        if t.numel() < need:
+            raise ValueError(f"{name} holds {t.numel()} int32, needs at least {need}")
+        return t
+
+    counts = torch.empty(E, **i32) if counts is None else given(counts, "counts", E)
+    offsets = torch.empty(E + 1, **i32) if offsets is None else given(offsets, "offsets", E + 1)
+    if dest_row is None:
+        dest_row = torch.empty((T, k), **i32)
+    else:
+        given(dest_row, "dest_row", T * k)
+        if tuple(dest_row.shape) != (T, k):
+            raise ValueError(f"dest_row must be [T, k] = [{T}, {k}], got {list(dest_row.shape)}")
+    src_token = torch.empty(T * k, **i32) if src_token is None else given(src_token, "src_token", T * k)
+    status = torch.empty(1, **i32) if status is None else given(status, "status", 1)
+    return counts, offsets, dest_row, src_token, status
+
+
 # ------------------------------------------------------------------ settings
 def ep_set_num_cus(n):
     return _check(lib().ep_set_num_cus(int(n)), "ep_set_num_cus")
@@ -184,21 +210,18 @@ def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, s
     import torch
 
     _device_tensor(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, k]")
     T, k = topk_idx.shape
     E = int(num_experts)
     dev = topk_idx.device
-    i32 = dict(dtype=torch.int32, device=dev)
-    counts = torch.empty(E, **i32) if counts is None else _device_tensor(counts, "counts", torch.int32)
-    offsets = torch.empty(E + 1, **i32) if offsets is None else _device_tensor(offsets, "offsets", torch.int32)
-    dest_row = torch.empty((T, k), **i32) if dest_row is None else _device_tensor(dest_row, "dest_row", torch.int32)
-    if src_token is None:
-        src_token = torch.empty(T * k, **i32)
-    else:
-        _device_tensor(src_token, "src_token", torch.int32)
-    status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
+    counts, offsets, dest_row, src_token, status = _layout_outputs(T, k, E, dev, counts, offsets, dest_row,
+                                                                   src_token, status)
     if workspace is None:
         need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _device_tensor(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(
         lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
@@ -217,22 +240,21 @@ def ep_layout_dispatch(topk_idx, num_experts, x, recv, counts=None, offsets=None
     _device_tensor(topk_idx, "topk_idx", torch.int32)
     _device_tensor(x, "x", torch.bfloat16)
     _device_tensor(recv, "recv", torch.bfloat16)
+    if topk_idx.dim() != 2 or x.dim() != 2:
+        raise ValueError("topk_idx must be [T, k] and x [T, H]")
     T, k = topk_idx.shape
     E = int(num_experts)
     H = x.shape[1]
     if x.shape[0] != T or recv.dim() != 2 or recv.shape[1] != H:
         raise ValueError("x must be [T, H] and recv [R, H]")
     dev = topk_idx.device
-    i32 = dict(dtype=torch.int32, device=dev)
-    counts = torch.empty(E, **i32) if counts is None else _device_tensor(counts, "counts", torch.int32)
-    offsets = torch.empty(E + 1, **i32) if offsets is None else _device_tensor(offsets, "offsets", torch.int32)
-    dest_row = torch.empty((T, k), **i32) if dest_row is None else _device_tensor(dest_row, "dest_row", torch.int32)
-    src_token = torch.empty(T * k, **i32) if src_token is None else _device_tensor(src_token, "src_token",
-                                                                                   torch.int32)
-    status = torch.empty(1, **i32) if status is None else _device_tensor(status, "status", torch.int32)
+    counts, offsets, dest_row, src_token, status = _layout_outputs(T, k, E, dev, counts, offsets, dest_row,
+                                                                   src_token, status)
     if workspace is None:
         need = ep_layout_workspace_bytes(T, k, E) if 1 <= k <= EP_MAX_TOPK and 1 <= E <= EP_MAX_EXPERTS else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _device_tensor(workspace, "workspace")
     _check(lib().ep_layout_dispatch(_ptr(topk_idx), T, k, E, _ptr(x), H, _ptr(counts), _ptr(offsets),
                                     _ptr(dest_row), _ptr(src_token), _ptr(status), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(recv), recv.shape[0],

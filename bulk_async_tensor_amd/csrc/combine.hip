@@ -622,11 +622,40 @@ CombineFn pick_vpl(Variant v, int vpl, int k) {
   }
 }
 
+// An empty receive buffer leaves every slot of every token out of range, and
+// the sum of no terms is +0.0: out is filled with zeros and y, which may then
+// be NULL, is never read.  (The phased kernel's loads are unconditional and
+// read row 0 for out-of-range slots, so it must not run on an empty buffer.)
+__global__ __launch_bounds__(1024) void combine_zero_kernel(u32x4* __restrict__ out, int64_t nvec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) st16<true>(out + i, z);
+}
+
+hipError_t launch_combine_zero(const Budget& b, void* out, int64_t nvec, hipStream_t stream) {
+  int grid;
+  size_t lds_bytes = 0;
+  if (b.num_cus > 0) {
+    // the budget's persistent grid: one workgroup per CU
+    grid = b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+    lds_bytes = kExclusiveLds;
+    hipError_t e = allow_dynamic_lds((const void*)combine_zero_kernel, lds_bytes);
+    if (e != hipSuccess) return e;
+  } else {
+    const int64_t want = (nvec + 1023) / 1024;
+    grid = (int)(want < (int64_t)b.device_cus * 4 ? want : (int64_t)b.device_cus * 4);
+  }
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(combine_zero_kernel, dim3(grid), dim3(1024), lds_bytes, stream, static_cast<u32x4*>(out), nvec);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t recv_rows, int H,
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream) {
   const int row_vec = H / 8;
+  if (recv_rows == 0) return launch_combine_zero(b, out, (int64_t)T * row_vec, stream);
   if (v == Variant::Lds3 || v == Variant::Pc) v = Variant::Auto;  // dispatch-only variants
   if (v == Variant::Auto) v = phase_preferred(b, row_vec, T, k) ? Variant::Phase : Variant::Vgpr;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);

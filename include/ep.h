@@ -228,10 +228,14 @@ int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void
  * rounded separately (never fused), then rounded once to bf16 (round to
  * nearest even).  An entry whose dest_row is outside [0, recv_rows)
  * contributes nothing.  Weights are used as given (not renormalised).
- *   y         bf16 [recv_rows, H] expert outputs in the ep_layout order
+ *   y         bf16 [recv_rows, H] expert outputs in the ep_layout order;
+ *             may be NULL when recv_rows == 0
  *   dest_row  int32 [T, k]
  *   topk_w    float32 [T, k]
  *   out       bf16 [T, H]
+ * With recv_rows == 0 (a receive buffer sized from offsets[E] when no id
+ * was valid) every slot is out of range: out is filled with +0.0 and y is
+ * never read.
  * Limits as ep_dispatch.
  */
 int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row, const float* topk_w,

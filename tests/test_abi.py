@@ -303,3 +303,68 @@ def test_binding_checks_tensors_before_the_library():
         ep.ep_dispatch(cpu, torch.zeros((4, 2), dtype=torch.int32), cpu)
     with pytest.raises(TypeError):
         ep.ep_combine(None, None, None, cpu)
+
+
+class _ReachedLibrary(Exception):
+    pass
+
+
+@pytest.fixture
+def host_binding(monkeypatch):
+    """The binding with host tensors standing in for device ones (only the
+    device test is lifted) and a library stub that raises as soon as it is
+    reached: a size error must be raised before any call into libep.so."""
+    import torch
+
+    def host_tensor(t, name, dtype=None):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        return t
+
+    class Stub:
+        def __getattr__(self, name):
+            if name == "ep_layout_workspace_bytes":
+                return lambda T, k, E: 64
+            raise _ReachedLibrary(name)
+
+    monkeypatch.setattr(ep, "_device_tensor", host_tensor)
+    monkeypatch.setattr(ep, "lib", lambda: Stub())
+    monkeypatch.setattr(ep, "_stream", lambda stream, t=None: 0)
+    return torch
+
+
+@pytest.mark.parametrize("which", ["counts", "offsets", "dest_row_short", "dest_row_shape", "src_token", "status"])
+@pytest.mark.parametrize("entry", ["ep_layout", "ep_layout_dispatch"])
+def test_layout_binding_rejects_short_outputs(host_binding, entry, which):
+    torch = host_binding
+    T, k, E, H = 16, 4, 8, 64
+    i32 = torch.int32
+    good = {"counts": torch.zeros(E, dtype=i32), "offsets": torch.zeros(E + 1, dtype=i32),
+            "dest_row": torch.zeros((T, k), dtype=i32), "src_token": torch.zeros(T * k, dtype=i32),
+            "status": torch.zeros(1, dtype=i32), "workspace": torch.zeros(64, dtype=torch.uint8)}
+    bad = dict(good)
+    if which == "counts":
+        bad["counts"] = torch.zeros(E - 1, dtype=i32)
+    elif which == "offsets":
+        bad["offsets"] = torch.zeros(E, dtype=i32)
+    elif which == "dest_row_short":
+        bad["dest_row"] = torch.zeros((T, k - 1), dtype=i32)
+    elif which == "dest_row_shape":
+        bad["dest_row"] = torch.zeros((T * k,), dtype=i32)
+    elif which == "src_token":
+        bad["src_token"] = torch.zeros(T * k - 1, dtype=i32)
+    else:
+        bad["status"] = torch.zeros(0, dtype=i32)
+    idx = torch.zeros((T, k), dtype=i32)
+    fn = getattr(ep, entry)
+    extra = () if entry == "ep_layout" else (torch.zeros((T, H), dtype=torch.bfloat16),
+                                            torch.zeros((T * k, H), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fn(idx, E, *extra, **bad)
+    # the same call with every output large enough gets through to the library
+    with pytest.raises(_ReachedLibrary):
+        fn(idx, E, *extra, **good)

@@ -409,6 +409,75 @@ def test_combine_unnormalised_weights_and_signed_zero():
     assert_combine_close(got, oracle.combine(recv, lay["dest_row"], wl.topk_w))
 
 
+@pytest.mark.parametrize(
+    "T,k,variant,budget,dest",
+    [
+        (4096, 8, "auto", 0, "none"), (4096, 8, "phase", 0, "none"), (4096, 8, "vgpr", 0, "none"),
+        (128, 8, "auto", 0, "none"), (128, 8, "phase", 0, "none"), (4096, 8, "auto", 24, "none"),
+        (4096, 8, "phase", 0, "stale"), (4096, 6, "auto", 0, "stale"),
+    ],
+)
+def test_combine_empty_receive_buffer(T, k, variant, budget, dest):
+    """recv_rows == 0 (a receive buffer sized from offsets[E] = 0): y is a
+    (0, H) tensor whose data pointer is NULL, and every slot is out of range,
+    so the oracle's sum of no terms is +0.0 everywhere.  dest "none" routes
+    every slot to -1 (what ep_layout writes for invalid ids); "stale" leaves
+    row numbers that would be valid in a full buffer."""
+    H = 7168
+    ep.ep_set_variant(variant)
+    ep.ep_set_num_cus(budget)
+    rng = np.random.default_rng(T + k)
+    if dest == "none":
+        dest_np = np.full((T, k), -1, dtype=np.int32)
+    else:
+        dest_np = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    w_np = rng.random((T, k), dtype=np.float32)
+    y = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    assert y.data_ptr() == 0
+    out = torch.full((T, H), 0x7E57, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    print(f"empty receive buffer: T={T} k={k} variant={variant} budget={budget} dest={dest}", flush=True)
+    ep.ep_combine(y, to_dev(dest_np), to_dev(w_np), out)
+    torch.cuda.synchronize()
+    got = from_dev_bf16(out)
+    ref = oracle.combine(np.zeros((0, H), dtype=np.uint16), dest_np, w_np)
+    assert np.array_equal(got, ref)
+    assert not got.any()  # +0.0, not -0.0
+
+
+def test_combine_unfused_golden_cases():
+    """The hand-derived cases of tests/golden/combine_unfused_cases.txt, where
+    rounding each product and each sum separately gives a different bf16
+    result from a fused multiply-add, through every combine kernel: 64 tokens
+    alternate between the cases, every column of a row holds the case's
+    value, and H = 1024 keeps several units per launch."""
+    from golden_io import read_unfused_cases
+
+    cases = read_unfused_cases()
+    T, H = 64, 1024
+    k = 2
+    y_np = np.empty((T * k, H), dtype=np.uint16)
+    w_np = np.empty((T, k), dtype=np.float32)
+    want = np.empty(T, dtype=np.uint16)
+    for t in range(T):
+        c = cases[t % len(cases)]
+        for j in range(k):
+            y_np[t * k + j, :] = c["y"][j]
+        w_np[t] = c["w"]
+        want[t] = c["unfused"]
+    dest_np = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    ref = oracle.combine(y_np, dest_np, w_np)
+    assert np.array_equal(ref, np.repeat(want[:, None], H, axis=1))
+    for variant in ("auto", "vgpr", "vgpr2", "lds1", "lds2", "phase"):
+        for budget in (0, 24):
+            ep.ep_set_variant(variant)
+            ep.ep_set_num_cus(budget)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+            ep.ep_combine(to_dev_bf16(y_np), to_dev(dest_np), to_dev(w_np), out)
+            torch.cuda.synchronize()
+            got = from_dev_bf16(out)
+            assert np.array_equal(got, ref), (variant, budget)
+
+
 # ----------------------------------------------------------------- probes
 def test_bw_probe_copies_and_writes():
     n = (1 << 22) + 4096

@@ -8,6 +8,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+from golden_io import read_unfused_cases
 from oracle import bf16_to_f32, combine, dispatch, expert_identity, expert_scale, f32_to_bf16_rne, layout
 from synth import make_workload
 
@@ -144,6 +145,31 @@ def test_combine_order_and_tie_rounding():
     # the same four terms summed small-first land above the tie
     out_rev = combine(y, dest[:, ::-1].copy(), w[:, ::-1].copy())
     assert out_rev[0, 0] == 0x3F81
+
+
+def test_combine_products_rounded_separately():
+    """Pins the no-fused-multiply-add reading with the hand-derived cases of
+    tests/golden/combine_unfused_cases.txt.  The oracle must give the
+    separately rounded value; the fused evaluation of the same terms (each
+    product exact, one binary32 rounding per slot) is computed here as well
+    and must give the other value, so a contracted oracle fails this test."""
+    cases = read_unfused_cases()
+    assert len(cases) >= 2
+    for c in cases:
+        y = np.array([[c["y"][0]], [c["y"][1]]], dtype=np.uint16)
+        w = c["w"].reshape(1, 2)
+        dest = np.array([[0, 1]], dtype=np.int32)
+        assert combine(y, dest, w)[0, 0] == c["unfused"], c["name"]
+        # fused: float64 holds each product (24 + 8 significant bits) and its
+        # sum with the binary32 accumulator exactly; then one rounding
+        yf = bf16_to_f32(y[:, 0])
+        acc = np.float32(0.0)
+        for j in range(2):
+            s64 = np.float64(acc) + np.float64(w[0, j]) * np.float64(yf[j])
+            assert Fraction(float(s64)) == Fraction(float(acc)) + Fraction(float(w[0, j])) * Fraction(float(yf[j]))
+            acc = np.float32(s64)
+        assert f32_to_bf16_rne(np.array([acc], dtype=np.float32))[0] == c["fused"], c["name"]
+        assert c["fused"] != c["unfused"]
 
 
 def test_combine_signed_zero_and_skip():
