@@ -1,17 +1,22 @@
 """Benchmark of the MoE row-movement hot path on one MI355X.
 
 One step = ep_layout + ep_dispatch + ep_combine over one batch of the chosen
-workload (default: the training shape, T=4096 tokens, H=7168 bf16, E=256
-experts, top-8), inputs resident in HBM.  The expert op between dispatch and
-combine (a per-expert scale for this shape) is applied once before timing and
-is not part of a step.
+workload (default: the prefill shape, T=16384 tokens, H=7168 bf16, E=64
+experts, top-6 with Zipf(1.0) routing, the largest of the workloads),
+inputs resident in HBM.  The expert op between dispatch and combine is
+applied once before timing and is not part of a step.
 
-Prints ONE JSON line: whole-step algorithmic HBM GB/s with all CUs
-(``value``), tokens/s, the same at a 24-CU budget, per-kernel times, the
-roofline entry of the dominant kernel (HIP events on the launch stream) and
-the CPU oracle timed on the host.
+Headline (``value``): every op timed alone with cold caches -- before each
+call 1 GiB of other memory is written, which evicts the L2s and the 256 MB
+Infinity Cache, and the call sits between two HIP events on its stream --
+over max(steps, --cold) such steps; value = algorithmic bytes of a step /
+(median layout + median dispatch + median combine).  The roofline entry is
+the dominant kernel's algorithmic bytes over its mean cold time.  Warm
+(back-to-back) figures, the training shape and a 24-CU budget are reported
+as labelled extra keys, with the CPU oracle timed on the host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
+  python bench.py --cold-only     # only the cold-protocol steps (for rocprofv3)
   python bench.py --sweep FILE   # CU-budget x variant sweep + copy ceilings, JSONL
 """
 
@@ -35,11 +40,16 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--cold", type=int, default=50,
-                   help="launches per kernel timed one by one after a 1 GiB cache flush (0: skip)")
+                   help="least number of cold-protocol steps (each op after a 1 GiB cache flush); "
+                        "max(--steps, --cold) are timed")
+    p.add_argument("--cold-only", action="store_true",
+                   help="only the cold-protocol steps of the workload (a profiling run)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the warm, 24-CU, training-shape and reduce-on-store extras")
     p.add_argument("--cold-study", action="store_true",
                    help="also time single launches with no flush and with write / read / write+read flushes")
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="train")
+    p.add_argument("--workload", default="prefill")
     p.add_argument("--variant", default="auto")
     p.add_argument("--budget", type=int, default=24, help="the restricted CU budget reported beside all CUs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -276,6 +286,107 @@ def cold_times(s, iters, flush_mode="write"):
     return out
 
 
+def cold_steps(s, iters, warmup=3):
+    """The cold-cache protocol: in every step each op (layout, dispatch,
+    combine) runs once right after 1 GiB of other memory has been written (a
+    torch fill on the launch stream, which evicts the L2s and the 256 MB
+    Infinity Cache), between two HIP events on the launch stream.  `warmup`
+    such steps run first and are not recorded.  Returns {op: [us per call]}."""
+    torch = s.torch
+    stream = s.stream if s.stream is not None else torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda:0")
+    ops = [("layout", s.layout)]
+    if s.do_dispatch and not s.fused:
+        ops.append(("dispatch", s.dispatch))
+    ops.append(("combine", s.combine))
+    evs = {name: [] for name, _ in ops}
+    for i in range(warmup + iters):
+        for name, fn in ops:
+            with torch.cuda.stream(stream):
+                flush.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            if i >= warmup:
+                evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    return {name: [a.elapsed_time(b) * 1e3 for a, b in v] for name, v in evs.items()}
+
+
+def summarize(us):
+    """p10 / p50 / p90 / mean of a list of times (us)."""
+    v = sorted(us)
+    pick = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+    return {"p10": round(pick(0.1), 2), "p50": round(pick(0.5), 2), "p90": round(pick(0.9), 2),
+            "mean": round(sum(v) / len(v), 2), "n": len(v)}
+
+
+def cold_report(s, iters, warmup):
+    """Cold-protocol steps of Setup s: per-op statistics, the step time (sum
+    of the per-op medians), step GB/s and tokens/s."""
+    raw = cold_steps(s, iters, warmup)
+    st = {op: summarize(v) for op, v in raw.items()}
+    t_us = sum(v["p50"] for v in st.values())
+    return {
+        "us_per_op": st,
+        "GBs_p50": {op: round(s.bytes[op] / (v["p50"] * 1e3), 1) for op, v in st.items() if s.bytes[op]},
+        "step_us": round(t_us, 2),
+        "value": round(s.step_bytes / (t_us * 1e3), 2),
+        "tokens_per_s": round(s.T / (t_us * 1e-6), 1),
+    }
+
+
+def budget_probes(budget):
+    """Streaming ceilings (GB/s of bytes moved) on a persistent grid of
+    `budget` CUs: nt reads, 8 and 32 KiB-per-wave writes, the phased 8:1 mix
+    (combine's ratio) and the 1:8 mix (dispatch's).  Best of three timings
+    of 10 launches over 1 GiB."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    once = min(n, budget * 16 * (128 << 10))
+    out = {}
+    ep.ep_set_num_cus(budget)
+    try:
+        for mode, label, nb in ((1, "read", n), (2, "write", n), (0x22, "write32", n), (5, "mix1to8", n),
+                                (7, "mix8to1_phase_once", once)):
+            for _ in range(3):
+                ep.ep_bw_probe(mode, a, b, nb)
+            best = None
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    ep.ep_bw_probe(mode, a, b, nb)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 10
+                best = ms if best is None else min(best, ms)
+            moved = nb + nb // 8 if mode in (5, 7) else nb
+            out[label] = round(moved / best / 1e6, 1)
+    finally:
+        ep.ep_set_num_cus(0)
+    del a, b
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover - non-Linux
+        pass
+    return None
+
+
 def reduce_times(s, steps, budgets):
     """ep_combine_reduce (zero fill, scatter-add with fp32 atomics, bf16
     conversion: three launches) on the workload's expert outputs: `steps`
@@ -352,27 +463,37 @@ def cpu_baseline(name, seconds, gpu=None):
     scales = wl.scales
     passes = 0
     t_total = 0.0
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        lay = oracle.layout(wl.topk_idx, c.E)
-        if c.ops != "combine":
-            recv = oracle.dispatch(wl.x, lay["dest_row"], c.T * c.k)
-        t1 = time.perf_counter()
-        # the expert op sits between the two and is not part of a step
-        if c.ops == "combine":
-            y = y_fixed
-        elif c.expert == "scale":
-            y = oracle.expert_scale(recv, lay["offsets"], scales)
-        else:
-            y = recv
-        t2 = time.perf_counter()
-        out = oracle.combine(y, lay["dest_row"], wl.topk_w)
-        t3 = time.perf_counter()
-        t_total += (t1 - t0) + (t3 - t2)
-        passes += 1
-        if time.perf_counter() - t_start >= seconds:
-            break
+    # one core: this process pinned to a single CPU, BLAS / OpenMP pools at one thread
+    from threadpoolctl import threadpool_limits
+
+    cores_before = os.sched_getaffinity(0)
+    pinned = min(cores_before)
+    os.sched_setaffinity(0, {pinned})
+    try:
+        with threadpool_limits(limits=1):
+            t_start = time.perf_counter()
+            while True:
+                t0 = time.perf_counter()
+                lay = oracle.layout(wl.topk_idx, c.E)
+                if c.ops != "combine":
+                    recv = oracle.dispatch(wl.x, lay["dest_row"], c.T * c.k)
+                t1 = time.perf_counter()
+                # the expert op sits between the two and is not part of a step
+                if c.ops == "combine":
+                    y = y_fixed
+                elif c.expert == "scale":
+                    y = oracle.expert_scale(recv, lay["offsets"], scales)
+                else:
+                    y = recv
+                t2 = time.perf_counter()
+                out = oracle.combine(y, lay["dest_row"], wl.topk_w)
+                t3 = time.perf_counter()
+                t_total += (t1 - t0) + (t3 - t2)
+                passes += 1
+                if time.perf_counter() - t_start >= seconds:
+                    break
+    finally:
+        os.sched_setaffinity(0, cores_before)
     per_step = t_total / passes
     parity = None if gpu is None else parity_against(gpu, lay, recv if c.ops != "combine" else None, out)
     parity_fused = None
@@ -397,7 +518,9 @@ def cpu_baseline(name, seconds, gpu=None):
         "cores": 1,
         "kind": "oracle",
         "sample": f"whole {name} workload (T={c.T}), {passes} pass(es) of layout+dispatch+combine, "
-                  f"single-threaded numpy/Python",
+                  f"single-threaded numpy/Python pinned to CPU {pinned} with BLAS/OpenMP pools at 1 thread",
+        "cpu_model": cpu_model(),
+        "host_cpus_available": len(cores_before),
         "parity_of_timed_gpu_outputs": parity,
         "parity_of_one_launch_layout_dispatch": parity_fused,
     }
@@ -914,7 +1037,7 @@ def main():
         sys.exit(2)
     # the all-cores oracle's processes start before anything touches the GPU
     pool = None
-    if not args.no_cpu and not (args.probe_sweep or args.overlap or args.sweep or args.kernels_only):
+    if not args.no_cpu and not (args.probe_sweep or args.overlap or args.sweep or args.kernels_only or args.cold_only):
         pool = oracle_pool(host_threads())
     import torch
 
@@ -936,9 +1059,9 @@ def main():
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
               [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes, shape=parse_shape(args.shape))
         return
-    if args.shape and not args.kernels_only:
-        raise SystemExit("bench.py: --shape applies to --sweep and --kernels-only; the benchmark line runs the "
-                         "named workload")
+    if args.shape and not (args.kernels_only or args.cold_only):
+        raise SystemExit("bench.py: --shape applies to --sweep, --kernels-only and --cold-only; the benchmark line "
+                         "runs the named workload")
 
     ep.ep_set_variant(args.variant)
     s = Setup(args.workload, shape=parse_shape(args.shape))
@@ -946,51 +1069,38 @@ def main():
     if args.kernels_only:
         kernels_only(s)
         return
-    results = {}
-    for label, budget in (("all", 0), (f"cu{args.budget}", args.budget)):
-        if args.only_all and budget:
-            continue
-        ep.ep_set_num_cus(budget)
-        ms, per = s.run(args.steps, args.warmup)
-        results[label] = (ms, per)
-    ep.ep_set_num_cus(0)
-    fused = None
-    if s.do_dispatch and not args.fused:
-        # the same step with layout and dispatch in one launch (ep_layout_dispatch)
-        s.fused = True
-        fused = s.run(args.steps, args.warmup)
-        s.fused = False
-    probes = probe_ceilings()
-    cold = cold_times(s, args.cold) if args.cold > 0 else None
-    if args.cold_study:
-        for mode in ("none", "write", "read", "write_read"):
-            print(json.dumps({"kind": "cold_study", "workload": args.workload, "flush": mode,
-                              "us_p10_p50_p90": cold_times(s, args.cold or 50, mode)}), flush=True)
-    if not args.only_all:
-        # the same budget as a CU-masked stream with an ordinary grid
-        mask_stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(args.budget)))
-        s.stream = mask_stream
-        results["mask"] = s.run(args.steps, args.warmup)
-        s.stream = None
+    iters = max(args.steps, args.cold)
+    if args.cold_only:
+        rep = cold_report(s, iters, args.warmup)
+        # the copy probe that moves exactly 256 MiB each way: the calibration
+        # kernel of the counter passes
+        a = torch.empty((256 << 20) // 4, dtype=torch.int32, device="cuda:0")
+        for _ in range(3):
+            ep.ep_bw_probe(0, a, torch.empty_like(a), 256 << 20)
         torch.cuda.synchronize()
-        ep.ep_stream_destroy(mask_stream)
+        print(json.dumps({"cold_only": True, "workload": args.workload, "steps": iters, "bytes": s.bytes, **rep}),
+              flush=True)
+        return
 
-    ms, per = results["all"]
-    value = s.step_bytes / (ms * 1e-3) / 1e9
-    kernels = ["dispatch", "combine"] if s.do_dispatch else ["combine"]
-    dom = max(kernels, key=lambda k: per[k])
-    achieved = s.bytes[dom] / (per[dom] * 1e-3) / 1e9
+    # ---- headline: the cold-cache protocol on all CUs (the library's default launches)
+    cold = cold_report(s, iters, args.warmup)
+    kernels = ["dispatch", "combine"] if (s.do_dispatch and not s.fused) else ["combine"]
+    st = cold["us_per_op"]
+    dom = max(kernels, key=lambda k: st[k]["mean"])
+    achieved = s.bytes[dom] / (st[dom]["mean"] * 1e3)
     kname = {"dispatch": "ep_dispatch", "combine": "ep_combine"}[dom]
     traffic = read_traffic(dom, args.workload)
-    ms_b, per_b = results.get(f"cu{args.budget}", (ms, per))
+    probes_all = budget_probes(torch.cuda.get_device_properties(0).multi_processor_count)
+    ref_all = {"dispatch": max(probes_all["mix1to8"], probes_all["write"]), "combine": probes_all["mix8to1_phase_once"]}
+
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": cold["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(cold["step_us"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -998,47 +1108,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": s.T, "H": s.H, "E": s.E, "k": s.k, "num_cus": "all",
                    "variant": ep.ep_get_variant(),
-                   "step": "layout_dispatch+combine" if args.fused else "layout+dispatch+combine"},
-        "tokens_per_s": round(s.T / (ms * 1e-3), 1),
-        "kernel_ms": {k: round(v, 5) for k, v in per.items()},
-        "kernel_timing": getattr(s, "kernel_timing", None),
-        "kernel_GBs": {k: round(s.bytes[k] / (per[k] * 1e6), 1) for k in per if per[k] > 0 and s.bytes[k]},
-        "cold_cache_us_p10_p50_p90": cold,
-        "cold_cache_GBs_p50": None if cold is None else {
-            k: round(s.bytes[k] / (v[1] * 1e3), 1) for k, v in cold.items() if s.bytes[k]},
-        f"cu{args.budget}": None if f"cu{args.budget}" not in results else {
-            "value": round(s.step_bytes / (ms_b * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "ms_per_step": round(ms_b, 5),
-            "tokens_per_s": round(s.T / (ms_b * 1e-3), 1),
-            "kernel_ms": {k: round(v, 5) for k, v in per_b.items()},
-            "kernel_GBs": {k: round(s.bytes[k] / (per_b[k] * 1e6), 1) for k in per_b if per_b[k] > 0 and s.bytes[k]},
-        },
-        f"cu{args.budget}_masked_stream": None if "mask" not in results else {
-            "value": round(s.step_bytes / (results["mask"][0] * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "ms_per_step": round(results["mask"][0], 5),
-            "tokens_per_s": round(s.T / (results["mask"][0] * 1e-3), 1),
-            "kernel_ms": {k: round(v, 5) for k, v in results["mask"][1].items()},
-            "kernel_GBs": {k: round(s.bytes[k] / (v * 1e6), 1) for k, v in results["mask"][1].items()
-                           if v > 0 and s.bytes[k]},
-        },
-        "fused_step": None if fused is None else {
-            "step": "layout_dispatch+combine",
-            "value": round(s.step_bytes / (fused[0] * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "ms_per_step": round(fused[0], 5),
-            "tokens_per_s": round(s.T / (fused[0] * 1e-3), 1),
-            "kernel_ms": {"layout_dispatch": round(fused[1]["layout"], 5), "combine": round(fused[1]["combine"], 5)},
-        },
-        "probe_ceilings_GBs": probes,
-        "frac_of_probe": {
-            "dispatch": (round(s.bytes["dispatch"] / (per["dispatch"] * 1e6) /
-                               max(probes["write_64cus"], probes["write32_64cus"]), 4)
-                         if s.do_dispatch and per["dispatch"] > 0 else None),
-            "combine": round(s.bytes["combine"] / (per["combine"] * 1e6) / probes["mix8to1_phase_once_all_cus"], 4),
-            "against": {"dispatch": "max(write_64cus, write32_64cus)", "combine": "mix8to1_phase_once_all_cus"},
-        },
+                   "step": "layout_dispatch+combine" if args.fused else "layout+dispatch+combine",
+                   "timing": f"cold caches: each op after a 1 GiB write, between HIP events; {iters} steps; "
+                             "step time = sum of per-op medians"},
+        "tokens_per_s": cold["tokens_per_s"],
+        "cold_us_per_op": st,
+        "cold_GBs_p50": cold["GBs_p50"],
+        "probe_ceilings_GBs": probes_all,
+        "frac_of_probe": {k: round(s.bytes[k] / (st[k]["p50"] * 1e3) / ref_all[k], 4) for k in kernels},
+        "frac_of_probe_against": {"dispatch": "max(mix1to8, write)", "combine": "mix8to1_phase_once"},
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
@@ -1048,18 +1126,85 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": s.bytes[dom],
+            "time": "mean of the cold-protocol calls (HIP events on the launch stream)",
         },
     }
-    if not args.no_reduce:
-        line["combine_reduce"] = reduce_times(s, min(args.steps, 50),
-                                              [0] if args.only_all else [0, args.budget])
-    if args.graph:
-        ms_g, ms_e, ms_m, per_graph = graph_step(s, args.steps, args.warmup)
-        line["graph_replay"] = {"ms_per_step": round(ms_g, 5), "eager_ms_per_step": round(ms_e, 5),
-                                "value": round(s.step_bytes / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
-                                "tokens_per_s": round(s.T / (ms_g * 1e-3), 1),
-                                "steps_per_graph": {"steps": per_graph, "ms_per_step": round(ms_m, 5),
-                                                    "tokens_per_s": round(s.T / (ms_m * 1e-3), 1)}}
+
+    if not args.no_extras:
+        # ---- the same workload at a restricted CU budget (persistent grid), cold and warm
+        b = args.budget
+        ep.ep_set_num_cus(b)
+        cold_b = cold_report(s, iters, args.warmup)
+        ms_b, per_b = s.run(args.steps, args.warmup)
+        ep.ep_set_num_cus(0)
+        probes_b = budget_probes(b)
+        ref_b = {"dispatch": max(probes_b["mix1to8"], probes_b["write"]), "combine": probes_b["read"]}
+        line[f"cu{b}"] = {
+            "cold": cold_b,
+            "warm": {"ms_per_step": round(ms_b, 5), "value": round(s.step_bytes / (ms_b * 1e6), 2),
+                     "kernel_ms": {k: round(v, 5) for k, v in per_b.items()}},
+            "probe_ceilings_GBs": probes_b,
+            "frac_of_probe_cold_p50": {k: round(s.bytes[k] / (cold_b["us_per_op"][k]["p50"] * 1e3) / ref_b[k], 4)
+                                       for k in kernels},
+            "frac_of_probe_against": {"dispatch": "max(mix1to8, write)", "combine": "read"},
+            "frac_of_hbm_peak_cold": round(cold_b["value"] / HBM_PEAK_GBS, 4),
+        }
+        # ---- the same budget as a CU-masked stream with ordinary grids (warm)
+        mask_stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(b)))
+        s.stream = mask_stream
+        ms_m, per_m = s.run(args.steps, args.warmup)
+        s.stream = None
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(mask_stream)
+        line[f"cu{b}_masked_stream_warm"] = {"ms_per_step": round(ms_m, 5),
+                                             "value": round(s.step_bytes / (ms_m * 1e6), 2),
+                                             "kernel_ms": {k: round(v, 5) for k, v in per_m.items()}}
+        # ---- warm: back-to-back launches on all CUs (inputs partly in the Infinity Cache)
+        ms_w, per_w = s.run(args.steps, args.warmup)
+        line["warm_all_cus"] = {
+            "ms_per_step": round(ms_w, 5), "value": round(s.step_bytes / (ms_w * 1e6), 2),
+            "kernel_ms": {k: round(v, 5) for k, v in per_w.items()},
+            "kernel_timing": getattr(s, "kernel_timing", None),
+            "kernel_GBs": {k: round(s.bytes[k] / (per_w[k] * 1e6), 1) for k in per_w if per_w[k] > 0 and s.bytes[k]},
+        }
+        if s.do_dispatch and not args.fused:
+            # the staged dispatch on 64 CUs, fastest while x is cache-resident
+            ep.ep_set_variant("lds1")
+            cold_l = cold_steps(s, max(20, iters // 2), 2)["dispatch"]
+            ms_l, per_l = s.run(args.steps, args.warmup)
+            ep.ep_set_variant(args.variant)
+            line["dispatch_lds1_64cus"] = {"cold": summarize(cold_l), "warm_us": round(per_l["dispatch"] * 1e3, 2)}
+            # layout and dispatch in one launch (ep_layout_dispatch), warm
+            s.fused = True
+            ms_f, per_f = s.run(args.steps, args.warmup)
+            s.fused = False
+            line["fused_step_warm"] = {"step": "layout_dispatch+combine", "ms_per_step": round(ms_f, 5),
+                                       "value": round(s.step_bytes / (ms_f * 1e6), 2),
+                                       "kernel_ms": {"layout_dispatch": round(per_f["layout"], 5),
+                                                     "combine": round(per_f["combine"], 5)}}
+        if not args.no_reduce:
+            line["combine_reduce_warm"] = reduce_times(s, min(args.steps, 50), [0])
+        if args.graph:
+            ms_g, ms_e, ms_m2, per_graph = graph_step(s, args.steps, args.warmup)
+            line["graph_replay"] = {"ms_per_step": round(ms_g, 5), "eager_ms_per_step": round(ms_e, 5),
+                                    "value": round(s.step_bytes / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                    "tokens_per_s": round(s.T / (ms_g * 1e-3), 1),
+                                    "steps_per_graph": {"steps": per_graph, "ms_per_step": round(ms_m2, 5),
+                                                        "tokens_per_s": round(s.T / (ms_m2 * 1e-3), 1)}}
+        # ---- the training shape (T=4096, E=256, k=8), cold and warm
+        if args.workload != "train" and not args.shape:
+            t = Setup("train")
+            cold_t = cold_report(t, iters, args.warmup)
+            ms_t, per_t = t.run(args.steps, args.warmup)
+            line["train"] = {"cold": cold_t,
+                             "warm": {"ms_per_step": round(ms_t, 5), "value": round(t.step_bytes / (ms_t * 1e6), 2),
+                                      "kernel_ms": {k: round(v, 5) for k, v in per_t.items()}}}
+            del t
+            torch.cuda.empty_cache()
+    if args.cold_study:
+        for mode in ("none", "write", "read", "write_read"):
+            print(json.dumps({"kind": "cold_study", "workload": args.workload, "flush": mode,
+                              "us_p10_p50_p90": cold_times(s, args.cold or 50, mode)}), flush=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, gpu=s)
         line["cpu_baseline"]["all_cores"] = cpu_baseline_parallel(args.workload, args.cpu_seconds / 2, pool,

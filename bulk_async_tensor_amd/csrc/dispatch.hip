@@ -369,10 +369,13 @@ DispatchFn pick_kind(Variant v) {
     case Variant::Pc: return dispatch_pc_kernel<VPL, K, EVEN, true>;
     default: break;
   }
-  // the double-buffered kernels hold two slabs (the three-stage one three):
-  // compiled up to 8 vectors per lane
-  if constexpr (VPL <= 8) {
+  // the register double buffer holds two slabs: compiled up to 14 vectors
+  // per lane (124 VGPRs at k = 8, no spills; 16 spill)
+  if constexpr (VPL <= 14) {
     if (v == Variant::Vgpr2) return dispatch_vgpr2_kernel<VPL, K, EVEN, true>;
+  }
+  // the LDS rings hold two or three slabs: compiled up to 8 vectors per lane
+  if constexpr (VPL <= 8) {
     if constexpr (K > 0) {
       if (v == Variant::Lds2) return dispatch_lds2_kernel<VPL, K, EVEN, true>;
       if (v == Variant::Lds3) return dispatch_lds3_kernel<VPL, K, EVEN, true>;
@@ -582,21 +585,42 @@ hipError_t launch_dispatch_phase(const Budget& b, const void* x, int T, int row_
 
 int dispatch_slab_vpl(int row_vec, int cap, int requested) { return choose_vpl(row_vec, cap, requested); }
 
+// The default for a large batch with no compute-unit budget on an unmasked
+// stream: the register double buffer (vgpr2) with whole-row slabs, as a
+// persistent grid on every CU.  Its loads of x are streaming, so its time
+// does not depend on whether x is still in the Infinity Cache; the LDS-staged
+// kernels load x with cacheable direct-to-LDS loads, which are fastest on 64
+// CUs while x is cached and up to 2.5x slower when it is not (each miss then
+// fills the Infinity Cache).  Measured at H = 7168, single launches after a
+// 1 GiB write that evicts x, and without it: T = 4096, k = 8: 105.7 / 103.7
+// us against lds1 on 64 CUs 193.6 / 87.9; T = 16384, k = 6, E = 64:
+// 339.4 / 335.3 against 647.3 / 258.2.  Callers whose x was just written
+// (and so is cache-resident) can ask for "lds1".
+bool dispatch_stream_preferred(const Budget& b, int64_t T) {
+  return b.num_cus == 0 && b.device_cus == b.all_cus && T >= 8LL * b.device_cus;
+}
+
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {
-  // direct-to-LDS staging measured fastest at every compute-unit budget
-  if (v == Variant::Auto) v = Variant::Lds1;
+  bool stream_default = false;
+  if (v == Variant::Auto) {
+    stream_default = dispatch_stream_preferred(b, T);
+    // direct-to-LDS staging otherwise: fastest at every compute-unit budget
+    v = stream_default ? Variant::Vgpr2 : Variant::Lds1;
+  }
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if ((v == Variant::Lds2 || v == Variant::Lds3 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
-  // default slabs of at most 8 KiB (half rows at H = 7168); whole 14 KiB
-  // rows per wave measured no faster.  A requested size may go to 16 for the
-  // single-set kernels; the double-buffered ones hold two slabs (the
-  // three-stage one three), so 8.
-  const bool multi = v == Variant::Vgpr2 || v == Variant::Lds2 || v == Variant::Lds3;
-  const int cap = (multi || b.slab_vpl == 0) ? 8 : 16;
+  // Slabs: the register double buffer takes whole rows of up to 14 KiB
+  // (T = 4096, H = 7168, all CUs, x evicted: 105.7 us against 106.7 us with
+  // half rows).  The staged kernels take at most 8 KiB (half rows at
+  // H = 7168; whole 14 KiB rows measured no faster), the LDS rings holding
+  // two or three slabs.  A requested size may go to 16 for the single-set
+  // kernels.
+  const bool ring = v == Variant::Lds2 || v == Variant::Lds3;
+  const int cap = v == Variant::Vgpr2 ? 14 : (ring || b.slab_vpl == 0) ? 8 : 16;
   const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
@@ -617,7 +641,8 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // start-up is cheaper.
   int budget = b.num_cus;
   const int write_cus = dispatch_write_cus(k);
-  if (budget == 0 && units >= write_cus * 16 * 2) budget = write_cus;
+  if (stream_default) budget = b.device_cus;
+  else if (budget == 0 && units >= write_cus * 16 * 2) budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W
     // slabs each; always a persistent grid (one workgroup per CU)

@@ -49,7 +49,7 @@ def trace(args):
     bench = None
     for line in open(args.bench_log):
         line = line.strip()
-        if line.startswith("{") and '"metric"' in line:
+        if line.startswith("{") and ('"metric"' in line or '"cold_only"' in line):
             bench = json.loads(line)
     out = [f"# rocprofv3 kernel trace: {args.title}", f"# command: {args.command}", "",
            f"{'kernel':<60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
@@ -60,7 +60,12 @@ def trace(args):
         nm = r["Name"].replace("ep::(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         out.append(f"{nm[:60]:<60s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
-    if bench:
+    if bench and bench.get("cold_only"):
+        out += ["", "same run, HIP events on the launch stream (bench.py --cold-only: every call after a 1 GiB "
+                    "write, us per call; a phased combine call is several launches):"]
+        for op, st in bench.get("us_per_op", {}).items():
+            out.append(f"  {op}: {json.dumps(st)}")
+    elif bench:
         out += ["", "same run, HIP events on the launch stream (bench.py, ms per launch):"]
         out.append("  " + json.dumps(bench.get("kernel_ms")))
         out.append(f"  roofline: {json.dumps(bench.get('roofline'))}")

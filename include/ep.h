@@ -71,12 +71,16 @@ enum {
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
  * launch.  n == 0: no budget; the library picks the launch per kernel --
  * an ordinary grid over the whole device, except that a dispatch of at
- * least 32 work units per CU of its default budget runs persistent on
- * that budget: 64 CUs for k >= 5 (at k = 8 its traffic is 8/9 writes, and
- * HBM write throughput peaks with about a quarter of the CUs issuing
- * them), 96 for k = 2..4 and 128 for k = 1, whose larger read share needs
- * more CUs in flight.  The initial value comes from the environment
- * variable EP_NUM_CUS (default 0).
+ * least 8 tokens per CU (variant "auto", unmasked stream) runs the register
+ * double buffer ("vgpr2") with whole-row slabs as a persistent grid on
+ * every CU: its streaming loads of x take the same time whether or not x is
+ * still in the Infinity Cache.  With another variant, a dispatch of at
+ * least 32 work units per CU of its default budget runs persistent on that
+ * budget: 64 CUs for k >= 5 (at k = 8 its traffic is 8/9 writes, and HBM
+ * write throughput peaks with about a quarter of the CUs issuing them), 96
+ * for k = 2..4 and 128 for k = 1, whose larger read share needs more CUs in
+ * flight.  The initial value comes from the environment variable
+ * EP_NUM_CUS (default 0).
  * On a CU-masked stream (ep_stream_create_cu_masked, or any stream whose
  * mask hipExtStreamGetCUMask reports) every launch counts only the CUs of
  * the mask: n and the default dispatch budget are clamped to them, ordinary
@@ -89,7 +93,13 @@ int ep_get_num_cus(void);
 
 /*
  * Kernel variant for dispatch and combine (process-wide):
- *   "auto"  the default choice per shape;
+ *   "auto"  the default choice per shape.  A large dispatch on the whole
+ *           device takes "vgpr2" with whole-row slabs on every CU, whose
+ *           time does not depend on the cache state of x (T = 16384,
+ *           H = 7168, k = 6: about 335 us whether or not x was evicted);
+ *           "lds1" on 64 CUs is faster while x is still in the Infinity
+ *           Cache (about 258 us) and much slower once it is not (about
+ *           650 us), so a caller that has just written x may prefer it;
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
  *           or k loads feeding one store (combine);
  *   "vgpr2" the same with the next work unit's loads issued before the
