@@ -41,6 +41,7 @@ _SIGNATURES = {
     "ep_get_slab": (_c_int, []),
     "ep_layout_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "ep_layout": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p]),
+    "ep_layout_noalloc": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p]),
     "ep_dispatch": (_c_int, [_p, _c_int, _c_int, _p, _c_int, _p, _c_i64, _p]),
     "ep_dispatch_rows": (_c_int, [_p, _c_int, _c_int, _p, _p, _c_i64, _p]),
     "ep_layout_dispatch": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _c_int, _p, _p, _p, _p, _p, _p, _c_sz, _p,
@@ -228,6 +229,29 @@ def ep_layout(topk_idx, num_experts, counts=None, offsets=None, dest_row=None, s
                         _ptr(status), _ptr(workspace), ws_bytes, _stream(stream, topk_idx)),
         "ep_layout",
     )
+    return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
+
+
+EP_LAYOUT_NOALLOC_MAX_SCRATCH = 4 << 20
+
+
+def ep_layout_noalloc(topk_idx, num_experts, counts, offsets, dest_row, src_token=None, status=None, stream=None):
+    """ep_layout with the library's static scratch instead of a workspace
+    (the C call allocates nothing).  Every output except src_token and
+    status must be given; returns the same dict as ep_layout."""
+    import torch
+
+    _device_tensor(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, k]")
+    if counts is None or offsets is None or dest_row is None:
+        raise ValueError("ep_layout_noalloc needs counts, offsets and dest_row")
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    counts, offsets, dest_row, src_token, status = _layout_outputs(T, k, E, topk_idx.device, counts, offsets,
+                                                                   dest_row, src_token, status)
+    _check(lib().ep_layout_noalloc(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(dest_row),
+                                   _ptr(src_token), _ptr(status), _stream(stream, topk_idx)), "ep_layout_noalloc")
     return {"counts": counts, "offsets": offsets, "dest_row": dest_row, "src_token": src_token, "status": status}
 
 

@@ -126,6 +126,33 @@ int check_rows(int H, int64_t recv_rows, const char* what) {
   return EP_OK;
 }
 
+// Scratch of ep_layout_noalloc: the (chunk, expert) count table and the
+// per-chunk status words of the two- and three-launch layout paths, in a
+// static device array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = EP_LAYOUT_NOALLOC_MAX_SCRATCH;
+static_assert(kStaticScratchBytes % 256 == 0, "the scratch holds 256-byte aligned tables");
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+int static_scratch(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EP_OK;
+}
+
 }  // namespace
 
 namespace ep {
@@ -213,9 +240,10 @@ size_t ep_layout_workspace_bytes(int T, int k, int E) {
 
 namespace {
 
+// check_workspace = false: the call brings its own scratch (ep_layout_noalloc).
 int check_layout_args(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
                       int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
-                      size_t workspace_bytes, const char* what) {
+                      size_t workspace_bytes, const char* what, bool check_workspace = true) {
   int rc = check_common(T, k, E, what);
   if (rc) return rc;
   if (E < 1 || E > EP_MAX_EXPERTS) return fail(EP_ERR_INVALID_ARG, "%s: E = %d outside [1, %d]", what, E, EP_MAX_EXPERTS);
@@ -226,7 +254,7 @@ int check_layout_args(const int32_t* topk_idx, int T, int k, int E, int32_t* cou
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return fail(EP_ERR_ALIGNMENT, "%s: int32 tensor not 4-byte aligned", what);
   const size_t need = ep::layout_workspace_bytes(T, k, E);
-  if (need > 0) {
+  if (check_workspace && need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(EP_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -250,6 +278,33 @@ int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int
   hipError_t e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ep_layout launch");
+  return EP_OK;
+}
+
+int ep_layout_noalloc(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                      int32_t* dest_row, int32_t* src_token, int32_t* status, void* stream) {
+  // the same checks as ep_layout, with the static scratch standing in for the workspace
+  int rc = check_layout_args(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, nullptr, 0,
+                             "ep_layout_noalloc", false);
+  if (rc) return rc;
+  const size_t need = ep::layout_workspace_bytes(T, k, E);
+  if (need > kStaticScratchBytes)
+    return fail(EP_ERR_WORKSPACE,
+                "ep_layout_noalloc: T = %d, k = %d, E = %d needs %zu bytes of scratch, above the static %zu; "
+                "use ep_layout with a workspace",
+                T, k, E, need, kStaticScratchBytes);
+  ep::Budget b;
+  rc = current_device(&b, stream);
+  if (rc) return rc;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  rc = static_scratch(dev, &ws);
+  if (rc) return rc;
+  e = ep::launch_layout(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, ws,
+                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_layout_noalloc launch");
   return EP_OK;
 }
 

@@ -178,6 +178,28 @@ int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int
               size_t workspace_bytes, void* stream);
 
 /*
+ * ep_layout_noalloc -- ep_layout for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (without the
+ * workspace), outputs, limits and errors as ep_layout, with identical
+ * results.  Where ep_layout needs scratch (ep_layout_workspace_bytes > 0:
+ * the two- and three-launch paths for larger batches), this call uses a
+ * static device array of EP_LAYOUT_NOALLOC_MAX_SCRATCH bytes inside the
+ * library instead; each GPU the library runs on holds its own copy until
+ * the process ends.  A batch whose scratch would exceed it returns
+ * EP_ERR_WORKSPACE before anything is enqueued (ep_layout with a workspace
+ * handles it).  The call allocates nothing, frees nothing and makes no
+ * memset: the layout overwrites every scratch entry it later reads, so the
+ * previous call's contents do not matter.  All calls on one GPU share its
+ * array: calls that may overlap on one GPU (on different streams without
+ * ordering between them, or from several threads) race and must be
+ * serialised by the caller.
+ */
+#define EP_LAYOUT_NOALLOC_MAX_SCRATCH ((size_t)4 << 20)
+int ep_layout_noalloc(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                      int32_t* dest_row, int32_t* src_token, int32_t* status, void* stream);
+
+/*
  * ep_dispatch -- recv[dest_row[t*k+j], :] = x[t, :] for all t < T, j < k
  * (bit copy).  The row copy of [DeepEP-TMA] section "Asynchronous Copy
  * Primitives": each source row is read once into an on-chip slice and

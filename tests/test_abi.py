@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -123,6 +123,45 @@ def layout(lib, idx=A4, T=16, k=2, E=8, counts=A4, offsets=A4, dest=A4, src=A4, 
 def test_layout_rejects(lib, kw, code):
     assert layout(lib, **kw) == code
     assert lib.ep_last_error().decode() != ""
+
+
+def layout_noalloc(lib, idx=A4, T=16, k=2, E=8, counts=A4, offsets=A4, dest=A4, src=A4, status=A4):
+    return lib.ep_layout_noalloc(idx, T, k, E, counts, offsets, dest, src, status, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=-1), ep.EP_ERR_INVALID_ARG),
+        (dict(k=0), ep.EP_ERR_INVALID_ARG),
+        (dict(E=1025), ep.EP_ERR_INVALID_ARG),
+        (dict(k=9, E=8), ep.EP_ERR_INVALID_ARG),
+        (dict(counts=None), ep.EP_ERR_INVALID_ARG),
+        (dict(dest=None), ep.EP_ERR_INVALID_ARG),
+        (dict(idx=ODD), ep.EP_ERR_ALIGNMENT),
+        # scratch above the static 4 MiB: 40000 x 32 with E = 1024 needs 5,125,000 bytes
+        (dict(T=40000, k=32, E=1024), ep.EP_ERR_WORKSPACE),
+        (dict(T=200000, k=8, E=1024), ep.EP_ERR_WORKSPACE),
+    ],
+)
+def test_layout_noalloc_rejects(lib, kw, code):
+    """Host-side errors of the no-allocation layout, before any HIP call; the
+    size limit is the static scratch (the same workspace sizes as ep_layout)."""
+    assert layout_noalloc(lib, **kw) == code
+    msg = lib.ep_last_error().decode()
+    assert msg.startswith("ep_layout_noalloc")
+    if code == ep.EP_ERR_WORKSPACE:
+        assert "scratch" in msg
+
+
+def test_layout_noalloc_scratch_limit(lib):
+    """The largest batches the static scratch covers at a few expert counts:
+    the limit equals ep_layout_workspace_bytes against the stated maximum."""
+    limit = ep.EP_LAYOUT_NOALLOC_MAX_SCRATCH
+    assert limit == 4 << 20
+    assert lib.ep_layout_workspace_bytes(16384, 6, 64) <= limit  # the prefill shape
+    assert lib.ep_layout_workspace_bytes(131072, 8, 256) <= limit
+    assert lib.ep_layout_workspace_bytes(40000, 32, 1024) > limit
 
 
 def dispatch(lib, x=A16, T=16, H=1024, dest=A4, k=2, recv=A16, rows=32):
