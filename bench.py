@@ -72,6 +72,9 @@ def parse_args():
                    help="a few launches of each kernel and of a 256 MiB copy probe (for counter passes)")
     p.add_argument("--probe-sweep", default=None, help="write a streaming-probe matrix as JSONL to this file")
     p.add_argument("--no-reduce", action="store_true", help="skip timing the reduce-on-store combine")
+    p.add_argument("--latency", default=None,
+                   help="pointer-chase latencies and the bytes-in-flight vs read GB/s table at --budget CUs, "
+                        "JSONL to this file")
     return p.parse_args()
 
 
@@ -829,6 +832,134 @@ def probe_sweep(path, budgets):
     ep.ep_set_num_cus(0)
 
 
+def latency_study(path, budget):
+    """Load latency and the per-CU read ceiling (ep_inflight_probe).
+
+    Every measured walk follows a fresh random cyclic chain of 256-byte
+    nodes (rebuilt from a new seed), so no hop finds its node in a cache it
+    did not get there itself:
+    1. Unloaded, one wave, nothing else running: an L2 hit (a 1 MiB chain
+       walked twice, the second walk reported); an Infinity Cache hit (a
+       128 MiB chain read once with cacheable loads, which thrashes the 4 MB
+       L2 but leaves the chain in the 256 MB Infinity Cache); HBM (a 4 GiB
+       chain after a 1 GiB write that evicts both).
+    2. Loaded, at `budget` CUs: waves_per_cu x vectors_per_lane of streaming
+       nt reads over 2 GiB while wave 0 of workgroup 0 chases a fresh 4 GiB
+       chain from HBM on its CU, which its other waves keep streaming.  Read
+       GB/s over the streaming waves, latency per hop, the clock from the
+       chase's shader-cycle and real-time counters, and the bytes in flight
+       per CU that Little's law gives (per-CU GB/s x latency).
+    3. The same at every CU with the deepest settings."""
+    import torch
+
+    import bulk_async_tensor_amd as ep
+
+    dev = "cuda:0"
+    sink = torch.empty(4, dtype=torch.int32, device=dev)
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    src = torch.empty(1 << 29, dtype=torch.int32, device=dev)  # 2 GiB
+    src.fill_(3)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    ndev = torch.cuda.get_device_properties(0).multi_processor_count
+    node = 256
+    per = node // 8
+    big = torch.zeros((4 << 30) // 8, dtype=torch.int64, device=dev)
+
+    def chain_of(set_bytes, seed):
+        n = set_bytes // node
+        chain = big[: n * per]
+        chain.zero_()
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        perm = torch.randperm(n, device=dev, generator=gen)
+        chain[perm * per] = torch.roll(perm, -1) * per
+        return chain
+
+    def walk(waves, vec, nbytes, chain, hops, cached=False):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ep.ep_inflight_probe(waves, vec, src, nbytes, sink, chain, hops, out, cached=cached)
+        e1.record()
+        torch.cuda.synchronize()
+        o = out.cpu().tolist()
+        ns = o[0] * 10.0  # 100 MHz ticks
+        return {"kernel_us": round(e0.elapsed_time(e1) * 1e3, 2), "chase_ns_per_hop": round(ns / hops, 1),
+                "chase_cycles_per_hop": round(o[1] / hops, 1), "clock_GHz": round(o[1] / ns, 3) if ns > 0 else None,
+                "chase_us": round(ns / 1e3, 2), "chase_xcc": o[3] >> 32}
+
+    seed = [100]
+
+    def fresh(set_bytes, evict=True):
+        seed[0] += 1
+        chain = chain_of(set_bytes, seed[0])
+        if evict:
+            flush.fill_(seed[0])
+        torch.cuda.synchronize()
+        return chain
+
+    with open(path, "w") as fh:
+        def emit(rec):
+            fh.write(json.dumps(rec) + "\n")
+            fh.flush()
+            print(json.dumps(rec), flush=True)
+
+        ep.ep_set_num_cus(1)
+        chain = fresh(1 << 20)
+        walk(1, 1, 0, chain, 4000)
+        emit({"kind": "unloaded", "level": "L2 hit", "set_MiB": 1, "hops": 4000, **walk(1, 1, 0, chain, 4000)})
+        chain = fresh(128 << 20)
+        ep.ep_set_num_cus(0)
+        ep.ep_bw_probe(1 | (1 << 8), chain, sink, chain.numel() * 8)  # cacheable read of the whole chain
+        torch.cuda.synchronize()
+        ep.ep_set_num_cus(1)
+        emit({"kind": "unloaded", "level": "Infinity Cache hit", "set_MiB": 128, "hops": 2000,
+              **walk(1, 1, 0, chain, 2000)})
+        for set_bytes in (1 << 30, 4 << 30):
+            chain = fresh(set_bytes)
+            emit({"kind": "unloaded", "level": "HBM", "set_MiB": set_bytes >> 20, "hops": 1500,
+                  **walk(1, 1, 0, chain, 1500)})
+        nbytes = src.numel() * 4
+        for cus, hops, grid in ((budget, 100, [(w, v) for w in (1, 2, 4, 8, 16) for v in (1, 2, 4, 8, 16)]),
+                                (ndev, 60, [(16, 8), (8, 16), (16, 4), (4, 8)])):
+            ep.ep_set_num_cus(cus)
+            for w, v in grid:
+                if v == 16 and w > 8:
+                    continue
+                chain = fresh(4 << 30)
+                r = walk(w, v, nbytes, chain, hops)
+                gbs = nbytes / (r["kernel_us"] * 1e3)
+                per_cu = gbs / cus
+                lat_ns = r["chase_ns_per_hop"]
+                emit({"kind": "loaded", "cus": cus, "waves_per_cu": w, "vectors_per_lane": v,
+                      "requested_KiB_in_flight_per_cu": [w * v, 2 * w * v], "streaming_waves": cus * w - 1,
+                      "GBs": round(gbs, 1), "GBs_per_cu": round(per_cu, 2),
+                      "B_per_clk_per_cu": round(per_cu / r["clock_GHz"], 2) if r["clock_GHz"] else None,
+                      "latency_ns": lat_ns, "littles_law_KiB_in_flight_per_cu": round(per_cu * lat_ns / 1024, 1),
+                      "chase_shorter_than_stream": r["chase_us"] < r["kernel_us"], **r})
+        # where the streamed data lives: HBM (nt or cacheable loads, after a flush) or the Infinity Cache
+        # (a 128 MiB source read once with cacheable loads first), at the same depth.  A per-CU cap that
+        # rises when the data comes from closer (lower latency) is a limit on outstanding misses; one that
+        # does not is a throughput limit of the CU's vector memory path.
+        small = 128 << 20
+        for cus in (budget, ndev):
+            ep.ep_set_num_cus(cus)
+            for w, v in ((16, 8), (8, 8), (4, 8)):
+                for where, nb, cached, warm in (("HBM", nbytes, False, False), ("HBM", nbytes, True, False),
+                                                ("Infinity Cache", small, True, True),
+                                                ("Infinity Cache (nt loads)", small, False, True)):
+                    chain = fresh(4 << 30)
+                    if warm:
+                        walk(w, v, nb, chain, 1, cached=True)
+                    r = walk(w, v, nb, chain, 40, cached=cached)
+                    gbs = nb / (r["kernel_us"] * 1e3)
+                    emit({"kind": "residency", "cus": cus, "waves_per_cu": w, "vectors_per_lane": v, "source": where,
+                          "loads": "cacheable" if cached else "nt", "MiB": nb >> 20, "GBs": round(gbs, 1),
+                          "GBs_per_cu": round(gbs / cus, 2),
+                          "B_per_clk_per_cu": round(gbs / cus / r["clock_GHz"], 2) if r["clock_GHz"] else None,
+                          "chase_ns_per_hop": r["chase_ns_per_hop"], "kernel_us": r["kernel_us"]})
+    ep.ep_set_num_cus(0)
+
+
 def graph_step(s, steps, warmup):
     """One whole step captured in a HIP graph (torch.cuda.CUDAGraph) and
     replayed: the step's device time without per-launch host overhead.
@@ -1037,7 +1168,8 @@ def main():
         sys.exit(2)
     # the all-cores oracle's processes start before anything touches the GPU
     pool = None
-    if not args.no_cpu and not (args.probe_sweep or args.overlap or args.sweep or args.kernels_only or args.cold_only):
+    if not args.no_cpu and not (args.probe_sweep or args.overlap or args.sweep or args.kernels_only or args.cold_only
+                                or args.latency):
         pool = oracle_pool(host_threads())
     import torch
 
@@ -1050,6 +1182,9 @@ def main():
     budgets = args.sweep_budgets.split(",")
     if args.probe_sweep:
         probe_sweep(args.probe_sweep, [int(b) for b in budgets])
+        return
+    if args.latency:
+        latency_study(args.latency, args.budget)
         return
     if args.overlap:
         overlap(args.overlap, args.workload, [int(b) for b in budgets], max(20, args.steps // 4),

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "ep_last_error": (ctypes.c_char_p, []),
     "ep_bw_probe": (_c_int, [_c_int, _p, _p, _c_i64, _p]),
     "ep_probe_placement": (_c_int, [_p, _c_int, _p]),
+    "ep_inflight_probe": (_c_int, [_c_int, _c_int, _c_int, _p, _c_i64, _p, _p, _c_i64, _c_i64, _p, _p]),
     "ep_mfma_probe": (_c_int, [_c_int, _c_int, _p, _p]),
     "ep_stream_create_cu_masked": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, ctypes.POINTER(_p)]),
     "ep_stream_destroy": (_c_int, [_p]),
@@ -374,6 +375,26 @@ def ep_combine_reduce(y, src_token, dest_row, topk_w, out, workspace=None, strea
 def ep_bw_probe(mode, src, dst, nbytes, stream=None):
     """Streaming probe under the current CU budget (0 copy, 1 read, 2 write)."""
     return _check(lib().ep_bw_probe(int(mode), _ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "ep_bw_probe")
+
+
+def ep_inflight_probe(waves_per_cu, vectors_per_lane, src, nbytes, sink, chain=None, hops=0, out=None, cached=False,
+                      stream=None):
+    """Streaming nt reads with a chosen depth per CU, beside one pointer-chasing
+    wave (see include/ep.h).  chain: int64 device tensor of next indices;
+    out: int64 device tensor of at least 4 elements."""
+    import torch
+
+    if chain is not None:
+        _device_tensor(chain, "chain", torch.int64)
+    if out is not None:
+        _device_tensor(out, "out", torch.int64)
+        if out.numel() < 4:
+            raise ValueError("out must hold 4 int64")
+    clen = 0 if chain is None else chain.numel()
+    return _check(lib().ep_inflight_probe(int(waves_per_cu), int(vectors_per_lane), int(bool(cached)), _ptr(src),
+                                          int(nbytes),
+                                          _ptr(sink), _ptr(chain), clen, int(hops), _ptr(out), _stream(stream)),
+                  "ep_inflight_probe")
 
 
 def ep_probe_placement(out, n_groups, stream=None):

@@ -463,6 +463,33 @@ int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* strea
   return EP_OK;
 }
 
+int ep_inflight_probe(int waves_per_cu, int vectors_per_lane, int cached, const void* src, int64_t bytes, void* sink,
+                      const int64_t* chain, int64_t chain_len, int64_t hops, int64_t* out, void* stream) {
+  if (cached != 0 && cached != 1) return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: cached = %d not 0 or 1", cached);
+  if (waves_per_cu < 1 || waves_per_cu > 16)
+    return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: waves_per_cu = %d outside [1, 16]", waves_per_cu);
+  if (vectors_per_lane != 1 && vectors_per_lane != 2 && vectors_per_lane != 4 && vectors_per_lane != 8 &&
+      vectors_per_lane != 16)
+    return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: vectors_per_lane = %d not 1, 2, 4, 8 or 16",
+                vectors_per_lane);
+  if (vectors_per_lane == 16 && waves_per_cu > 8)
+    return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: 16 vectors per lane allow at most 8 waves per CU");
+  if (bytes < 0 || bytes % 16) return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: bytes must be a multiple of 16");
+  if (hops < 0 || chain_len < 0) return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: negative hops or chain_len");
+  if (!sink || (bytes > 0 && !src)) return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: null src/sink");
+  if (hops > 0 && (!chain || !out || chain_len < 1))
+    return fail(EP_ERR_INVALID_ARG, "ep_inflight_probe: a chase needs chain, chain_len >= 1 and out");
+  if ((src && !aligned(src, 16)) || !aligned(sink, 16) || (chain && !aligned(chain, 8)) || (out && !aligned(out, 8)))
+    return fail(EP_ERR_ALIGNMENT, "ep_inflight_probe: alignment");
+  ep::Budget b;
+  int rc = current_device(&b, stream);
+  if (rc) return rc;
+  hipError_t e = ep::launch_inflight_probe(b, waves_per_cu, vectors_per_lane, cached, src, bytes, sink, chain,
+                                           chain_len, hops, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ep_inflight_probe launch");
+  return EP_OK;
+}
+
 int ep_probe_placement(int32_t* out, int n_groups, void* stream) {
   if (!out || n_groups < 1 || n_groups > 65536)
     return fail(EP_ERR_INVALID_ARG, "ep_probe_placement: bad output or n_groups");

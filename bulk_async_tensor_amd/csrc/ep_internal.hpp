@@ -77,6 +77,9 @@ hipError_t launch_combine_reduce(const Budget& b, const void* y, int64_t recv_ro
 hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst, int64_t bytes,
                            hipStream_t stream);
 hipError_t launch_placement(const Budget& b, int n_groups, int32_t* out, hipStream_t stream, int* launched);
+hipError_t launch_inflight_probe(const Budget& b, int waves_per_cu, int vec_per_lane, int cached, const void* src,
+                                 int64_t bytes, void* sink, const int64_t* chain, int64_t chain_len, int64_t hops,
+                                 int64_t* out, hipStream_t stream);
 hipError_t launch_mfma_probe(int n_groups, int iters, float* out, hipStream_t stream);
 
 // Raise the dynamic-LDS limit of a kernel once (needed above 64 KiB).

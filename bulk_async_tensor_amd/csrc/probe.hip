@@ -254,6 +254,99 @@ __global__ __launch_bounds__(1024) void bw_mix_burst_kernel(const u32x4* __restr
   }
 }
 
+// ---- in-flight read probe with a pointer chase
+//
+// Every wave but one streams reads of src (streaming nt loads, or cacheable
+// ones with NTL = false) in batches of V 16-byte vectors per lane; the next batch is issued before the current one is folded, so V
+// to 2V vectors per lane stay in flight.  Wave 0 of workgroup 0 instead
+// follows `hops` links of `chain` (element i holds the index of the next
+// element; an index outside [0, chain_len) restarts at 0), one dependent
+// vector load at a time, and records the 100 MHz real-time ticks and
+// shader-clock cycles it took: the load latency seen on a CU whose other
+// waves keep streaming (or, with nothing to stream, unloaded).
+__device__ __forceinline__ int64_t chase_load(const int64_t* p) {
+  int64_t v;
+  // a vector load (not a scalar one) and its wait in one statement
+  asm volatile("global_load_dwordx2 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+// Two batches of V vectors per lane: 16 leave room for 8 waves per CU only.
+template <int V>
+constexpr int inflight_max_threads() {
+  return V >= 16 ? 512 : 1024;
+}
+
+template <int V, bool NTL>
+__global__ __launch_bounds__(inflight_max_threads<V>()) void inflight_kernel(const u32x4* __restrict__ src, int64_t nvec,
+                                                        u32x4* __restrict__ sink, const int64_t* __restrict__ chain,
+                                                        int64_t chain_len, int64_t hops, int64_t* __restrict__ out) {
+  const int lane = lane_id();
+  const int wave = wave_in_group();
+  const int wpg = blockDim.x >> 6;
+  const int chasers = hops > 0 ? 1 : 0;
+  if (chasers && blockIdx.x == 0 && wave == 0) {
+    int64_t idx = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    for (int64_t h = 0; h < hops; ++h) {
+      const int64_t nx = chase_load(chain + idx);
+      idx = (uint64_t)nx < (uint64_t)chain_len ? nx : 0;
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      out[0] = (int64_t)(t1 - t0);
+      out[1] = (int64_t)(c1 - c0);
+      out[2] = idx;
+      out[3] = (int64_t)hw_id_reg() | ((int64_t)(xcc_id_reg() & 0xF) << 32);
+    }
+    return;
+  }
+  const int64_t nstream = (int64_t)gridDim.x * wpg - chasers;
+  const int64_t sid = (int64_t)blockIdx.x * wpg + wave - chasers;
+  constexpr int64_t kChunk = (int64_t)V * kWave;
+  const int64_t stride = nstream * kChunk;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 a[V], b[V];
+  int64_t c = sid * kChunk;
+  if (c < nvec) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int64_t e = c + i * kWave + lane;
+      a[i] = e < nvec ? ld16<NTL>(src + e) : acc;
+    }
+    for (;;) {
+      int64_t n1 = c + stride;
+      if (n1 < nvec) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int64_t e = n1 + i * kWave + lane;
+          b[i] = e < nvec ? ld16<NTL>(src + e) : acc;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc ^= a[i];
+      if (n1 >= nvec) break;
+      c = n1;
+      n1 = c + stride;
+      if (n1 < nvec) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int64_t e = n1 + i * kWave + lane;
+          a[i] = e < nvec ? ld16<NTL>(src + e) : acc;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc ^= b[i];
+      if (n1 >= nvec) break;
+      c = n1;
+    }
+  }
+  // keeps the reads alive; true only for a vanishingly unlikely checksum
+  if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && acc[2] == 0x94d049bbu) sink[0] = acc;
+}
+
 using BwFn = void (*)(const u32x4*, u32x4*, int64_t);
 
 template <int OP, int D>
@@ -346,6 +439,31 @@ hipError_t launch_bw_probe(const Budget& b, int mode, const void* src, void* dst
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(wpg * kWave), lds, stream, static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), nvec);
+  return hipGetLastError();
+}
+
+using InflightFn = void (*)(const u32x4*, int64_t, u32x4*, const int64_t*, int64_t, int64_t, int64_t*);
+
+template <bool NTL>
+InflightFn inflight_pick(int vec_per_lane) {
+  return vec_per_lane == 1 ? inflight_kernel<1, NTL> : vec_per_lane == 2 ? inflight_kernel<2, NTL>
+       : vec_per_lane == 4 ? inflight_kernel<4, NTL> : vec_per_lane == 8 ? inflight_kernel<8, NTL>
+       : vec_per_lane == 16 ? inflight_kernel<16, NTL> : nullptr;
+}
+
+hipError_t launch_inflight_probe(const Budget& b, int waves_per_cu, int vec_per_lane, int cached, const void* src,
+                                 int64_t bytes, void* sink, const int64_t* chain, int64_t chain_len, int64_t hops,
+                                 int64_t* out, hipStream_t stream) {
+  InflightFn fn = cached ? inflight_pick<false>(vec_per_lane) : inflight_pick<true>(vec_per_lane);
+  if (!fn) return hipErrorInvalidValue;
+  // one workgroup per CU of the budget (exclusive LDS), waves_per_cu waves each
+  int grid = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  if (grid < 1) grid = 1;
+  const size_t lds = kExclusiveLds;
+  hipError_t e = allow_dynamic_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(waves_per_cu * kWave), lds, stream, static_cast<const u32x4*>(src),
+                     bytes / 16, static_cast<u32x4*>(sink), chain, chain_len, hops, out);
   return hipGetLastError();
 }
 

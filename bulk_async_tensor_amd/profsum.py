@@ -8,6 +8,9 @@
       the step records of bench.py --sweep files as one table (dispatch and
       combine GB/s per shape, variant and CU budget).
 
+  python -m bulk_async_tensor_amd.profsum latency <latency.jsonl> --title "..." --command "..."
+      the pointer-chase latencies and bytes-in-flight tables of bench.py --latency.
+
   python -m bulk_async_tensor_amd.profsum hbm <fetch_counter_collection.csv> <write_counter_collection.csv>
           --kernel dispatch|combine|layout|layout_dispatch --workload NAME --out FILE --command "..."
       HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
@@ -182,6 +185,39 @@ def sweep_table(args):
     sys.stdout.write("\n".join(out) + "\n")
 
 
+def latency_table(args):
+    """The records of bench.py --latency as three tables: unloaded chase
+    latency per memory level; read GB/s against requested bytes in flight at
+    the CU budgets, with the loaded latency and Little's-law bytes in flight;
+    and the per-CU rate by where the streamed data lives."""
+    recs = [json.loads(line) for path in args.jsonl for line in open(path) if line.strip()]
+    out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [""]
+    out.append("unloaded latency (one wave, random chain of 256-byte nodes, nothing else running):")
+    out.append(f"  {'level':<22s} {'set MiB':>8s} {'ns/hop':>8s} {'cycles/hop':>11s} {'clock GHz':>10s}")
+    for r in recs:
+        if r["kind"] == "unloaded":
+            out.append(f"  {r['level']:<22s} {r['set_MiB']:8d} {r['chase_ns_per_hop']:8.1f} "
+                       f"{r['chase_cycles_per_hop']:11.1f} {r['clock_GHz']:10.3f}")
+    out += ["", "streaming nt reads of 2 GiB from HBM beside a pointer chase on a streaming CU (fresh 4 GiB chain):",
+            f"  {'CUs':>4s} {'waves/CU':>8s} {'vec/lane':>8s} {'req KiB/CU':>11s} {'GB/s':>8s} {'GB/s/CU':>8s} "
+            f"{'B/clk/CU':>8s} {'lat ns':>7s} {'Little KiB/CU':>13s}"]
+    for r in recs:
+        if r["kind"] == "loaded":
+            req = r["requested_KiB_in_flight_per_cu"]
+            out.append(f"  {r['cus']:4d} {r['waves_per_cu']:8d} {r['vectors_per_lane']:8d} {req[0]:>5d}-{req[1]:<5d} "
+                       f"{r['GBs']:8.1f} {r['GBs_per_cu']:8.2f} {r['B_per_clk_per_cu']:8.2f} {r['latency_ns']:7.1f} "
+                       f"{r['littles_law_KiB_in_flight_per_cu']:13.1f}")
+    out += ["", "per-CU read rate by where the data lives (same depth; the chase on a fresh HBM chain):",
+            f"  {'CUs':>4s} {'waves/CU':>8s} {'vec/lane':>8s} {'source':<26s} {'loads':<9s} {'MiB':>5s} {'GB/s':>8s} "
+            f"{'GB/s/CU':>8s} {'B/clk/CU':>8s} {'chase ns':>8s}"]
+    for r in recs:
+        if r["kind"] == "residency":
+            out.append(f"  {r['cus']:4d} {r['waves_per_cu']:8d} {r['vectors_per_lane']:8d} {r['source']:<26s} "
+                       f"{r['loads']:<9s} {r['MiB']:5d} {r['GBs']:8.1f} {r['GBs_per_cu']:8.2f} "
+                       f"{r['B_per_clk_per_cu']:8.2f} {r['chase_ns_per_hop']:8.1f}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="mode", required=True)
@@ -211,8 +247,12 @@ def main(argv=None):
     w.add_argument("jsonl", nargs="+")
     w.add_argument("--title", default="")
     w.add_argument("--command", action="append", default=[])
+    lt = sub.add_parser("latency")
+    lt.add_argument("jsonl", nargs="+")
+    lt.add_argument("--title", default="")
+    lt.add_argument("--command", action="append", default=[])
     args = p.parse_args(argv)
-    {"trace": trace, "hbm": hbm, "sq": sq, "sweep": sweep_table}[args.mode](args)
+    {"trace": trace, "hbm": hbm, "sq": sq, "sweep": sweep_table, "latency": latency_table}[args.mode](args)
 
 
 if __name__ == "__main__":

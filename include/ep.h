@@ -353,6 +353,27 @@ const char* ep_last_error(void);
 int ep_bw_probe(int mode, const void* src, void* dst, int64_t bytes, void* stream);
 
 /*
+ * ep_inflight_probe: the per-CU read ceiling and the load latency behind it.
+ * A persistent grid of one workgroup of waves_per_cu (1..16; 1..8 with 16
+ * vectors per lane) waves per CU of
+ * the budget (every CU when ep_get_num_cus() == 0) streams reads over
+ * `bytes` of src (streaming nt loads; cacheable ones with cached = 1), each wave keeping vectors_per_lane (1, 2, 4, 8 or 16) to
+ * twice that many 16-byte vectors per lane in flight (the next batch is
+ * issued before the current one is consumed).  With hops > 0, wave 0 of
+ * workgroup 0 does not stream: it follows `hops` links of `chain` (int64
+ * element i holds the index of the next element; an index outside
+ * [0, chain_len) restarts the walk at 0), one dependent vector load at a
+ * time, and writes out[0] = elapsed 100 MHz real-time ticks, out[1] =
+ * elapsed shader-clock cycles, out[2] = the last index, out[3] = HW_ID
+ * (low 32 bits) and XCC id (bits 32..35) of its CU.  With bytes == 0 the
+ * chase runs on an otherwise idle device (unloaded latency).  sink holds
+ * 16 bytes and is written only for an improbable checksum.  Returns EP_OK,
+ * EP_ERR_INVALID_ARG, EP_ERR_ALIGNMENT or EP_ERR_HIP.
+ */
+int ep_inflight_probe(int waves_per_cu, int vectors_per_lane, int cached, const void* src, int64_t bytes, void* sink,
+                      const int64_t* chain, int64_t chain_len, int64_t hops, int64_t* out, void* stream);
+
+/*
  * ep_probe_placement: launch min(n_groups, budget) workgroups that each
  * need more than half a CU's LDS (budget = the CU count when
  * ep_get_num_cus() > 0, else n_groups), each holding its CU for ~50 us, and

@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -323,6 +323,21 @@ def test_masked_stream_rejects(lib):
     assert lib.ep_stream_create_cu_masked(mask, 8, ctypes.byref(out)) == ep.EP_ERR_INVALID_ARG  # empty
     assert lib.ep_stream_destroy(None) == ep.EP_ERR_INVALID_ARG
     assert ep.cu_mask_words([0, 33, 255]) == [1, 2, 0, 0, 0, 0, 0, 1 << 31]
+
+
+def test_inflight_probe_rejects(lib):
+    f = lib.ep_inflight_probe
+    assert f(0, 8, 0, A16, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(17, 8, 0, A16, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(4, 3, 0, A16, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(16, 16, 0, A16, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(4, 8, 0, A16, 1000, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(4, 8, 0, None, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert f(4, 8, 0, A16, 1024, A16, None, 0, 10, A16, None) == ep.EP_ERR_INVALID_ARG  # a chase needs a chain
+    assert f(4, 8, 0, A16, 1024, A16, A16, 0, 10, A16, None) == ep.EP_ERR_INVALID_ARG  # of at least one element
+    assert f(4, 8, 0, A16, 1024, A16, A4, 8, 10, A16, None) == ep.EP_ERR_ALIGNMENT
+    assert f(4, 8, 0, A4, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_ALIGNMENT
+    assert f(4, 8, 2, A16, 1024, A16, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

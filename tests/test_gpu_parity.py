@@ -479,6 +479,32 @@ def test_combine_unfused_golden_cases():
 
 
 # ----------------------------------------------------------------- probes
+def test_inflight_probe_chase_lands_on_the_walked_index():
+    """The pointer chase of ep_inflight_probe follows the chain exactly: after
+    `hops` links its last index is the one a host walk reaches, with and
+    without streaming waves beside it."""
+    n, per = 4096, 32  # 4096 nodes of 256 bytes
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(n)
+    chain_np = np.zeros(n * per, dtype=np.int64)
+    chain_np[perm * per] = np.roll(perm, -1) * per
+    chain = to_dev(chain_np)
+    src = torch.ones(1 << 22, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    out = torch.zeros(4, dtype=torch.int64, device=DEV)
+    for budget, waves, vec, nbytes, hops in ((1, 1, 1, 0, 777), (24, 4, 8, src.numel() * 4, 301),
+                                             (0, 8, 16, src.numel() * 4, 55)):
+        ep.ep_set_num_cus(budget)
+        ep.ep_inflight_probe(waves, vec, src, nbytes, sink, chain, hops, out, cached=budget == 24)
+        torch.cuda.synchronize()
+        idx = 0
+        for _ in range(hops):
+            idx = int(chain_np[idx])
+        o = out.cpu().tolist()
+        assert o[2] == idx and o[0] > 0 and o[1] > 0
+        assert int(sink.abs().sum()) == 0
+
+
 def test_bw_probe_copies_and_writes():
     n = (1 << 22) + 4096
     src = torch.randint(-(1 << 31), 1 << 31, (n // 4,), dtype=torch.int32, device=DEV)

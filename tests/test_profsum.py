@@ -90,3 +90,24 @@ def test_bench_shape_overrides():
     for bad in ("q=3", "k=two", "k"):
         with pytest.raises(SystemExit):
             bench.parse_shape(bad)
+
+
+def test_latency_table_formats_every_record_kind(tmp_path, capsys):
+    from bulk_async_tensor_amd import profsum
+
+    recs = [
+        {"kind": "unloaded", "level": "HBM", "set_MiB": 4096, "chase_ns_per_hop": 420.0,
+         "chase_cycles_per_hop": 1000.0, "clock_GHz": 2.4},
+        {"kind": "loaded", "cus": 24, "waves_per_cu": 8, "vectors_per_lane": 8,
+         "requested_KiB_in_flight_per_cu": [64, 128], "GBs": 1387.4, "GBs_per_cu": 57.81,
+         "B_per_clk_per_cu": 23.91, "latency_ns": 621.2, "littles_law_KiB_in_flight_per_cu": 35.1},
+        {"kind": "residency", "cus": 24, "waves_per_cu": 16, "vectors_per_lane": 8, "source": "Infinity Cache",
+         "loads": "cacheable", "MiB": 128, "GBs": 2065.2, "GBs_per_cu": 86.05, "B_per_clk_per_cu": 35.69,
+         "chase_ns_per_hop": 563.0},
+    ]
+    path = tmp_path / "lat.jsonl"
+    path.write_text("\n".join(__import__("json").dumps(r) for r in recs) + "\n")
+    profsum.main(["latency", str(path), "--title", "t", "--command", "c"])
+    text = capsys.readouterr().out
+    assert "# command: c" in text
+    assert "420.0" in text and "1387.4" in text and "35.1" in text and "86.05" in text
