@@ -61,6 +61,8 @@ def parse_args():
     p.add_argument("--shape", default=None,
                    help="--sweep and --kernels-only: override the workload's sizes, e.g. k=2,T=16384 (keys T, H, E, k)")
     p.add_argument("--no-probes", action="store_true", help="skip the streaming probes in --sweep")
+    p.add_argument("--sweep-cold", type=int, default=0,
+                   help="--sweep: also time this many cold-protocol steps per budget and variant")
     p.add_argument("--only-all", action="store_true", help="time only the all-CU configuration")
     p.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
     p.add_argument("--fused", action="store_true", help="layout and dispatch through ep_layout_dispatch")
@@ -715,8 +717,10 @@ def parse_shape(text):
     return out
 
 
-def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True, shape=None):
-    """CU budget x variant x slab over the workload, plus the streaming-probe ceilings."""
+def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True, shape=None, cold=0):
+    """CU budget x variant x slab over the workload, plus the streaming-probe
+    ceilings.  With cold > 0, each record also carries the cold-protocol
+    per-op statistics (every call after a 1 GiB write) over `cold` steps."""
     import torch
 
     import bulk_async_tensor_amd as ep
@@ -767,6 +771,7 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True, shap
                     s.gather = v.startswith("rows")
                     ep.ep_set_variant({"rows": "auto", "rows_nt": "vgpr_cached"}.get(v, v))
                     ep.ep_set_slab(slab)
+                    cold_rep = cold_report(s, cold, 2) if cold > 0 and not s.gather else None
                     ms, per = s.run(steps, warmup)
                     gbs = {k: (s.bytes[k] / (per[k] * 1e6) if per[k] > 0 else None) for k in per}
                     # streaming ceilings at this budget: dispatch (8/9 writes) against the
@@ -782,6 +787,8 @@ def sweep(path, name, steps, warmup, budgets, variants, slabs, probes=True, shap
                            "frac_of_probe": {k: (gbs[k] / ref[k] if gbs.get(k) and ref.get(k) else None)
                                              for k in ("dispatch", "combine")},
                            "probe_ref": {"dispatch": "max(write, write32)", "combine": "mix8to1_phase_once"}}
+                    if cold_rep is not None:
+                        rec["cold"] = cold_rep
                     fh.write(json.dumps(rec) + "\n")
                     print(json.dumps(rec), flush=True)
             ep.ep_set_slab(0)
@@ -1192,7 +1199,8 @@ def main():
         return
     if args.sweep:
         sweep(args.sweep, args.workload, max(20, args.steps // 4), 5, budgets, args.sweep_variants.split(","),
-              [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes, shape=parse_shape(args.shape))
+              [int(v) for v in args.sweep_slabs.split(",")], probes=not args.no_probes, shape=parse_shape(args.shape),
+              cold=args.sweep_cold)
         return
     if args.shape and not (args.kernels_only or args.cold_only):
         raise SystemExit("bench.py: --shape applies to --sweep, --kernels-only and --cold-only; the benchmark line "
@@ -1213,8 +1221,8 @@ def main():
         for _ in range(3):
             ep.ep_bw_probe(0, a, torch.empty_like(a), 256 << 20)
         torch.cuda.synchronize()
-        print(json.dumps({"cold_only": True, "workload": args.workload, "steps": iters, "bytes": s.bytes, **rep}),
-              flush=True)
+        print(json.dumps({"cold_only": True, "workload": args.workload, "steps": iters, "warmup": args.warmup,
+                          "bytes": s.bytes, **rep}), flush=True)
         return
 
     # ---- headline: the cold-cache protocol on all CUs (the library's default launches)

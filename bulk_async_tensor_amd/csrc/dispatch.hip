@@ -585,42 +585,58 @@ hipError_t launch_dispatch_phase(const Budget& b, const void* x, int T, int row_
 
 int dispatch_slab_vpl(int row_vec, int cap, int requested) { return choose_vpl(row_vec, cap, requested); }
 
-// The default for a large batch with no compute-unit budget on an unmasked
-// stream: the register double buffer (vgpr2) with whole-row slabs, as a
-// persistent grid on every CU.  Its loads of x are streaming, so its time
-// does not depend on whether x is still in the Infinity Cache; the LDS-staged
-// kernels load x with cacheable direct-to-LDS loads, which are fastest on 64
-// CUs while x is cached and up to 2.5x slower when it is not (each miss then
-// fills the Infinity Cache).  Measured at H = 7168, single launches after a
-// 1 GiB write that evicts x, and without it: T = 4096, k = 8: 105.7 / 103.7
-// us against lds1 on 64 CUs 193.6 / 87.9; T = 16384, k = 6, E = 64:
-// 339.4 / 335.3 against 647.3 / 258.2.  Callers whose x was just written
-// (and so is cache-resident) can ask for "lds1".
-bool dispatch_stream_preferred(const Budget& b, int64_t T) {
-  return b.num_cus == 0 && b.device_cus == b.all_cus && T >= 8LL * b.device_cus;
+bool dispatch_auto_large(const Budget& b, int64_t T) {
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  return T >= 8LL * cus;
+}
+
+// The default for a batch of at least 8 tokens per CU of its launch: a
+// persistent grid on every CU it may use (the budget, the stream's mask or
+// the device) with whole-row slabs and a kernel that keeps the next rows'
+// loads in flight while it stores: the register double buffer (vgpr2) on at
+// least half the device, the producer/consumer split (pc, an issuer wave
+// with four rows in flight per CU) on fewer CUs, where each CU's outstanding
+// reads are the bound.  Their loads of x take about the same time whether x
+// is in the Infinity Cache or not.  The LDS-staged kernels load x with
+// cacheable direct-to-LDS loads: fastest on 64 CUs while x is cached, up to
+// 2.5x slower when it is not (each miss then fills the Infinity Cache).
+// Measured at H = 7168, single launches after a 1 GiB write that evicts x
+// and without it (x cached):
+//   T = 4096, k = 8, all CUs: vgpr2 105.7 / 103.7 us, lds1 on 64 CUs
+//     193.6 / 87.9; T = 16384, k = 6, E = 64: 339.4 / 335.3 against
+//     647.3 / 258.2 (and 322 against 589 us when x was written just before
+//     the dispatch, which leaves only part of its 235 MB cached);
+//   24 CUs, T = 4096: pc 286.7 / 201.6 us, vgpr2 320.2 / 316.4, lds1
+//     352.6 / 192.6; 64 CUs: pc 149.7 / 94.6, vgpr2 167.5 / 164.6, lds1
+//     194.5 / 88.9; 128 CUs: vgpr2 117.1 / 116.9, lds1 127.4 / 94.9.
+// Callers whose x is cache-resident can ask for "lds1".
+Variant dispatch_auto(const Budget& b, int64_t T, int* persistent_cus) {
+  const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
+  if (!dispatch_auto_large(b, T)) return Variant::Lds1;
+  *persistent_cus = cus;
+  return 2 * cus >= b.all_cus ? Variant::Vgpr2 : Variant::Pc;
 }
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {
-  bool stream_default = false;
-  if (v == Variant::Auto) {
-    stream_default = dispatch_stream_preferred(b, T);
-    // direct-to-LDS staging otherwise: fastest at every compute-unit budget
-    v = stream_default ? Variant::Vgpr2 : Variant::Lds1;
-  }
+  int auto_cus = 0;  // the persistent grid the default chose (0: none)
+  if (v == Variant::Auto) v = dispatch_auto(b, T, &auto_cus);
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if ((v == Variant::Lds2 || v == Variant::Lds3 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
   const int row_vec = H / 8;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
-  // Slabs: the register double buffer takes whole rows of up to 14 KiB
-  // (T = 4096, H = 7168, all CUs, x evicted: 105.7 us against 106.7 us with
-  // half rows).  The staged kernels take at most 8 KiB (half rows at
+  // Slabs: the register double buffer and the producer/consumer split take
+  // whole rows of up to 14 KiB (T = 4096, H = 7168, x evicted: vgpr2 on all
+  // CUs 105.7 against 106.7 us with half rows; pc on 24 CUs 286.7 against
+  // 311.8 us).  The other staged kernels take at most 8 KiB (half rows at
   // H = 7168; whole 14 KiB rows measured no faster), the LDS rings holding
   // two or three slabs.  A requested size may go to 16 for the single-set
   // kernels.
   const bool ring = v == Variant::Lds2 || v == Variant::Lds3;
-  const int cap = v == Variant::Vgpr2 ? 14 : (ring || b.slab_vpl == 0) ? 8 : 16;
+  const int cap = v == Variant::Vgpr2 ? 14
+                : v == Variant::Pc ? (b.slab_vpl > 0 ? 16 : 14)
+                : (ring || b.slab_vpl == 0) ? 8 : 16;
   const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
@@ -641,7 +657,7 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // start-up is cheaper.
   int budget = b.num_cus;
   const int write_cus = dispatch_write_cus(k);
-  if (stream_default) budget = b.device_cus;
+  if (auto_cus > 0) budget = auto_cus;
   else if (budget == 0 && units >= write_cus * 16 * 2) budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W

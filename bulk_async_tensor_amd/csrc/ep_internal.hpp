@@ -55,6 +55,11 @@ hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T
 // vectors, at most `cap` (a requested size is rounded down to a compiled one).
 int dispatch_slab_vpl(int row_vec, int cap, int requested);
 
+// True when variant "auto" dispatches T tokens with its large-batch kernels
+// (at least 8 tokens per CU of the launch), which stream x instead of
+// staging it through cacheable direct-to-LDS loads.
+bool dispatch_auto_large(const Budget& b, int64_t T);
+
 // ---- fused layout + dispatch (layout_dispatch.hip)
 // One launch for small batches and, with the lds1-style copy, for wide ones;
 // otherwise launch_layout then launch_dispatch (workspace as for the layout).

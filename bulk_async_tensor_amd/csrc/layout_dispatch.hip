@@ -492,12 +492,14 @@ hipError_t launch_layout_dispatch(Variant v, const Budget& b, const int32_t* idx
                                   hipStream_t stream) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  // The wide kernel copies as the lds1 dispatch does: taken unless another
-  // dispatch kernel was asked for.  It is also the faster one for decode
-  // batches where it applies (T = 128, E = 256, k = 8: 8.1 against 8.7 us
-  // for the small kernel; T = 64: 6.5 against 7.6 us), so the small kernel
-  // serves the rest: few experts, other k, other variants.
-  if (T > 0 && (v == Variant::Auto || v == Variant::Lds1)) {
+  // The wide kernel copies as the lds1 dispatch does: taken for "lds1", and
+  // for "auto" below the batch size from which the default dispatch streams
+  // x (its cacheable loads of x are fast only while x is cached).  It is
+  // also the faster one for decode batches where it applies (T = 128,
+  // E = 256, k = 8: 8.1 against 8.7 us for the small kernel; T = 64: 6.5
+  // against 7.6 us), so the small kernel serves the rest: few experts,
+  // other k, other variants.
+  if (T > 0 && (v == Variant::Lds1 || (v == Variant::Auto && !dispatch_auto_large(b, T)))) {
     const WidePlan p = wide_plan(b, T, k, E, H);
     if (p.ok)
       return launch_wide(p, idx, T, k, E, nbits, x, H, counts, offsets, dest_row, src_token, status, recv,

@@ -170,7 +170,7 @@ def sweep_table(args):
         "# GB/s are algorithmic bytes over the HIP-event time per launch; slab 0 = the kernels' default; "
         "CUs 0 = the library's default launch", "",
         f"{'k':>2s} {'T':>6s} {'H':>5s} {'E':>4s} {'variant':<8s} {'slab':>4s} {'CUs':>4s} {'dispatch GB/s':>14s} "
-        f"{'combine GB/s':>13s}"]
+        f"{'combine GB/s':>13s} {'cold disp GB/s':>15s} {'cold comb GB/s':>15s} {'cold step GB/s':>15s}"]
     for path in args.jsonl:
         for line in open(path):
             r = json.loads(line)
@@ -179,9 +179,137 @@ def sweep_table(args):
             sh = r.get("shape") or {}
             g = r.get("GBs") or {}
             cell = lambda v, w: f"{v:{w}.0f}" if v else f"{'-':>{w}s}"
+            c = (r.get("cold") or {}).get("GBs_p50") or {}
+            cstep = (r.get("cold") or {}).get("value")
             out.append(f"{sh.get('k', 0):2d} {sh.get('T', 0):6d} {sh.get('H', 0):5d} {sh.get('E', 0):4d} "
                        f"{r['variant']:<8s} {r.get('slab', 0):4d} {r['num_cus']:>4s} {cell(g.get('dispatch'), 14)} "
-                       f"{cell(g.get('combine'), 13)}")
+                       f"{cell(g.get('combine'), 13)} {cell(c.get('dispatch'), 15)} {cell(c.get('combine'), 15)} "
+                       f"{cell(cstep, 15)}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
+def budgets_table(args):
+    """HBM bytes per call, LDS bank conflicts and VALU busy per kernel kind
+    across CU budgets, from one FETCH_SIZE, one WRITE_SIZE and one SQ pass
+    per budget over bench.py --cold-only.  Each --run is
+    LABEL:CUS:FETCH_CSV:WRITE_CSV:SQ_CSV:BENCH_LOG; the bench log's last
+    line gives the algorithmic bytes and the number of calls (steps plus
+    warm-up).  Counters are scaled by what they read for the 256 MiB copy
+    probe of the same pass."""
+    out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [
+        "# HBM MB = (FETCH_SIZE x fetch scale + WRITE_SIZE x write scale) summed over a kind's launches, per call",
+        "# (launches / launches per call, the latter rounded from launches / calls);",
+        "# ratio = HBM bytes / algorithmic bytes; LDS_conf% and VALUBusy% are medians over the kind's launches,",
+        "# over the budget's CUs (GUI = GRBM_GUI_ACTIVE / 8).", "",
+        f"{'budget':<8s} {'kernel':<10s} {'launches/call':>13s} {'read MB':>9s} {'write MB':>9s} {'HBM MB':>9s} "
+        f"{'alg MB':>9s} {'ratio':>7s} {'LDS_conf%':>9s} {'VALUBusy%':>9s}"]
+    for spec in args.run:
+        label, cus, fetch_csv, write_csv, sq_csv, log = spec.split(":")
+        cus = int(cus)
+        bench = None
+        for line in open(log):
+            if line.strip().startswith("{") and '"cold_only"' in line:
+                bench = json.loads(line)
+        calls = bench["steps"] + bench.get("warmup", 0)
+        fsum, fn = sums_of(fetch_csv, "FETCH_SIZE")
+        wsum, _ = sums_of(write_csv, "WRITE_SIZE")
+        copy_kib = args.copy_bytes / 1024.0
+        f_scale = copy_kib / (fsum["copy_probe"] / fn["copy_probe"])
+        w_scale = copy_kib / (wsum["copy_probe"] / fn["copy_probe"])
+        sq = sq_of(sq_csv)
+        for kind in ("layout", "dispatch", "combine"):
+            if kind not in fsum:
+                continue
+            # launches per call from the counts (the setup's own first
+            # launches of layout and dispatch make a few more than calls x n)
+            per_call = max(1, round(fn[kind] / calls))
+            ncalls = fn[kind] / per_call
+            rd = fsum[kind] * f_scale * 1024.0 / ncalls
+            wr = wsum.get(kind, 0.0) * w_scale * 1024.0 / ncalls
+            hbm = rd + wr
+            alg = bench["bytes"].get(kind) or 0
+            q = sq.get(kind, {})
+            gui = q.get("GRBM_GUI_ACTIVE", 0.0) / args.xcds
+            conf = 100 * q.get("SQ_LDS_BANK_CONFLICT", 0.0) / gui / cus if gui else 0.0
+            valu = 100 * q.get("SQ_ACTIVE_INST_VALU", 0.0) / cus / gui if gui else 0.0
+            out.append(f"{label:<8s} {kind:<10s} {per_call:13d} {rd / 1e6:9.2f} {wr / 1e6:9.2f} "
+                       f"{hbm / 1e6:9.2f} {alg / 1e6:9.2f} {(hbm / alg if alg else 0.0):7.4f} {conf:9.3f} {valu:9.2f}")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
+def sums_of(path, counter):
+    """Sum of a counter and launch count per kernel kind."""
+    tot, cnt = {}, {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = kind_of(r["Kernel_Name"])
+        if k is not None:
+            tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+            cnt[k] = cnt.get(k, 0) + 1
+    return tot, cnt
+
+
+def sq_of(path):
+    """Median per kind of each SQ/GRBM counter over the kind's launches."""
+    per = {}
+    for r in csv.DictReader(open(path)):
+        k = kind_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = {}
+    for k, launches in per.items():
+        names = set().union(*[set(c) for c in launches.values()])
+        out[k] = {n: statistics.median(c.get(n, 0.0) for c in launches.values()) for n in names}
+    return out
+
+
+def overlap_table(args):
+    """The records of bench.py --overlap: the step on n masked CUs beside the
+    computation on the other CUs, each alone on its partition and both
+    together, and both together without a partition."""
+    out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [""]
+    for path in args.jsonl:
+        for line in open(path):
+            r = json.loads(line)
+            if r["kind"] == "overlap_base":
+                out.append(f"{r['compute']} computation alone on all CUs: {r['gemm_ms_all_cus']:.3f} ms "
+                           f"({r['gemm_TFLOPs_all_cus']:.0f} TFLOP/s); step ({r['workload']}) alone on all CUs: "
+                           f"{r['step_ms_all_cus'] * 1e3:.1f} us")
+                out.append(f"  {'copy/compute CUs':<17s} {'compute alone':>14s} {'compute with step':>18s} "
+                           f"{'slowdown':>9s} {'step alone us':>14s} {'step with compute us':>21s} {'slowdown':>9s} "
+                           f"{'step GB/s':>10s}")
+            elif r.get("partition") == "none":
+                out.append(f"  {'none (shared)':<17s} {'-':>14s} {r['gemm_ms'] * 1e3:15.1f} us {r['gemm_slowdown']:9.3f} "
+                           f"{'-':>14s} {r['step_ms'] * 1e3:21.1f} {r['step_slowdown']:9.3f} {'-':>10s}")
+            else:
+                out.append(f"  {r['partition']:<17s} {r['gemm_ms_alone_on_rest'] * 1e3:11.1f} us "
+                           f"{r['gemm_ms'] * 1e3:15.1f} us {r['gemm_slowdown_vs_alone_on_rest']:9.3f} "
+                           f"{r['step_ms_alone_on_n'] * 1e3:14.1f} {r['step_ms'] * 1e3:21.1f} "
+                           f"{r['step_slowdown_vs_alone_on_n']:9.3f} {r['step_GBs_concurrent']:10.0f}")
+        out.append("")
+    sys.stdout.write("\n".join(out) + "\n")
+
+
+def probes_table(args):
+    """The streaming-probe matrix of bench.py --probe-sweep: GB/s per
+    operation, depth and load policy (rows) at each CU budget (columns)."""
+    recs = [json.loads(line) for path in args.jsonl for line in open(path) if line.strip()]
+    budgets = sorted({r["num_cus"] for r in recs}, key=lambda b: (b == 0, b))
+    keys = []
+    for r in recs:
+        k = (r["op"], r["depth"], r["policy"])
+        if k not in keys:
+            keys.append(k)
+    val = {(r["op"], r["depth"], r["policy"], r["num_cus"]): r["GBs"] for r in recs}
+    out = [f"# {args.title}"] + [f"# command: {c}" for c in args.command] + [
+        "# GB/s of bytes moved (copy: read + write; mixes: both sides), 1 GiB buffers, mean of 10 launches; "
+        "budget 0 = the probe's ordinary grid on every CU", "",
+        f"{'op':<9s} {'depth':>5s} {'policy':<7s} " + " ".join(f"{('all' if b == 0 else str(b)):>7s}" for b in budgets)]
+    for op, d, pol in keys:
+        out.append(f"{op:<9s} {d:5d} {pol:<7s} " + " ".join(
+            f"{val[(op, d, pol, b)]:7.0f}" if (op, d, pol, b) in val else f"{'-':>7s}" for b in budgets))
     sys.stdout.write("\n".join(out) + "\n")
 
 
@@ -247,12 +375,28 @@ def main(argv=None):
     w.add_argument("jsonl", nargs="+")
     w.add_argument("--title", default="")
     w.add_argument("--command", action="append", default=[])
+    bu = sub.add_parser("budgets")
+    bu.add_argument("--run", action="append", required=True,
+                    help="LABEL:CUS:FETCH_CSV:WRITE_CSV:SQ_CSV:BENCH_LOG, one per budget")
+    bu.add_argument("--title", default="")
+    bu.add_argument("--command", action="append", default=[])
+    bu.add_argument("--copy-bytes", type=int, default=256 << 20)
+    bu.add_argument("--xcds", type=int, default=8)
+    ov = sub.add_parser("overlap")
+    ov.add_argument("jsonl", nargs="+")
+    ov.add_argument("--title", default="")
+    ov.add_argument("--command", action="append", default=[])
+    pr = sub.add_parser("probes")
+    pr.add_argument("jsonl", nargs="+")
+    pr.add_argument("--title", default="")
+    pr.add_argument("--command", action="append", default=[])
     lt = sub.add_parser("latency")
     lt.add_argument("jsonl", nargs="+")
     lt.add_argument("--title", default="")
     lt.add_argument("--command", action="append", default=[])
     args = p.parse_args(argv)
-    {"trace": trace, "hbm": hbm, "sq": sq, "sweep": sweep_table, "latency": latency_table}[args.mode](args)
+    {"trace": trace, "hbm": hbm, "sq": sq, "sweep": sweep_table, "latency": latency_table,
+     "budgets": budgets_table, "overlap": overlap_table, "probes": probes_table}[args.mode](args)
 
 
 if __name__ == "__main__":

@@ -645,6 +645,45 @@ def test_step_on_masked_stream(n):
         ep.ep_stream_destroy(stream)
 
 
+def test_step_on_24_cus_beside_matrix_core_work():
+    """The pages' premise in one test: the step (layout, dispatch, combine as
+    separate calls) on a stream masked to 24 CUs while the matrix-core probe
+    keeps the other CUs busy on a second masked stream, both launched before
+    either is waited for.  The step's outputs equal the oracle's, and the
+    compute kernel has not finished before the step was issued."""
+    ndev = torch.cuda.get_device_properties(0).multi_processor_count
+    comm = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(24)))
+    comp = ep.ep_stream_create_cu_masked(ep.cu_mask_words(range(24, ndev)))
+    try:
+        wl = workload("train")
+        c = wl.config
+        ref = oracle_layout("train")
+        recv = torch.empty((c.T * c.k, c.H), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+        idx, x, w = to_dev(wl.topk_idx), to_dev_bf16(wl.x), to_dev(wl.topk_w)
+        y = to_dev_bf16(expert_outputs("train"))
+        groups = (ndev - 24) * 8
+        mfma_out = torch.zeros(256 * groups, dtype=torch.float32, device=DEV)
+        done = torch.cuda.Event()
+        torch.cuda.synchronize()
+        ep.ep_mfma_probe(groups, 4096, mfma_out, stream=comp)
+        done.record(comp)
+        lay = ep.ep_layout(idx, c.E, stream=comm)
+        ep.ep_dispatch(x, lay["dest_row"], recv, stream=comm)
+        ep.ep_combine(y, lay["dest_row"], w, out, stream=comm)
+        overlapped = not done.query()
+        torch.cuda.synchronize()
+        check_layout({k: v.cpu().numpy() for k, v in lay.items()}, ref, c.T, c.k)
+        np.testing.assert_array_equal(from_dev_bf16(recv), oracle_recv("train"))
+        assert_combine_close(from_dev_bf16(out), oracle_out("train"))
+        assert overlapped
+        assert int((mfma_out != 0).sum()) == 0
+    finally:
+        torch.cuda.synchronize()
+        ep.ep_stream_destroy(comm)
+        ep.ep_stream_destroy(comp)
+
+
 def test_k4_step_on_masked_stream():
     """k = 4 on a stream masked to 192 CUs: the one-launch layout + dispatch
     on k = 4's default budget and the phased combine with 2-vector runs, in
@@ -859,14 +898,21 @@ def test_layout_dispatch_decode_sizes(name, over, variant, budget):
     run_layout_dispatch(make_workload(name, seed=16, **over))
 
 
+# Under "lds1" the wide kernel takes every case it applies to; under "auto"
+# batches of at least 8 tokens per CU of the launch run the layout and the
+# default (streaming) dispatch instead.
 @pytest.mark.parametrize("name,over", WIDE_CASES)
 @pytest.mark.parametrize("budget", [0, 24, 256])
-def test_layout_dispatch_wide(name, over, budget):
+@pytest.mark.parametrize("variant", ["lds1", "auto"])
+def test_layout_dispatch_wide(name, over, budget, variant):
+    ep.ep_set_variant(variant)
     ep.ep_set_num_cus(budget)
     run_layout_dispatch(make_workload(name, seed=8, **over))
 
 
-def test_layout_dispatch_wide_prefill_full_size():
+@pytest.mark.parametrize("variant", ["lds1", "auto"])
+def test_layout_dispatch_wide_prefill_full_size(variant):
+    ep.ep_set_variant(variant)
     run_layout_dispatch(workload("prefill"))
 
 

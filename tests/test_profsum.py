@@ -78,8 +78,8 @@ def test_sweep_table_lists_step_records(tmp_path, capsys):
     out = capsys.readouterr().out.splitlines()
     assert out[:3] == ["# t", "# command: c1", "# command: c2"]
     rows = [line.split() for line in out if line and line[0] != "#" and not line.lstrip().startswith("k ")]
-    assert rows == [["2", "16384", "7168", "256", "lds1", "0", "96", "7012", "5401"],
-                    ["8", "128", "7168", "256", "vgpr", "2", "0", "-", "812"]]
+    assert rows == [["2", "16384", "7168", "256", "lds1", "0", "96", "7012", "5401", "-", "-", "-"],
+                    ["8", "128", "7168", "256", "vgpr", "2", "0", "-", "812", "-", "-", "-"]]
 
 
 def test_bench_shape_overrides():
@@ -111,3 +111,41 @@ def test_latency_table_formats_every_record_kind(tmp_path, capsys):
     text = capsys.readouterr().out
     assert "# command: c" in text
     assert "420.0" in text and "1387.4" in text and "35.1" in text and "86.05" in text
+
+
+def test_budgets_table_scales_sums_per_call(tmp_path, capsys):
+    """Per-budget counter table: FETCH/WRITE sums per kind over the calls,
+    scaled by the copy probe's reading, and SQ medians per kind."""
+    import json
+
+    from bulk_async_tensor_amd import profsum
+
+    disp = "void ep::(anonymous namespace)::dispatch_vgpr2_kernel<14, 6, true, true>(args)"
+    copy = "void ep::(anonymous namespace)::bw_kernel<0, 8, 0>(args)"
+
+    def counters(path, name, rows):
+        with open(path, "w") as fh:
+            fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for i, (kern, val) in enumerate(rows):
+                fh.write(f'{i},"{kern}",{name},{val}\n')
+
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    q = tmp_path / "q.csv"
+    # copy probe: FETCH reads half the true 256 MiB, WRITE reads it exactly
+    counters(f, "FETCH_SIZE", [(copy, 131072.0), (disp, 100.0), (disp, 300.0)])
+    counters(w, "WRITE_SIZE", [(copy, 262144.0), (disp, 1000.0), (disp, 1000.0)])
+    with open(q, "w") as fh:
+        fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i in (1, 2):
+            for name, val in (("GRBM_GUI_ACTIVE", 8000.0), ("SQ_LDS_BANK_CONFLICT", 0.0),
+                              ("SQ_ACTIVE_INST_VALU", 256000.0 * i)):
+                fh.write(f'{i},"{disp}",{name},{val}\n')
+    log = tmp_path / "b.log"
+    log.write_text(json.dumps({"cold_only": True, "steps": 1, "warmup": 1, "bytes": {"dispatch": 4096000}}) + "\n")
+    profsum.main(["budgets", "--run", f"all:256:{f}:{w}:{q}:{log}", "--title", "t"])
+    row = [line.split() for line in capsys.readouterr().out.splitlines() if line.startswith("all ")][0]
+    # (400 KiB x 2 + 2000 KiB x 1) x 1024 / 2 calls = 1,433,600 bytes -> 1.43 MB, ratio 0.35
+    assert row[:8] == ["all", "dispatch", "1", "0.41", "1.02", "1.43", "4.10", "0.3500"]
+    # VALU busy: median of 256000 and 512000 over 256 CUs and GUI 1000 -> 150%
+    assert row[9] == "150.00"
