@@ -522,9 +522,33 @@ int ep_stream_create_cu_masked(const uint32_t* mask, int mask_words, void** stre
   uint32_t any = 0;
   for (int i = 0; i < mask_words; ++i) any |= mask[i];
   if (!any) return fail(EP_ERR_INVALID_ARG, "ep_stream_create_cu_masked: empty mask");
+  // The runtime numbers CUs round-robin over the XCDs (bit i selects a CU of
+  // XCD i mod the XCD count; measured on MI355X with the placement probe),
+  // and a masked stream's queue runs on every XCD: a mask that leaves an XCD
+  // without a CU is refused, with an error that the next HIP call would
+  // also report.  Check it here first.
+  int dev = 0, cus = 0, xccs = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && xccs > 1 && cus > 0) {
+    for (int x = 0; x < xccs; ++x) {
+      bool has = false;
+      for (int i = x; i < cus && i < 32 * mask_words && !has; i += xccs) has = (mask[i / 32] >> (i % 32)) & 1u;
+      if (!has)
+        return fail(EP_ERR_INVALID_ARG,
+                    "ep_stream_create_cu_masked: no CU of XCD %d in the mask (bit i selects a CU of XCD i mod %d; "
+                    "every XCD needs one)",
+                    x, xccs);
+    }
+  } else {
+    (void)hipGetLastError();
+  }
   hipStream_t s = nullptr;
   hipError_t e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask_words, mask);
-  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask");
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the refusal for the next HIP call to report
+    return hip_fail(e, "hipExtStreamCreateWithCUMask");
+  }
   *stream = s;
   return EP_OK;
 }

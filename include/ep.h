@@ -409,6 +409,16 @@ int ep_mfma_probe(int n_groups, int iters, float* out, void* stream);
  * CU numbering).  *stream receives the hipStream_t handle; the caller
  * releases it with ep_stream_destroy.  Returns EP_OK, EP_ERR_INVALID_ARG
  * (null pointers, mask_words outside [1, 64], an empty mask) or EP_ERR_HIP.
+ * On MI355X (8 XCDs of 32 CUs) the runtime's numbering interleaves the
+ * XCDs: bit i selects a CU of XCD i mod 8, so any 8 consecutive bits hold
+ * one CU of every XCD and bits 32 apart land on the same XCD (placement
+ * measured with ep_probe_placement).  A masked stream's queue runs on every
+ * XCD, and the runtime refuses a mask that leaves some XCD without a CU
+ * (hipExtStreamCreateWithCUMask reports "out of memory" for the 8-CU mask
+ * {0, 32, ..., 224}, all on XCD 0, or for {0, 1, 2, 3}); this call checks
+ * that first, with the XCD count the device reports, and returns
+ * EP_ERR_INVALID_ARG for such a mask.  Masks built from consecutive bits
+ * reach every XCD evenly once they hold 8 or more bits.
  */
 int ep_stream_create_cu_masked(const uint32_t* mask, int mask_words, void** stream);
 int ep_stream_destroy(void* stream);

@@ -619,6 +619,34 @@ def test_cu_masked_stream_confines_work():
         ep.ep_stream_destroy(stream)
 
 
+def test_cu_mask_bits_interleave_over_the_xcds():
+    """Mask bit i selects a CU of XCD i mod 8: eight consecutive bits give one
+    CU on each XCD, and bits 8 apart stay on one XCD's CUs while the mask as
+    a whole still reaches every XCD (masks that leave an XCD without CUs are
+    refused on the host, before the runtime sees them)."""
+    for bits in (range(4), [32 * i for i in range(8)]):
+        with pytest.raises(ep.EpError) as exc:
+            ep.ep_stream_create_cu_masked(ep.cu_mask_words(bits))
+        assert exc.value.code == ep.EP_ERR_INVALID_ARG and "XCD" in str(exc.value)
+    torch.zeros(16, device=DEV)  # no error was left behind for the next HIP call
+    torch.cuda.synchronize()
+    for bits, want in ((range(8), [1] * 8), (list(range(8)) + [8, 16, 24], [4, 1, 1, 1, 1, 1, 1, 1]),
+                       (range(24), [3] * 8)):
+        stream = ep.ep_stream_create_cu_masked(ep.cu_mask_words(bits))
+        try:
+            groups = 64
+            out = torch.full((groups, 4), -1, dtype=torch.int32, device=DEV)
+            ep.ep_probe_placement(out, groups, stream=stream)
+            stream.synchronize()
+            rows = {tuple(r) for r in out.cpu().numpy()[:, :3].tolist()}
+            per_xcc = np.bincount([r[0] for r in rows], minlength=8).tolist()
+            print(f"mask bits {list(bits)}: distinct CUs per XCD {per_xcc}", flush=True)
+            assert per_xcc == want
+        finally:
+            torch.cuda.synchronize()
+            ep.ep_stream_destroy(stream)
+
+
 @pytest.mark.parametrize("n", [24, 128])
 def test_step_on_masked_stream(n):
     """Layout, dispatch (in one launch) and combine on a stream masked to n
