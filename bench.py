@@ -213,46 +213,6 @@ class Setup:
         return ms, per
 
 
-def probe_ceilings():
-    """Streaming ceilings of this device in the same run (ep_bw_probe), for
-    the dispatch and combine launches the step uses: plain writes on the
-    dispatch's 64 CUs (8 and 32 KiB contiguous per wave), and on every CU the
-    phased 8:1 mix (each wave reads 128 KiB, then writes 16 KiB, once).  GB/s
-    of bytes moved, best of three timings of 10 launches."""
-    import torch
-
-    import bulk_async_tensor_amd as ep
-
-    n = 1 << 30
-    ndev = torch.cuda.get_device_properties(0).multi_processor_count
-    a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
-    b = torch.empty_like(a)
-
-    def rate(mode, nb, budget):
-        ep.ep_set_num_cus(budget)
-        for _ in range(3):
-            ep.ep_bw_probe(mode, a, b, nb)
-        best = None
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                ep.ep_bw_probe(mode, a, b, nb)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 10
-            best = ms if best is None else min(best, ms)
-        moved = nb + nb // 8 if (mode & 7) == 7 else nb
-        return moved / best / 1e6
-
-    try:
-        out = {"write_64cus": rate(2, n, 64), "write32_64cus": rate(0x22, n, 64),
-               "mix8to1_phase_once_all_cus": rate(7, min(n, ndev * 16 * (128 << 10)), 0)}
-    finally:
-        ep.ep_set_num_cus(0)
-    return {k: round(v, 1) for k, v in out.items()}
-
-
 def cold_times(s, iters, flush_mode="write"):
     """Per-launch times with cold caches: before each launch 1 GiB of other
     memory is written (torch fill), read (the read probe) or both, which
