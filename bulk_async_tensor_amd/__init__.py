@@ -27,7 +27,7 @@ EP_STATUS_DUPLICATE_EXPERT = 2
 EP_MAX_TOPK = 32
 EP_MAX_EXPERTS = 1024
 
-VARIANTS = ("auto", "vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached", "phase", "lds3", "pc")
+VARIANTS = ("auto", "vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached", "phase", "lds3", "pc", "vgpr_wg")
 
 _c_int, _c_i64, _c_sz, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 

@@ -656,7 +656,7 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
                           const int32_t* dest_row, const float* w, int T, int k, void* out, hipStream_t stream) {
   const int row_vec = H / 8;
   if (recv_rows == 0) return launch_combine_zero(b, out, (int64_t)T * row_vec, stream);
-  if (v == Variant::Lds3 || v == Variant::Pc) v = Variant::Auto;  // dispatch-only variants
+  if (v == Variant::Lds3 || v == Variant::Pc || v == Variant::VgprWg) v = Variant::Auto;  // dispatch-only variants
   if (v == Variant::Auto) v = phase_preferred(b, row_vec, T, k) ? Variant::Phase : Variant::Vgpr;
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if (!known_k) v = Variant::Vgpr;  // the any-k kernel

@@ -134,6 +134,37 @@ __global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) 
   }
 }
 
+// The register kernel with each workgroup reading in step: every wave loads
+// its unit and waits for the loads, then the workgroup meets at a barrier
+// before any wave stores.  A CU's loads queue behind its own stores in its
+// memory pipeline; on a small CU budget, where each CU's outstanding reads
+// bound the copy, the barrier keeps more of a CU's reads out of that queue.
+// Every wave makes the workgroup's trip count, so each barrier is met by all
+// of its waves.
+template <int VPL, int K, bool EVEN, bool NT>
+__global__ __launch_bounds__(1024) void dispatch_wg_kernel(EP_DISPATCH_ARGS) {
+  const int k = K > 0 ? K : k_rt;
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  const int first = blockIdx.x * wpg;
+  if (first >= units) return;  // the same for every wave of the workgroup
+  const int trips = (units - first + stride - 1) / stride;
+  for (int r = 0; r < trips; ++r) {
+    const int u = first + r * stride + wave_in_group();
+    const bool live = u < units;
+    const Unit un = unit_of<VPL>(live ? u : first, nslab, row_vec, lane);
+    const int32_t* dr = dest_row + un.t * k;
+    Dests<K> ds;
+    fetch_dests<K>(ds, dr);
+    u32x4 v[VPL];
+    load_slab<VPL, EVEN, NT>(v, x + un.t * row_vec, un, row_vec);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (live) store_slab<VPL, K, EVEN, NT>(v, recv, ds, dr, k, recv_rows, un, row_vec);
+  }
+}
+
 template <int VPL, int K, bool EVEN, bool NT>
 __global__ __launch_bounds__(1024) void dispatch_lds1_kernel(EP_DISPATCH_ARGS) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -367,6 +398,7 @@ DispatchFn pick_kind(Variant v) {
     case Variant::VgprCached: return dispatch_vgpr_kernel<VPL, K, EVEN, false>;
     case Variant::Lds1: return dispatch_lds1_kernel<VPL, K, EVEN, true>;
     case Variant::Pc: return dispatch_pc_kernel<VPL, K, EVEN, true>;
+    case Variant::VgprWg: return dispatch_wg_kernel<VPL, K, EVEN, true>;
     default: break;
   }
   // the register double buffer holds two slabs: compiled up to 14 vectors
@@ -592,29 +624,31 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 
 // The default for a batch of at least 8 tokens per CU of its launch: a
 // persistent grid on every CU it may use (the budget, the stream's mask or
-// the device) with whole-row slabs and a kernel that keeps the next rows'
-// loads in flight while it stores: the register double buffer (vgpr2) on at
-// least half the device, the producer/consumer split (pc, an issuer wave
-// with four rows in flight per CU) on fewer CUs, where each CU's outstanding
-// reads are the bound.  Their loads of x take about the same time whether x
-// is in the Infinity Cache or not.  The LDS-staged kernels load x with
-// cacheable direct-to-LDS loads: fastest on 64 CUs while x is cached, up to
-// 2.5x slower when it is not (each miss then fills the Infinity Cache).
-// Measured at H = 7168, single launches after a 1 GiB write that evicts x
-// and without it (x cached):
-//   T = 4096, k = 8, all CUs: vgpr2 105.7 / 103.7 us, lds1 on 64 CUs
-//     193.6 / 87.9; T = 16384, k = 6, E = 64: 339.4 / 335.3 against
+// the device) with whole-row slabs, loading x with streaming loads: the
+// register double buffer (vgpr2) on at least half the device, the
+// workgroup-phased register kernel (vgpr_wg) on fewer CUs, where each CU's
+// outstanding reads are the bound and a CU's reads would otherwise queue
+// behind its own stores.  Their times hardly depend on whether x is in the
+// Infinity Cache.  The LDS-staged kernels (lds1, pc) load x with cacheable
+// direct-to-LDS loads: faster while x is cached, up to 2.5x slower when it
+// is not (each miss then fills the Infinity Cache).  Measured at H = 7168,
+// single launches after a 1 GiB write that evicts x, and without it (x
+// cached), cold / warm in us:
+//   T = 4096, k = 8, all CUs: vgpr2 105.7 / 103.7, lds1 on 64 CUs
+//     193.6 / 87.9; T = 16384, k = 6, E = 64: vgpr2 339.4 / 335.3, lds1
 //     647.3 / 258.2 (and 322 against 589 us when x was written just before
 //     the dispatch, which leaves only part of its 235 MB cached);
-//   24 CUs, T = 4096: pc 286.7 / 201.6 us, vgpr2 320.2 / 316.4, lds1
-//     352.6 / 192.6; 64 CUs: pc 149.7 / 94.6, vgpr2 167.5 / 164.6, lds1
-//     194.5 / 88.9; 128 CUs: vgpr2 117.1 / 116.9, lds1 127.4 / 94.9.
-// Callers whose x is cache-resident can ask for "lds1".
+//   24 CUs: vgpr_wg 245.7 / 244.8 (T = 4096) and 777.4 / 774.9
+//     (T = 16384), pc 288.5 / 201.0 and 973.8 / 645.4, vgpr2 320.2 / 316.4
+//     (T = 4096); 64 CUs: vgpr_wg 129.9 / 126.7 and 450.7 / 449.9, pc
+//     149.7 / 94.9 and 537.6 / 270.0; 128 CUs: vgpr2 111.0 and 379.4,
+//     vgpr_wg 113.0 and 352.6 (cold).
+// Callers whose x is cache-resident can ask for "lds1" or "pc".
 Variant dispatch_auto(const Budget& b, int64_t T, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (!dispatch_auto_large(b, T)) return Variant::Lds1;
   *persistent_cus = cus;
-  return 2 * cus >= b.all_cus ? Variant::Vgpr2 : Variant::Pc;
+  return 2 * cus >= b.all_cus ? Variant::Vgpr2 : Variant::VgprWg;
 }
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
@@ -626,15 +660,15 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const int row_vec = H / 8;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
-  // Slabs: the register double buffer and the producer/consumer split take
-  // whole rows of up to 14 KiB (T = 4096, H = 7168, x evicted: vgpr2 on all
+  // Slabs: the register double buffer, the workgroup-phased register kernel
+  // and the producer/consumer split take whole rows of up to 14 KiB (T = 4096, H = 7168, x evicted: vgpr2 on all
   // CUs 105.7 against 106.7 us with half rows; pc on 24 CUs 286.7 against
   // 311.8 us).  The other staged kernels take at most 8 KiB (half rows at
   // H = 7168; whole 14 KiB rows measured no faster), the LDS rings holding
   // two or three slabs.  A requested size may go to 16 for the single-set
   // kernels.
   const bool ring = v == Variant::Lds2 || v == Variant::Lds3;
-  const int cap = v == Variant::Vgpr2 ? 14
+  const int cap = (v == Variant::Vgpr2 || v == Variant::VgprWg) ? 14
                 : v == Variant::Pc ? (b.slab_vpl > 0 ? 16 : 14)
                 : (ring || b.slab_vpl == 0) ? 8 : 16;
   const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);

@@ -194,7 +194,8 @@ int ep_set_variant(const char* name) {
     ep::Variant v;
   } table[] = {{"auto", ep::Variant::Auto}, {"vgpr", ep::Variant::Vgpr}, {"vgpr2", ep::Variant::Vgpr2},
                {"lds1", ep::Variant::Lds1}, {"lds2", ep::Variant::Lds2}, {"vgpr_cached", ep::Variant::VgprCached},
-               {"phase", ep::Variant::Phase}, {"lds3", ep::Variant::Lds3}, {"pc", ep::Variant::Pc}};
+               {"phase", ep::Variant::Phase}, {"lds3", ep::Variant::Lds3}, {"pc", ep::Variant::Pc},
+               {"vgpr_wg", ep::Variant::VgprWg}};
   for (const auto& e : table) {
     if (strcmp(e.name, name) == 0) {
       g_variant.store(static_cast<int>(e.v));
@@ -214,6 +215,7 @@ const char* ep_get_variant(void) {
     case ep::Variant::Phase: return "phase";
     case ep::Variant::Lds3: return "lds3";
     case ep::Variant::Pc: return "pc";
+    case ep::Variant::VgprWg: return "vgpr_wg";
     default: return "auto";
   }
 }

@@ -7,7 +7,18 @@
 
 namespace ep {
 
-enum class Variant : int { Auto = 0, Vgpr = 1, Vgpr2 = 2, Lds1 = 3, Lds2 = 4, VgprCached = 5, Phase = 6, Lds3 = 7, Pc = 8 };
+enum class Variant : int {
+  Auto = 0,
+  Vgpr = 1,
+  Vgpr2 = 2,
+  Lds1 = 3,
+  Lds2 = 4,
+  VgprCached = 5,
+  Phase = 6,
+  Lds3 = 7,
+  Pc = 8,
+  VgprWg = 9
+};
 
 // Launch geometry chosen by the host for the row-movement kernels.
 struct Budget {

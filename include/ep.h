@@ -93,13 +93,18 @@ int ep_get_num_cus(void);
 
 /*
  * Kernel variant for dispatch and combine (process-wide):
- *   "auto"  the default choice per shape.  A large dispatch on the whole
- *           device takes "vgpr2" with whole-row slabs on every CU, whose
- *           time does not depend on the cache state of x (T = 16384,
- *           H = 7168, k = 6: about 335 us whether or not x was evicted);
- *           "lds1" on 64 CUs is faster while x is still in the Infinity
- *           Cache (about 258 us) and much slower once it is not (about
- *           650 us), so a caller that has just written x may prefer it;
+ *   "auto"  the default choice per shape.  A dispatch of at least 8 tokens
+ *           per CU of its launch runs as a persistent grid on every CU it
+ *           may use, with whole-row slabs and streaming loads of x: "vgpr2"
+ *           on at least half the device, "vgpr_wg" on fewer CUs.  Their
+ *           times hardly depend on whether x is still cached (T = 16384,
+ *           H = 7168, k = 6: about 340 us on the whole device, about
+ *           780 us on 24 CUs, evicted or not).  "lds1" (64 CUs) and "pc"
+ *           (the budget's CUs) load x with cacheable loads: faster while x
+ *           is in the Infinity Cache (about 258 us on 64 CUs, 645 us on
+ *           24), much slower once it is not (about 650 and 975 us), so a
+ *           caller that has just written x may prefer them.  Smaller
+ *           batches take "lds1";
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
  *           or k loads feeding one store (combine);
  *   "vgpr2" the same with the next work unit's loads issued before the
@@ -127,7 +132,13 @@ int ep_get_num_cus(void);
  *           two-slot ring and 3 to 8 consumer waves store the slabs, in
  *           step through workgroup barriers (the elected issuer of
  *           [DeepEP-TMA] "Asynchronous Copy Primitives" as a whole wave);
- *           always a persistent grid of one workgroup per CU.
+ *           always a persistent grid of one workgroup per CU;
+ *   "vgpr_wg" (dispatch; combine takes its default) "vgpr" with each
+ *           workgroup in step: every wave loads its slab and waits for it,
+ *           the workgroup meets at a barrier, then every wave stores.  A
+ *           CU's loads then do not queue behind its own stores, which pays
+ *           on a small CU budget, where each CU's outstanding reads bound
+ *           the copy.
  * lds2, lds3 and phase need k in {2, 4, 6, 8}; for other k dispatch runs lds1.
  * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
  */

@@ -133,7 +133,7 @@ def test_dispatch_full_size(name):
     np.testing.assert_array_equal(got, oracle_recv(name))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "vgpr_cached", "phase"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "vgpr_cached", "phase", "vgpr_wg"])
 @pytest.mark.parametrize("budget", BUDGETS)
 def test_dispatch_variants_train(variant, budget):
     ep.ep_set_variant(variant)
@@ -143,7 +143,7 @@ def test_dispatch_variants_train(variant, budget):
     np.testing.assert_array_equal(got, oracle_recv("train"))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "phase"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "phase", "vgpr_wg"])
 @pytest.mark.parametrize("H", [8, 520, 1024, 4104, 7168, 7176, 8712, 16384])
 @pytest.mark.parametrize("k", [2, 3, 4, 6])
 @pytest.mark.parametrize("budget", [0, 24])
@@ -157,7 +157,7 @@ def test_dispatch_ragged_rows(variant, H, k, budget):
     np.testing.assert_array_equal(got, oracle.dispatch(wl.x, lay["dest_row"], T * k))
 
 
-@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc"])
+@pytest.mark.parametrize("variant", ["vgpr", "vgpr2", "lds1", "lds2", "lds3", "pc", "vgpr_wg"])
 @pytest.mark.parametrize("slab", [1, 2, 4, 7, 8, 14, 16])
 @pytest.mark.parametrize("budget", [0, 24])
 def test_dispatch_slab_sizes(variant, slab, budget):
@@ -189,6 +189,24 @@ def test_dispatch_phase_units(H, T, budget):
     lay = oracle.layout(wl.topk_idx, 32)
     dest = lay["dest_row"].copy()
     dest[T // 2, k - 1] = -1  # a slot whose row is never written
+    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
+    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
+# The workgroup-phased dispatch: several trips per wave with a ragged last
+# trip (waves past the last unit still meet every barrier), workgroups with
+# no unit at all, a dropped slot and a row outside the receive buffer.
+@pytest.mark.parametrize("T,H,k", [(1, 7168, 8), (333, 7168, 6), (1000, 520, 3), (257, 8712, 8), (64, 8, 2)])
+@pytest.mark.parametrize("budget", [0, 1, 3, 24, 256])
+def test_dispatch_vgpr_wg_trips(T, H, k, budget):
+    ep.ep_set_variant("vgpr_wg")
+    ep.ep_set_num_cus(budget)
+    wl = make_workload("prefill", seed=T + H + k, T=T, H=H, E=16, k=k)
+    lay = oracle.layout(wl.topk_idx, 16)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1
+    dest[T - 1, 0] = 1 << 30
     got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
     want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
     np.testing.assert_array_equal(got, want)
@@ -390,7 +408,7 @@ def test_combine_slab_sizes(variant, slab, budget):
         ep.ep_set_slab(0)
 
 
-@pytest.mark.parametrize("variant", ["lds3", "pc"])
+@pytest.mark.parametrize("variant", ["lds3", "pc", "vgpr_wg"])
 def test_combine_under_dispatch_only_variants(variant):
     # these name dispatch kernels only; combine runs its default
     ep.ep_set_variant(variant)
