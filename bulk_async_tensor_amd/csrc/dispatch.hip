@@ -135,33 +135,53 @@ __global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) 
 }
 
 // The register kernel with each workgroup reading in step: every wave loads
-// its unit and waits for the loads, then the workgroup meets at a barrier
+// kWgUnits units and waits for them, then the workgroup meets at a barrier
 // before any wave stores.  A CU's loads queue behind its own stores in its
 // memory pipeline; on a small CU budget, where each CU's outstanding reads
-// bound the copy, the barrier keeps more of a CU's reads out of that queue.
-// Every wave makes the workgroup's trip count, so each barrier is met by all
-// of its waves.
+// bound the copy, the barrier keeps a CU's reads out of that queue, and two
+// rows per wave (in workgroups of 8 waves) make each read burst and each
+// write burst twice as long for the same number of barriers.  Every wave
+// makes the workgroup's trip count, so each barrier is met by all of its
+// waves.
+constexpr int kWgUnits = 2;
+constexpr int kWgWaves = 8;
+
 template <int VPL, int K, bool EVEN, bool NT>
-__global__ __launch_bounds__(1024) void dispatch_wg_kernel(EP_DISPATCH_ARGS) {
+__global__ __launch_bounds__(kWgWaves * kWave) void dispatch_wg_kernel(EP_DISPATCH_ARGS) {
   const int k = K > 0 ? K : k_rt;
   const int lane = lane_id();
   const int wpg = blockDim.x >> 6;
   const int stride = gridDim.x * wpg;
   const int first = blockIdx.x * wpg;
   if (first >= units) return;  // the same for every wave of the workgroup
-  const int trips = (units - first + stride - 1) / stride;
+  const int per_trip = stride * kWgUnits;
+  const int trips = (units - first + per_trip - 1) / per_trip;
   for (int r = 0; r < trips; ++r) {
-    const int u = first + r * stride + wave_in_group();
-    const bool live = u < units;
-    const Unit un = unit_of<VPL>(live ? u : first, nslab, row_vec, lane);
-    const int32_t* dr = dest_row + un.t * k;
-    Dests<K> ds;
-    fetch_dests<K>(ds, dr);
-    u32x4 v[VPL];
-    load_slab<VPL, EVEN, NT>(v, x + un.t * row_vec, un, row_vec);
+    Unit un[kWgUnits];
+    bool live[kWgUnits];
+    Dests<K> ds[kWgUnits];
+    u32x4 v[kWgUnits][VPL];
+#pragma unroll
+    for (int q = 0; q < kWgUnits; ++q) {
+      const int u = first + (r * kWgUnits + q) * stride + wave_in_group();
+      live[q] = u < units;
+      un[q] = unit_of<VPL>(live[q] ? u : first, nslab, row_vec, lane);
+      fetch_dests<K>(ds[q], dest_row + un[q].t * k);
+      // every load issued (vectors past the row end clamped, never stored)
+      load_slab_fixed<VPL, NT>(v[q], x + un[q].t * row_vec, un[q], row_vec);
+    }
+    // The barrier and wait builtins do not stop the compiler from sinking
+    // the loads below them, towards their first use: tying every loaded
+    // register to this point keeps all of them above the barrier.
+#pragma unroll
+    for (int q = 0; q < kWgUnits; ++q)
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) asm volatile("" : "+v"(v[q][i]));
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (live) store_slab<VPL, K, EVEN, NT>(v, recv, ds, dr, k, recv_rows, un, row_vec);
+#pragma unroll
+    for (int q = 0; q < kWgUnits; ++q)
+      if (live[q]) store_slab<VPL, K, EVEN, NT>(v[q], recv, ds[q], dest_row + un[q].t * k, k, recv_rows, un[q], row_vec);
   }
 }
 
@@ -638,11 +658,11 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 //     193.6 / 87.9; T = 16384, k = 6, E = 64: vgpr2 339.4 / 335.3, lds1
 //     647.3 / 258.2 (and 322 against 589 us when x was written just before
 //     the dispatch, which leaves only part of its 235 MB cached);
-//   24 CUs: vgpr_wg 245.7 / 244.8 (T = 4096) and 777.4 / 774.9
-//     (T = 16384), pc 288.5 / 201.0 and 973.8 / 645.4, vgpr2 320.2 / 316.4
-//     (T = 4096); 64 CUs: vgpr_wg 129.9 / 126.7 and 450.7 / 449.9, pc
-//     149.7 / 94.9 and 537.6 / 270.0; 128 CUs: vgpr2 111.0 and 379.4,
-//     vgpr_wg 113.0 and 352.6 (cold).
+//   24 CUs: vgpr_wg 224.7 / 217.4 (T = 4096) and 706.0 / 689.1
+//     (T = 16384), pc 288.5 / 201.0 and 973.8 / 645.4, vgpr2 319.0 / 318.2
+//     and 1066.5 / 1071.5; 64 CUs: vgpr_wg 122.1 / 119.8 and
+//     404.3 / 367.0, pc 149.7 / 94.9 and 537.6 / 270.0; 128 CUs: vgpr2
+//     108.5 and 379.5, vgpr_wg 109.9 and 355.1 (cold).
 // Callers whose x is cache-resident can ask for "lds1" or "pc".
 Variant dispatch_auto(const Budget& b, int64_t T, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
@@ -704,7 +724,8 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
     if (lds_bytes < kExclusiveLds) lds_bytes = kExclusiveLds;
   } else if (budget > 0) {
     // persistent: one workgroup per CU, as many waves as the LDS ring allows
-    wpg = 16;
+    // (the workgroup-phased kernel: its own workgroup size)
+    wpg = v == Variant::VgprWg ? kWgWaves : 16;
     if (per_wave && (int)(kLdsPerCu / per_wave) < wpg) wpg = (int)(kLdsPerCu / per_wave);
     grid = budget < b.device_cus ? budget : b.device_cus;
     lds_bytes = per_wave * wpg;
