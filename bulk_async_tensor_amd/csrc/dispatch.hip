@@ -135,53 +135,165 @@ __global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) 
 }
 
 // The register kernel with each workgroup reading in step: every wave loads
-// kWgUnits units and waits for them, then the workgroup meets at a barrier
-// before any wave stores.  A CU's loads queue behind its own stores in its
-// memory pipeline; on a small CU budget, where each CU's outstanding reads
-// bound the copy, the barrier keeps a CU's reads out of that queue, and two
-// rows per wave (in workgroups of 8 waves) make each read burst and each
-// write burst twice as long for the same number of barriers.  Every wave
-// makes the workgroup's trip count, so each barrier is met by all of its
-// waves.
-constexpr int kWgUnits = 2;
-constexpr int kWgWaves = 8;
+// wg_units<VPL>() units and waits for them (and for their destination rows),
+// then the workgroup meets at a barrier before any wave stores.  A CU's loads
+// queue behind its own stores in its memory pipeline; the barrier keeps a
+// CU's reads out of that queue, and a few long read and write bursts per CU
+// (four whole rows per wave in workgroups of four waves) beat many short
+// ones.  Every wave makes the workgroup's trip count, so each barrier is met
+// by all of its waves.
+constexpr int kWgWaves = 4;
+
+constexpr int wg_units_of(int vpl) { return vpl > 14 ? 2 : 4; }  // at most 224 VGPRs of row data per lane
+
+template <int VPL>
+constexpr int wg_units() {
+  return wg_units_of(VPL);
+}
+
+// Loads of one slab for the workgroup-phased kernel, every one issued.  A row
+// that is a whole number of KiB needs no per-lane clamp: vectors past the
+// slab re-read the slab's last vector (a uniform offset), so one base address
+// per wave serves every load.  Other rows clamp per lane as load_slab_fixed.
+template <int VPL, bool EVEN, bool NT>
+__device__ __forceinline__ void load_slab_wg(u32x4 (&v)[VPL], const u32x4* __restrict__ src, const Unit& un,
+                                             int row_vec) {
+  if constexpr (EVEN) {
+    const u32x4* p = src + un.c0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int ii = i < un.nvec ? i : un.nvec - 1;
+      v[i] = ld16<NT>(p + ii * kWave);
+    }
+  } else {
+    load_slab_fixed<VPL, NT>(v, src, un, row_vec);
+  }
+}
 
 template <int VPL, int K, bool EVEN, bool NT>
 __global__ __launch_bounds__(kWgWaves * kWave) void dispatch_wg_kernel(EP_DISPATCH_ARGS) {
+  constexpr int U = wg_units<VPL>();
   const int k = K > 0 ? K : k_rt;
   const int lane = lane_id();
   const int wpg = blockDim.x >> 6;
   const int stride = gridDim.x * wpg;
   const int first = blockIdx.x * wpg;
   if (first >= units) return;  // the same for every wave of the workgroup
-  const int per_trip = stride * kWgUnits;
+  const int per_trip = stride * U;
   const int trips = (units - first + per_trip - 1) / per_trip;
   for (int r = 0; r < trips; ++r) {
-    Unit un[kWgUnits];
-    bool live[kWgUnits];
-    Dests<K> ds[kWgUnits];
-    u32x4 v[kWgUnits][VPL];
+    Unit un[U];
+    bool live[U];
+    Dests<K> ds[U];
+    u32x4 v[U][VPL];
 #pragma unroll
-    for (int q = 0; q < kWgUnits; ++q) {
-      const int u = first + (r * kWgUnits + q) * stride + wave_in_group();
+    for (int q = 0; q < U; ++q) {
+      const int u = first + (r * U + q) * stride + wave_in_group();
       live[q] = u < units;
       un[q] = unit_of<VPL>(live[q] ? u : first, nslab, row_vec, lane);
+      load_slab_wg<VPL, EVEN, NT>(v[q], x + un[q].t * row_vec, un[q], row_vec);
       fetch_dests<K>(ds[q], dest_row + un[q].t * k);
-      // every load issued (vectors past the row end clamped, never stored)
-      load_slab_fixed<VPL, NT>(v[q], x + un[q].t * row_vec, un[q], row_vec);
     }
     // The barrier and wait builtins do not stop the compiler from sinking
-    // the loads below them, towards their first use: tying every loaded
-    // register to this point keeps all of them above the barrier.
+    // loads below them, towards their first use: tying every loaded register
+    // and destination row to this point keeps all of them above the barrier
+    // (a destination fetched after it would delay the first store by a
+    // memory round trip).
 #pragma unroll
-    for (int q = 0; q < kWgUnits; ++q)
+    for (int q = 0; q < U; ++q) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i) asm volatile("" : "+v"(v[q][i]));
+      if constexpr (K > 0) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) asm volatile("" : "+s"(ds[q].d[j]));
+      }
+    }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int q = 0; q < kWgUnits; ++q)
+    for (int q = 0; q < U; ++q)
       if (live[q]) store_slab<VPL, K, EVEN, NT>(v[q], recv, ds[q], dest_row + un[q].t * k, k, recv_rows, un[q], row_vec);
+  }
+}
+
+// The workgroup-phased kernel for its common case: rows of exactly VPL KiB
+// (row_vec == VPL * 64) with k known at compile time.  A unit is a token; its
+// loads and stores are straight-line, with no per-vector row-end checks (one
+// wave runs per SIMD, so every extra instruction between the memory
+// operations costs issue time), and every workgroup makes the same `trips`.
+template <int VPL, int K, bool NT>
+__global__ __launch_bounds__(kWgWaves * kWave) void dispatch_wg_rows_kernel(const u32x4* __restrict__ x,
+                                                                            u32x4* __restrict__ recv,
+                                                                            const int32_t* __restrict__ dest_row,
+                                                                            int64_t recv_rows, int T, int trips) {
+  constexpr int U = wg_units<VPL>();
+  constexpr int RV = VPL * kWave;
+  const int lane = lane_id();
+  const int wpg = blockDim.x >> 6;
+  const int stride = gridDim.x * wpg;
+  const int first = blockIdx.x * wpg + wave_in_group();
+  for (int r = 0; r < trips; ++r) {
+    u32x4 v[U][VPL];
+    int32_t d[U][K];
+    bool live[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int t = first + (r * U + q) * stride;
+      live[q] = t < T;
+      const int64_t tc = live[q] ? t : 0;
+      const u32x4* src = x + tc * RV + lane;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) v[q][i] = ld16<NT>(src + i * kWave);
+#pragma unroll
+      for (int j = 0; j < K; ++j) d[q][j] = dest_row[tc * K + j];
+    }
+    // keeps every load and destination fetch above the barrier (see
+    // dispatch_wg_kernel)
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) asm volatile("" : "+v"(v[q][i]));
+#pragma unroll
+      for (int j = 0; j < K; ++j) asm volatile("" : "+s"(d[q][j]));
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (!live[q]) continue;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        if ((uint64_t)(int64_t)d[q][j] >= (uint64_t)recv_rows) continue;
+        u32x4* p = recv + (int64_t)d[q][j] * RV + lane;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) st16<NT>(p + i * kWave, v[q][i]);
+      }
+    }
+  }
+}
+
+using WgRowsFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, int);
+
+template <int VPL>
+WgRowsFn wg_rows_pick_k(int k) {
+  switch (k) {
+    case 2: return dispatch_wg_rows_kernel<VPL, 2, true>;
+    case 4: return dispatch_wg_rows_kernel<VPL, 4, true>;
+    case 6: return dispatch_wg_rows_kernel<VPL, 6, true>;
+    case 8: return dispatch_wg_rows_kernel<VPL, 8, true>;
+    default: return nullptr;
+  }
+}
+
+WgRowsFn wg_rows_pick(int vpl, int k) {
+  switch (vpl) {
+    case 2: return wg_rows_pick_k<2>(k);
+    case 4: return wg_rows_pick_k<4>(k);
+    case 7: return wg_rows_pick_k<7>(k);
+    case 8: return wg_rows_pick_k<8>(k);
+    case 14: return wg_rows_pick_k<14>(k);
+    case 16: return wg_rows_pick_k<16>(k);
+    default: return nullptr;
   }
 }
 
@@ -644,31 +756,26 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 
 // The default for a batch of at least 8 tokens per CU of its launch: a
 // persistent grid on every CU it may use (the budget, the stream's mask or
-// the device) with whole-row slabs, loading x with streaming loads: the
-// register double buffer (vgpr2) on at least half the device, the
-// workgroup-phased register kernel (vgpr_wg) on fewer CUs, where each CU's
-// outstanding reads are the bound and a CU's reads would otherwise queue
-// behind its own stores.  Their times hardly depend on whether x is in the
-// Infinity Cache.  The LDS-staged kernels (lds1, pc) load x with cacheable
-// direct-to-LDS loads: faster while x is cached, up to 2.5x slower when it
-// is not (each miss then fills the Infinity Cache).  Measured at H = 7168,
-// single launches after a 1 GiB write that evicts x, and without it (x
-// cached), cold / warm in us:
-//   T = 4096, k = 8, all CUs: vgpr2 105.7 / 103.7, lds1 on 64 CUs
-//     193.6 / 87.9; T = 16384, k = 6, E = 64: vgpr2 339.4 / 335.3, lds1
-//     647.3 / 258.2 (and 322 against 589 us when x was written just before
-//     the dispatch, which leaves only part of its 235 MB cached);
-//   24 CUs: vgpr_wg 224.7 / 217.4 (T = 4096) and 706.0 / 689.1
-//     (T = 16384), pc 288.5 / 201.0 and 973.8 / 645.4, vgpr2 319.0 / 318.2
-//     and 1066.5 / 1071.5; 64 CUs: vgpr_wg 122.1 / 119.8 and
-//     404.3 / 367.0, pc 149.7 / 94.9 and 537.6 / 270.0; 128 CUs: vgpr2
-//     108.5 and 379.5, vgpr_wg 109.9 and 355.1 (cold).
+// the device) running the workgroup-phased register kernel (vgpr_wg) with
+// whole-row slabs and streaming loads of x.  Its time hardly depends on
+// whether x is in the Infinity Cache.  The LDS-staged kernels (lds1, pc)
+// load x with cacheable direct-to-LDS loads: faster while x is cached, up to
+// 2.5x slower when it is not (each miss then fills the Infinity Cache).
+// Measured at H = 7168, single launches after a 1 GiB write that evicts x
+// (cold), and without it (warm), in us, for T = 4096, k = 8 and
+// T = 16384, k = 6, E = 64:
+//   all CUs: vgpr_wg 105.1 / 101.9 and 334.2 / 332.7; vgpr2 107.5 / 104.7
+//     and 344.4 / 339.7; lds1 on 64 CUs 193.6 / 87.9 and 647.3 / 258.2;
+//   24 CUs: vgpr_wg 209.3 / 207.7 and 661.8 / 661.2; pc 288.5 / 201.0 and
+//     973.8 / 645.4; vgpr2 321.7 / 319.1 and 1068.4 / 1069.4;
+//   64 CUs: vgpr_wg 122.5 / 122.1 and 366.1 / 365.5; pc 149.7 / 94.9 and
+//     537.6 / 270.0.
 // Callers whose x is cache-resident can ask for "lds1" or "pc".
 Variant dispatch_auto(const Budget& b, int64_t T, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (!dispatch_auto_large(b, T)) return Variant::Lds1;
   *persistent_cus = cus;
-  return 2 * cus >= b.all_cus ? Variant::Vgpr2 : Variant::VgprWg;
+  return Variant::VgprWg;
 }
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
@@ -688,13 +795,17 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // two or three slabs.  A requested size may go to 16 for the single-set
   // kernels.
   const bool ring = v == Variant::Lds2 || v == Variant::Lds3;
-  const int cap = (v == Variant::Vgpr2 || v == Variant::VgprWg) ? 14
+  const int cap = v == Variant::VgprWg ? 16
+                : v == Variant::Vgpr2 ? 14
                 : v == Variant::Pc ? (b.slab_vpl > 0 ? 16 : 14)
                 : (ring || b.slab_vpl == 0) ? 8 : 16;
   const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;
+  // the workgroup-phased kernel's common case: whole rows of exactly vpl KiB
+  const WgRowsFn rows_fn =
+      (v == Variant::VgprWg && nslab == 1 && row_vec == vpl * kWave) ? wg_rows_pick(vpl, k) : nullptr;
   DispatchFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
   if (!fn) return hipErrorInvalidValue;
 
@@ -743,6 +854,17 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
     lds_bytes = per_wave * wpg;
   }
   if (grid < 1) grid = 1;
+  if (rows_fn) {
+    if (lds_bytes > 64 * 1024) {
+      hipError_t e = allow_dynamic_lds((const void*)rows_fn, lds_bytes);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t per_trip = (int64_t)grid * wpg * wg_units_of(vpl);
+    const int trips = (int)((T + per_trip - 1) / per_trip);
+    hipLaunchKernelGGL(rows_fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x),
+                       static_cast<u32x4*>(recv), dest_row, recv_rows, T, trips);
+    return hipGetLastError();
+  }
   if (lds_bytes > 64 * 1024) {
     hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
     if (e != hipSuccess) return e;

@@ -94,15 +94,14 @@ int ep_get_num_cus(void);
 /*
  * Kernel variant for dispatch and combine (process-wide):
  *   "auto"  the default choice per shape.  A dispatch of at least 8 tokens
- *           per CU of its launch runs as a persistent grid on every CU it
- *           may use, with whole-row slabs and streaming loads of x: "vgpr2"
- *           on at least half the device, "vgpr_wg" on fewer CUs.  Their
- *           times hardly depend on whether x is still cached (T = 16384,
- *           H = 7168, k = 6: about 340 us on the whole device, about
- *           700 us on 24 CUs, evicted or not).  "lds1" (64 CUs) and "pc"
- *           (the budget's CUs) load x with cacheable loads: faster while x
- *           is in the Infinity Cache (about 258 us on 64 CUs, 645 us on
- *           24), much slower once it is not (about 650 and 975 us), so a
+ *           per CU of its launch runs "vgpr_wg" as a persistent grid on
+ *           every CU it may use, with whole-row slabs and streaming loads of
+ *           x.  Its time hardly depends on whether x is still cached
+ *           (T = 16384, H = 7168, k = 6: about 335 us on the whole device,
+ *           about 660 us on 24 CUs, evicted or not).  "lds1" (64 CUs) and
+ *           "pc" (the budget's CUs) load x with cacheable loads: faster
+ *           while x is in the Infinity Cache (about 258 us on 64 CUs, 645 us
+ *           on 24), much slower once it is not (about 650 and 975 us), so a
  *           caller that has just written x may prefer them.  Smaller
  *           batches take "lds1";
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
@@ -134,11 +133,11 @@ int ep_get_num_cus(void);
  *           [DeepEP-TMA] "Asynchronous Copy Primitives" as a whole wave);
  *           always a persistent grid of one workgroup per CU;
  *   "vgpr_wg" (dispatch; combine takes its default) "vgpr" with each
- *           workgroup in step: every wave loads two slabs and waits for
- *           them, the workgroup (8 waves) meets at a barrier, then every
- *           wave stores.  A CU's loads then do not queue behind its own
- *           stores, which pays on a small CU budget, where each CU's
- *           outstanding reads bound the copy.
+ *           workgroup in step: every wave loads four slabs (two of 16 KiB)
+ *           and waits for them, the workgroup (4 waves) meets at a barrier,
+ *           then every wave stores.  A CU's loads then do not queue behind
+ *           its own stores, and each CU alternates a few long read and
+ *           write bursts.
  * lds2, lds3 and phase need k in {2, 4, 6, 8}; for other k dispatch runs lds1.
  * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
  */
