@@ -305,9 +305,10 @@ def cold_report(s, iters, warmup):
 
 def budget_probes(budget):
     """Streaming ceilings (GB/s of bytes moved) on a persistent grid of
-    `budget` CUs: nt reads, 8 and 32 KiB-per-wave writes, the phased 8:1 mix
-    (combine's ratio) and the 1:8 mix (dispatch's).  Best of three timings
-    of 10 launches over 1 GiB."""
+    `budget` CUs: a plain copy (read and written bytes both counted), nt
+    reads, 8 and 32 KiB-per-wave writes, the phased 8:1 mix (combine's ratio)
+    and the 1:8 mix (dispatch's).  Best of three timings of 10 launches over
+    1 GiB."""
     import torch
 
     import bulk_async_tensor_amd as ep
@@ -319,8 +320,8 @@ def budget_probes(budget):
     out = {}
     ep.ep_set_num_cus(budget)
     try:
-        for mode, label, nb in ((1, "read", n), (2, "write", n), (0x22, "write32", n), (5, "mix1to8", n),
-                                (7, "mix8to1_phase_once", once)):
+        for mode, label, nb in ((0, "copy", n), (1, "read", n), (2, "write", n), (0x22, "write32", n),
+                                (5, "mix1to8", n), (7, "mix8to1_phase_once", once)):
             for _ in range(3):
                 ep.ep_bw_probe(mode, a, b, nb)
             best = None
@@ -333,7 +334,7 @@ def budget_probes(budget):
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
                 best = ms if best is None else min(best, ms)
-            moved = nb + nb // 8 if mode in (5, 7) else nb
+            moved = 2 * nb if mode == 0 else nb + nb // 8 if mode in (5, 7) else nb
             out[label] = round(moved / best / 1e6, 1)
     finally:
         ep.ep_set_num_cus(0)
@@ -1220,6 +1221,7 @@ def main():
         "probe_ceilings_GBs": probes_all,
         "frac_of_probe": {k: round(s.bytes[k] / (st[k]["p50"] * 1e3) / ref_all[k], 4) for k in kernels},
         "frac_of_probe_against": {"dispatch": "max(mix1to8, write)", "combine": "mix8to1_phase_once"},
+        "frac_of_copy_probe": {k: round(s.bytes[k] / (st[k]["p50"] * 1e3) / probes_all["copy"], 4) for k in kernels},
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
@@ -1250,6 +1252,8 @@ def main():
             "frac_of_probe_cold_p50": {k: round(s.bytes[k] / (cold_b["us_per_op"][k]["p50"] * 1e3) / ref_b[k], 4)
                                        for k in kernels},
             "frac_of_probe_against": {"dispatch": "max(mix1to8, write)", "combine": "read"},
+            "frac_of_copy_probe_cold_p50": {k: round(s.bytes[k] / (cold_b["us_per_op"][k]["p50"] * 1e3) / probes_b["copy"], 4)
+                                            for k in kernels},
             "frac_of_hbm_peak_cold": round(cold_b["value"] / HBM_PEAK_GBS, 4),
         }
         # ---- the same budget as a CU-masked stream with ordinary grids (warm)
