@@ -860,10 +860,24 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
       if (e != hipSuccess) return e;
     }
     const int64_t per_trip = (int64_t)grid * wpg * wg_units_of(vpl);
-    const int trips = (int)((T + per_trip - 1) / per_trip);
-    hipLaunchKernelGGL(rows_fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream, static_cast<const u32x4*>(x),
-                       static_cast<u32x4*>(recv), dest_row, recv_rows, T, trips);
-    return hipGetLastError();
+    // On at least half the device, where HBM is the bound, one launch per
+    // trip: the kernel boundary starts every CU's read burst together, which
+    // the per-workgroup barrier alone does not (T = 16384, k = 6 on 256 CUs,
+    // x evicted: 314.6 us in four launches against 337.4 in one).  On fewer
+    // CUs each CU's reads are the bound and a launch per trip only adds
+    // ramps (24 CUs: 743 against 666 us), so the grid stays persistent.
+    const bool per_trip_launch = 2 * (int64_t)grid >= b.all_cus;
+    const int64_t batch = per_trip_launch ? per_trip : (int64_t)T;
+    for (int64_t t0 = 0; t0 < T; t0 += batch) {
+      const int tb = (int)(T - t0 < batch ? T - t0 : batch);
+      const int trips = (int)((tb + per_trip - 1) / per_trip);
+      hipLaunchKernelGGL(rows_fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream,
+                         static_cast<const u32x4*>(x) + t0 * row_vec, static_cast<u32x4*>(recv), dest_row + t0 * k,
+                         recv_rows, tb, trips);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (lds_bytes > 64 * 1024) {
     hipError_t e = allow_dynamic_lds((const void*)fn, lds_bytes);
