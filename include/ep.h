@@ -97,8 +97,8 @@ int ep_get_num_cus(void);
  *           per CU of its launch runs "vgpr_wg" as a persistent grid on
  *           every CU it may use, with whole-row slabs and streaming loads of
  *           x.  Its time hardly depends on whether x is still cached
- *           (T = 16384, H = 7168, k = 6: about 335 us on the whole device,
- *           about 660 us on 24 CUs, evicted or not).  "lds1" (64 CUs) and
+ *           (T = 16384, H = 7168, k = 6: about 310 us on the whole device,
+ *           about 670 us on 24 CUs, evicted or not).  "lds1" (64 CUs) and
  *           "pc" (the budget's CUs) load x with cacheable loads: faster
  *           while x is in the Infinity Cache (about 258 us on 64 CUs, 645 us
  *           on 24), much slower once it is not (about 650 and 975 us), so a
@@ -137,7 +137,9 @@ int ep_get_num_cus(void);
  *           and waits for them, the workgroup (4 waves) meets at a barrier,
  *           then every wave stores.  A CU's loads then do not queue behind
  *           its own stores, and each CU alternates a few long read and
- *           write bursts.
+ *           write bursts.  On at least half the device a call is split into
+ *           one launch per such trip (a launch boundary starts every CU's
+ *           read burst together); on fewer CUs it is one persistent launch.
  * lds2, lds3 and phase need k in {2, 4, 6, 8}; for other k dispatch runs lds1.
  * Returns EP_OK or EP_ERR_UNSUPPORTED for an unknown name.
  */
