@@ -212,6 +212,24 @@ def test_dispatch_vgpr_wg_trips(T, H, k, budget):
     np.testing.assert_array_equal(got, want)
 
 
+# On at least half the device the workgroup-phased dispatch issues one
+# launch per trip (each launch offsets x and dest_row by the tokens before
+# it): several launches with a ragged last one, a dropped slot and a row
+# outside the receive buffer.
+@pytest.mark.parametrize("T,k,budget", [(5000, 6, 128), (9000, 8, 0), (4097, 6, 256), (12345, 2, 192)])
+def test_dispatch_vgpr_wg_launch_per_trip(T, k, budget):
+    ep.ep_set_num_cus(budget)
+    H = 7168
+    wl = make_workload("prefill", seed=T + k, T=T, H=H, E=64, k=k)
+    lay = oracle.layout(wl.topk_idx, 64)
+    dest = lay["dest_row"].copy()
+    dest[T // 3, k - 1] = -1
+    dest[T - 1, 0] = 1 << 30
+    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
+    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.parametrize("name", DISPATCH_CONFIGS)
 @pytest.mark.parametrize("variant,budget", [("auto", 0), ("vgpr_cached", 0), ("auto", 24), ("auto", 64)])
 def test_dispatch_rows_matches(name, variant, budget):
