@@ -580,15 +580,26 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
 }
 
 // The phase kernel is the default on at least half the device when each
-// of its launches gives at least two thirds of the waves of a full grid a
-// unit: it reads all rows of its unit before its first store, so a wave
-// with little work gains nothing (decode batches stay on the register
-// kernel), and on fewer CUs the per-CU read rate, not the read/write
-// turnaround, is the bound.  Measured at H = 7168 on 256 CUs: launches of
-// 61-63% of the grid ran 7-10% slower than the register kernel at k = 2, 6
-// and 8, and of 67-73% 2-4% faster at k = 4, 6 and 8.  At k = 2 and 4 it
-// needs runs of 2 vectors per read (see combine_phase_seg): with single
-// vectors the register kernel was 11-20% faster there.
+// of its launches gives enough of the waves of a full grid a unit: it reads
+// all rows of its unit before its first store, so a wave with little work
+// gains nothing (decode batches stay on the register kernel), and on fewer
+// CUs the per-CU read rate, not the read/write turnaround, is the bound.
+// Cold single calls against the register kernel, every CU, two runs each:
+//  - two rows per wave in 8-wave workgroups (k >= 6 at H = 4104..7168):
+//    two thirds.  H = 5120 at 45-60% of the grid 5-37% slower (k = 6 and
+//    8), at 65% 2% faster (k = 6) and 10% slower (k = 8); H = 7168, k = 8
+//    at 62.5% 7% slower and at 75% 4% faster; earlier at H = 7168, k = 6
+//    67% 4% faster, 55% 7% slower;
+//  - the 16-wave shape at k >= 4: nine twentieths.  H = 2048, 3072, 4096
+//    and k = 4, 6, 8 at 45-65%: 3-11% faster in every case; at 37.5%, k = 4
+//    3-6% slower (H = 1024, 2048, 7168);
+//  - the 16-wave shape at k = 2: three fifths.  At 55% 0.4% faster to 3.5%
+//    slower, at 60% 1% slower (H = 3072) to 4% faster, from 62.5% 2-5%
+//    faster (H = 1024 .. 7168).
+// On part of the device (128-192 CUs, not measured this way) the rule stays
+// at two thirds.  At k = 2 and 4 the kernel needs runs of 2 vectors per read
+// (see combine_phase_seg): with single vectors the register kernel was
+// 11-20% faster there.
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
@@ -597,7 +608,9 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (k <= 4 && seg_vec != 2) return false;
   const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
-  return units * 3 >= (int64_t)cus * ps.wpg * 2;
+  const int64_t slots = (int64_t)cus * ps.wpg;
+  if (cus >= b.all_cus && ps.held != kPhaseWideHeld) return k == 2 ? units * 5 >= slots * 3 : units * 20 >= slots * 9;
+  return units * 3 >= slots * 2;
 }
 
 using CombineFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int);

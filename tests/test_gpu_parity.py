@@ -406,6 +406,28 @@ def test_combine_phase_batches(T, budget, k):
     assert_combine_close(got, oracle.combine(wl.y, lay["dest_row"], wl.topk_w))
 
 
+# The default combine with every CU on both sides of its fill thresholds for
+# the phased kernel (the fraction of the grid's waves one launch gives a
+# unit): 16-wave shapes take it from 9/20 at k >= 4 and 3/5 at k = 2, the
+# two-row 8-wave shape from 2/3.  (H, k, T): H = 2048 holds four tokens per
+# unit (16384 per full launch), H = 3072 and 4096 two (8192), H = 5120 at
+# k = 8 two rows per wave in 8-wave workgroups (4096).
+@pytest.mark.parametrize(
+    "H,k,T",
+    [(2048, 4, 7000), (2048, 4, 8192), (4096, 8, 3686), (4096, 6, 4505), (3072, 2, 4600), (3072, 2, 4915),
+     (2048, 2, 9830), (5120, 8, 2457), (5120, 8, 2800)],
+)
+def test_combine_default_partial_fill(H, k, T):
+    ep.ep_set_variant("auto")
+    ep.ep_set_num_cus(0)
+    wl = make_workload("combine_stress", seed=H + k + T, T=T, H=H, E=64, k=k)
+    lay = oracle.layout(wl.topk_idx, 64)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1  # a slot that contributes nothing
+    got = run_combine(wl, wl.y, dest)
+    assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
+
+
 @pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2", "phase"])
 @pytest.mark.parametrize("slab", [1, 2, 4])
 @pytest.mark.parametrize("budget", [0, 24])
