@@ -289,8 +289,11 @@ WgRowsFn wg_rows_pick(int vpl, int k) {
   switch (vpl) {
     case 2: return wg_rows_pick_k<2>(k);
     case 4: return wg_rows_pick_k<4>(k);
+    case 6: return wg_rows_pick_k<6>(k);
     case 7: return wg_rows_pick_k<7>(k);
     case 8: return wg_rows_pick_k<8>(k);
+    case 10: return wg_rows_pick_k<10>(k);
+    case 12: return wg_rows_pick_k<12>(k);
     case 14: return wg_rows_pick_k<14>(k);
     case 16: return wg_rows_pick_k<16>(k);
     default: return nullptr;
@@ -771,20 +774,36 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 //   64 CUs: vgpr_wg 122.5 / 122.1 and 366.1 / 365.5; pc 149.7 / 94.9 and
 //     537.6 / 270.0.
 // Callers whose x is cache-resident can ask for "lds1" or "pc".
-Variant dispatch_auto(const Budget& b, int64_t T, int* persistent_cus) {
+//
+// Smaller batches on every CU, from 2 tokens per CU (4 for rows of at most
+// 4 KiB) up: the register double buffer (vgpr2) on the ordinary grid, which
+// also streams x.  lds1 there goes persistent on dispatch_write_cus(k) CUs
+// once it has that many units, and cold those CUs' reads are the bound.
+// Cold, us, H = 7168, k = 8: T = 512 15.9 against 16.6 for lds1, T = 1024
+// 28.0 against 44.1, T = 1536 41.0 against 66.1; k = 6, T = 1536 32.3
+// against 59.6; H = 4096, k = 2, T = 1024 9.1 against 10.1.  Below that,
+// lds1 on the ordinary grid: H = 7168, k = 8, T = 256 10.6 against 13.6;
+// H = 2048, k = 8, T = 512 7.7 against 9.6, T = 1024 10.9 against 11.2.
+// On a CU budget or mask small batches keep lds1 (not measured this way).
+Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-  if (!dispatch_auto_large(b, T)) return Variant::Lds1;
-  *persistent_cus = cus;
-  return Variant::VgprWg;
+  if (dispatch_auto_large(b, T)) {
+    *persistent_cus = cus;
+    return Variant::VgprWg;
+  }
+  const int64_t per_cu = row_vec <= 4 * kWave ? 4 : 2;
+  if (cus >= b.all_cus && T >= per_cu * cus) return Variant::Vgpr2;
+  return Variant::Lds1;
 }
 
 hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int H, const int32_t* dest_row, int k,
                            void* recv, int64_t recv_rows, hipStream_t stream) {
+  const int row_vec = H / 8;
   int auto_cus = 0;  // the persistent grid the default chose (0: none)
-  if (v == Variant::Auto) v = dispatch_auto(b, T, &auto_cus);
+  const bool chosen = v == Variant::Auto;
+  if (chosen) v = dispatch_auto(b, T, row_vec, &auto_cus);
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if ((v == Variant::Lds2 || v == Variant::Lds3 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
-  const int row_vec = H / 8;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
   const bool even = row_vec % kWave == 0;
   // Slabs: the register double buffer, the workgroup-phased register kernel
@@ -803,9 +822,10 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;
-  // the workgroup-phased kernel's common case: whole rows of exactly vpl KiB
-  const WgRowsFn rows_fn =
-      (v == Variant::VgprWg && nslab == 1 && row_vec == vpl * kWave) ? wg_rows_pick(vpl, k) : nullptr;
+  // the workgroup-phased kernel's common case: one slab per row, the row a
+  // whole number of KiB (rows_vpl vectors per lane)
+  const int rows_vpl = (v == Variant::VgprWg && nslab == 1 && row_vec % kWave == 0) ? row_vec / kWave : 0;
+  const WgRowsFn rows_fn = rows_vpl > 0 ? wg_rows_pick(rows_vpl, k) : nullptr;
   DispatchFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
   if (!fn) return hipErrorInvalidValue;
 
@@ -819,11 +839,12 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // write throughput was measured highest with about a quarter of the CUs
   // issuing them (more add contention, not bandwidth); smaller k carry more
   // reads and take more CUs.  Small batches keep the ordinary grid, whose
-  // start-up is cheaper.
+  // start-up is cheaper, and so does the default's choice of vgpr2 for
+  // smaller batches (measured on the ordinary grid).
   int budget = b.num_cus;
   const int write_cus = dispatch_write_cus(k);
   if (auto_cus > 0) budget = auto_cus;
-  else if (budget == 0 && units >= write_cus * 16 * 2) budget = write_cus;
+  else if (budget == 0 && !(chosen && v == Variant::Vgpr2) && units >= write_cus * 16 * 2) budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W
     // slabs each; always a persistent grid (one workgroup per CU)
@@ -859,7 +880,7 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
       hipError_t e = allow_dynamic_lds((const void*)rows_fn, lds_bytes);
       if (e != hipSuccess) return e;
     }
-    const int64_t per_trip = (int64_t)grid * wpg * wg_units_of(vpl);
+    const int64_t per_trip = (int64_t)grid * wpg * wg_units_of(rows_vpl);
     // On at least half the device, where HBM is the bound, one launch per
     // trip: the kernel boundary starts every CU's read burst together, which
     // the per-workgroup barrier alone does not (T = 16384, k = 6 on 256 CUs,

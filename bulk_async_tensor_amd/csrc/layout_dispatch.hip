@@ -493,8 +493,9 @@ hipError_t launch_layout_dispatch(Variant v, const Budget& b, const int32_t* idx
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   // The wide kernel copies as the lds1 dispatch does: taken for "lds1", and
-  // for "auto" below the batch size from which the default dispatch streams
-  // x (its cacheable loads of x are fast only while x is cached).  It is
+  // for "auto" below the batch size from which the default dispatch runs
+  // the workgroup-phased kernel (its cacheable loads of x are fast only
+  // while x is cached).  It is
   // also the faster one for decode batches where it applies (T = 128,
   // E = 256, k = 8: 8.1 against 8.7 us for the small kernel; T = 64: 6.5
   // against 7.6 us), so the small kernel serves the rest: few experts,

@@ -71,15 +71,15 @@ enum {
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
  * launch.  n == 0: no budget; the library picks the launch per kernel --
  * an ordinary grid over the whole device, except that a dispatch of at
- * least 8 tokens per CU (variant "auto", unmasked stream) runs the register
- * double buffer ("vgpr2") with whole-row slabs as a persistent grid on
- * every CU: its streaming loads of x take the same time whether or not x is
- * still in the Infinity Cache.  With another variant, a dispatch of at
- * least 32 work units per CU of its default budget runs persistent on that
- * budget: 64 CUs for k >= 5 (at k = 8 its traffic is 8/9 writes, and HBM
- * write throughput peaks with about a quarter of the CUs issuing them), 96
- * for k = 2..4 and 128 for k = 1, whose larger read share needs more CUs in
- * flight.  The initial value comes from the environment variable
+ * least 8 tokens per CU (variant "auto") runs the workgroup-phased register
+ * kernel ("vgpr_wg") with whole-row slabs as a persistent grid on every CU
+ * it may use: its streaming loads of x take the same time whether or not x
+ * is still in the Infinity Cache.  With another variant (or "auto" taking
+ * "lds1"), a dispatch of at least 32 work units per CU of its default
+ * budget runs persistent on that budget: 64 CUs for k >= 5 (at k = 8 its
+ * traffic is 8/9 writes, and HBM write throughput peaks with about a
+ * quarter of the CUs issuing them), 96 for k = 2..4 and 128 for k = 1,
+ * whose larger read share needs more CUs in flight.  The initial value comes from the environment variable
  * EP_NUM_CUS (default 0).
  * On a CU-masked stream (ep_stream_create_cu_masked, or any stream whose
  * mask hipExtStreamGetCUMask reports) every launch counts only the CUs of
@@ -103,7 +103,10 @@ int ep_get_num_cus(void);
  *           while x is in the Infinity Cache (about 258 us on 64 CUs, 645 us
  *           on 24), much slower once it is not (about 650 and 975 us), so a
  *           caller that has just written x may prefer them.  Smaller
- *           batches take "lds1";
+ *           batches on every CU take "vgpr2" on an ordinary grid from 2
+ *           tokens per CU (4 for rows of at most 4 KiB), which also streams
+ *           x; the smallest batches, and small ones on a CU budget or mask,
+ *           take "lds1";
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
  *           or k loads feeding one store (combine);
  *   "vgpr2" the same with the next work unit's loads issued before the
@@ -121,8 +124,9 @@ int ep_get_num_cus(void);
  *           4, 6 or 8, else combine runs the any-k register kernel and
  *           dispatch lds1.  "auto" picks it for combine on at least half
  *           the device when each launch fills two thirds of a full grid
- *           (at k = 2 and 4 reading runs of 2 vectors per source row, where
- *           the row allows them);
+ *           (with every CU and units of at most 16 KiB per wave: 9/20 at
+ *           k >= 4, 3/5 at k = 2), at k = 2 and 4 reading runs of 2
+ *           vectors per source row where the row allows them;
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
  *           the next two units' direct-to-LDS loads are in flight while the
  *           current one is stored (fewer waves fit a CU);

@@ -230,6 +230,44 @@ def test_dispatch_vgpr_wg_launch_per_trip(T, k, budget):
     np.testing.assert_array_equal(got, want)
 
 
+# Whole-row instances of the workgroup-phased dispatch for rows of 2 .. 16
+# KiB other than 7 and 14 (H = 1024 .. 8192): the kernel's vectors per lane
+# are the row's own, not the slab size the other kernels take.
+@pytest.mark.parametrize("H", [1024, 2048, 3072, 4096, 5120, 6144, 8192])
+@pytest.mark.parametrize("T,budget", [(300, 0), (300, 24), (2600, 256)])
+def test_dispatch_vgpr_wg_row_sizes(H, T, budget):
+    ep.ep_set_variant("vgpr_wg")
+    ep.ep_set_num_cus(budget)
+    k = 6 if H % 3072 == 0 else 8
+    wl = make_workload("prefill", seed=T + H, T=T, H=H, E=32, k=k)
+    lay = oracle.layout(wl.topk_idx, 32)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1
+    dest[T - 1, 0] = 1 << 30
+    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
+    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
+# The default dispatch on every CU around its batch-size thresholds: lds1
+# below 2 tokens per CU (4 for rows of at most 4 KiB), vgpr2 on the ordinary
+# grid up to 8 tokens per CU, the workgroup-phased kernel from there (the
+# thresholds scale with the device's CU count; these sizes bracket them on
+# a 256-CU device).
+@pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
+                                   (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536)])
+def test_dispatch_default_batch_sizes(H, k, T):
+    ep.ep_set_variant("auto")
+    ep.ep_set_num_cus(0)
+    wl = make_workload("prefill", seed=T + H + k, T=T, H=H, E=64, k=k)
+    lay = oracle.layout(wl.topk_idx, 64)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1
+    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
+    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.parametrize("name", DISPATCH_CONFIGS)
 @pytest.mark.parametrize("variant,budget", [("auto", 0), ("vgpr_cached", 0), ("auto", 24), ("auto", 64)])
 def test_dispatch_rows_matches(name, variant, budget):
