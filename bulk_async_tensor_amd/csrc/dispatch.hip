@@ -784,15 +784,20 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 // against 59.6; H = 4096, k = 2, T = 1024 9.1 against 10.1.  Below that,
 // lds1 on the ordinary grid: H = 7168, k = 8, T = 256 10.6 against 13.6;
 // H = 2048, k = 8, T = 512 7.7 against 9.6, T = 1024 10.9 against 11.2.
-// On a CU budget or mask small batches keep lds1 (not measured this way).
+// On part of the device (a CU budget or mask) every batch size takes
+// vgpr_wg on the budget's CUs, whose reads are the bound there: cold, 1 to 6
+// tokens per CU on 24, 64 and 128 CUs, 7-59% faster than lds1 on the same
+// CUs (H = 7168, k = 8, 128 CUs, T = 256: 12.4 against 18.8 us; 24 CUs,
+// T = 96: 11.4 against 15.4, T = 144: 15.4 against 16.6; H = 4096, k = 2,
+// 64 CUs, T = 256: 7.5 against 10.9) and 15-49% faster than vgpr2 there.
 Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-  if (dispatch_auto_large(b, T)) {
+  if (dispatch_auto_large(b, T) || cus < b.all_cus) {
     *persistent_cus = cus;
     return Variant::VgprWg;
   }
   const int64_t per_cu = row_vec <= 4 * kWave ? 4 : 2;
-  if (cus >= b.all_cus && T >= per_cu * cus) return Variant::Vgpr2;
+  if (T >= per_cu * cus) return Variant::Vgpr2;
   return Variant::Lds1;
 }
 

@@ -71,10 +71,10 @@ enum {
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
  * launch.  n == 0: no budget; the library picks the launch per kernel --
  * an ordinary grid over the whole device, except that a dispatch of at
- * least 8 tokens per CU (variant "auto") runs the workgroup-phased register
- * kernel ("vgpr_wg") with whole-row slabs as a persistent grid on every CU
- * it may use: its streaming loads of x take the same time whether or not x
- * is still in the Infinity Cache.  With another variant (or "auto" taking
+ * least 8 tokens per CU (variant "auto"; any size on a budget or mask)
+ * runs the workgroup-phased register kernel ("vgpr_wg") with whole-row
+ * slabs as a persistent grid on every CU it may use: its streaming loads of
+ * x take the same time whether or not x is still in the Infinity Cache.  With another variant (or "auto" taking
  * "lds1"), a dispatch of at least 32 work units per CU of its default
  * budget runs persistent on that budget: 64 CUs for k >= 5 (at k = 8 its
  * traffic is 8/9 writes, and HBM write throughput peaks with about a
@@ -105,8 +105,8 @@ int ep_get_num_cus(void);
  *           caller that has just written x may prefer them.  Smaller
  *           batches on every CU take "vgpr2" on an ordinary grid from 2
  *           tokens per CU (4 for rows of at most 4 KiB), which also streams
- *           x; the smallest batches, and small ones on a CU budget or mask,
- *           take "lds1";
+ *           x, and the smallest ones "lds1".  On a CU budget or mask every
+ *           batch size takes "vgpr_wg" on the budget's CUs;
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
  *           or k loads feeding one store (combine);
  *   "vgpr2" the same with the next work unit's loads issued before the
