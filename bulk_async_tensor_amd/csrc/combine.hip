@@ -710,6 +710,16 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   // 1.17 TB/s, k = 4 on 64 CUs 3.15 against 3.00; k = 1 and 8 keep 2
   // (4-vector slabs cost them 3-10%).
   if (single && b.slab_vpl == 0 && b.num_cus > 0 && k >= 2 && k <= 7) vpl = 4;
+  // On a budget, batches of up to 32 tokens per CU take 1-vector slabs: more
+  // units for the budget's 16 waves per CU.  Cold, us, against the slabs
+  // above, 24 and 64 CUs, 0.5 to 64 tokens per CU: H = 7168, k = 8 7.8
+  // against 11.0 (24 CUs, T = 24), 24.4 against 28.1 (T = 192), equal from
+  // 32 per CU; k = 4 6.6 against 8.2 (T = 24), 1-6% faster up to 64 per CU;
+  // H = 4096, k = 6 9.5 against 10.6 (T = 96), 38.7 against 40.5 (T = 768),
+  // 1.5% slower at 64 per CU (64 CUs, T = 4096).
+  if (single && b.slab_vpl == 0 && b.num_cus > 0 &&
+      (int64_t)T <= 32LL * (b.num_cus < b.device_cus ? b.num_cus : b.device_cus))
+    vpl = 1;
   if (row_vec <= kWave) vpl = 1;
   const int max_wpg = (single && vpl >= 4) ? 8 : 16;
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);

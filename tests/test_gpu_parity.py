@@ -466,6 +466,22 @@ def test_combine_default_partial_fill(H, k, T):
     assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
 
 
+# The default combine on a CU budget around its slab threshold: 1-vector
+# slabs up to 32 tokens per CU of the budget, the 2- or 4-vector slabs above
+# (k = 2..7 take 4), with whole and ragged rows.
+@pytest.mark.parametrize("T", [24, 768, 769])
+@pytest.mark.parametrize("H,k", [(7168, 8), (7168, 4), (520, 6)])
+def test_combine_default_budget_slabs(T, H, k):
+    ep.ep_set_variant("auto")
+    ep.ep_set_num_cus(24)
+    wl = make_workload("combine_stress", seed=T + H + k, T=T, H=H, E=64, k=k)
+    lay = oracle.layout(wl.topk_idx, 64)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1  # a slot that contributes nothing
+    got = run_combine(wl, wl.y, dest)
+    assert_combine_close(got, oracle.combine(wl.y, dest, wl.topk_w))
+
+
 @pytest.mark.parametrize("variant", ["vgpr", "vgpr_cached", "lds2", "phase"])
 @pytest.mark.parametrize("slab", [1, 2, 4])
 @pytest.mark.parametrize("budget", [0, 24])
