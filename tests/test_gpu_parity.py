@@ -1158,8 +1158,8 @@ def _random_cases(n, seed=2026):
         if T * k * H * 2 > 96 << 20:  # keep the oracle to a few seconds
             continue
         cases.append(dict(name=str(rng.choice(["train", "prefill"])), T=T, H=H, E=E, k=k,
-                          budget=int(rng.choice([0, 0, 24, 64, 200])),
-                          variant=str(rng.choice(["auto", "auto", "lds1", "vgpr", "phase"])),
+                          budget=int(rng.choice([0, 0, 24, 64, 200, 256])),
+                          variant=str(rng.choice(["auto", "auto", "lds1", "vgpr", "phase", "vgpr_wg", "vgpr2"])),
                           one_launch=bool(rng.integers(0, 2))))
     return cases
 
@@ -1167,7 +1167,7 @@ def _random_cases(n, seed=2026):
 # Seeded random shapes through the default and forced launches: layout and
 # dispatch bit-exact, combine against the oracle, with and without the
 # one-launch layout + dispatch.
-@pytest.mark.parametrize("case", _random_cases(100), ids=lambda c: "{name}-T{T}-H{H}-E{E}-k{k}-b{budget}-{variant}"
+@pytest.mark.parametrize("case", _random_cases(150), ids=lambda c: "{name}-T{T}-H{H}-E{E}-k{k}-b{budget}-{variant}"
                          .format(**c) + ("-one" if c["one_launch"] else ""))
 def test_random_shapes(case):
     ep.ep_set_num_cus(case["budget"])
