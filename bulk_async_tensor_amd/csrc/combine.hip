@@ -585,11 +585,11 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
 // gains nothing (decode batches stay on the register kernel), and on fewer
 // CUs the per-CU read rate, not the read/write turnaround, is the bound.
 // Cold single calls against the register kernel, every CU, two runs each:
-//  - two rows per wave in 8-wave workgroups (k >= 6 at H = 4104..7168):
-//    two thirds.  H = 5120 at 45-60% of the grid 5-37% slower (k = 6 and
-//    8), at 65% 2% faster (k = 6) and 10% slower (k = 8); H = 7168, k = 8
-//    at 62.5% 7% slower and at 75% 4% faster; earlier at H = 7168, k = 6
-//    67% 4% faster, 55% 7% slower;
+//  - two or three rows per wave in 8-wave workgroups (k >= 6 at H = 4104
+//    .. 7168): two thirds at k = 6, seven tenths at k = 8.  H = 4608,
+//    5120, 6144, 7168: k = 6 at 67% 5-9% faster, at 60% 1-5% slower; k = 8
+//    at 67% 2-6% slower, at 70-73% between 3% faster and 3% slower (slower
+//    only at H = 5120), from 80% 4-12% faster;
 //  - the 16-wave shape at k >= 4: nine twentieths.  H = 2048, 3072, 4096
 //    and k = 4, 6, 8 at 45-65%: 3-11% faster in every case; at 37.5%, k = 4
 //    3-6% slower (H = 1024, 2048, 7168);
@@ -610,6 +610,7 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
   const int64_t slots = (int64_t)cus * ps.wpg;
   if (cus >= b.all_cus && ps.held != kPhaseWideHeld) return k == 2 ? units * 5 >= slots * 3 : units * 20 >= slots * 9;
+  if (ps.held == kPhaseWideHeld && k == 8) return units * 10 >= slots * 7;
   return units * 3 >= slots * 2;
 }
 

@@ -125,8 +125,9 @@ int ep_get_num_cus(void);
  *           dispatch lds1.  "auto" picks it for combine on at least half
  *           the device when each launch fills two thirds of a full grid
  *           (with every CU and units of at most 16 KiB per wave: 9/20 at
- *           k >= 4, 3/5 at k = 2), at k = 2 and 4 reading runs of 2
- *           vectors per source row where the row allows them;
+ *           k >= 4, 3/5 at k = 2; with two rows per wave at k = 8: seven
+ *           tenths), at k = 2 and 4 reading runs of 2 vectors per source
+ *           row where the row allows them;
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
  *           the next two units' direct-to-LDS loads are in flight while the
  *           current one is stored (fewer waves fit a CU);
