@@ -277,9 +277,13 @@ using WgRowsFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, in
 template <int VPL>
 WgRowsFn wg_rows_pick_k(int k) {
   switch (k) {
+    case 1: return dispatch_wg_rows_kernel<VPL, 1, true>;
     case 2: return dispatch_wg_rows_kernel<VPL, 2, true>;
+    case 3: return dispatch_wg_rows_kernel<VPL, 3, true>;
     case 4: return dispatch_wg_rows_kernel<VPL, 4, true>;
+    case 5: return dispatch_wg_rows_kernel<VPL, 5, true>;
     case 6: return dispatch_wg_rows_kernel<VPL, 6, true>;
+    case 7: return dispatch_wg_rows_kernel<VPL, 7, true>;
     case 8: return dispatch_wg_rows_kernel<VPL, 8, true>;
     default: return nullptr;
   }

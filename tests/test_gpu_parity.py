@@ -232,13 +232,14 @@ def test_dispatch_vgpr_wg_launch_per_trip(T, k, budget):
 
 # Whole-row instances of the workgroup-phased dispatch for rows of 2 .. 16
 # KiB other than 7 and 14 (H = 1024 .. 8192): the kernel's vectors per lane
-# are the row's own, not the slab size the other kernels take.
+# are the row's own, not the slab size the other kernels take.  k runs
+# through 1 .. 8 with the row size (every k has its own instance).
 @pytest.mark.parametrize("H", [1024, 2048, 3072, 4096, 5120, 6144, 8192])
 @pytest.mark.parametrize("T,budget", [(300, 0), (300, 24), (2600, 256)])
 def test_dispatch_vgpr_wg_row_sizes(H, T, budget):
     ep.ep_set_variant("vgpr_wg")
     ep.ep_set_num_cus(budget)
-    k = 6 if H % 3072 == 0 else 8
+    k = (H // 1024) % 8 + 1
     wl = make_workload("prefill", seed=T + H, T=T, H=H, E=32, k=k)
     lay = oracle.layout(wl.topk_idx, 32)
     dest = lay["dest_row"].copy()
