@@ -482,19 +482,24 @@ __global__ __launch_bounds__(MAXT) void combine_phase_kernel(const u32x4* __rest
 using PhaseFn = void (*)(const u32x4*, u32x4*, const int32_t*, const float*, int64_t, int, int, int, int, int, int,
                          int);
 
-// Slots per register set: with single-vector runs, two equal sets of k/2
+// Slots per register set: with single-vector runs, two sets of (k + 1) / 2
+// (at odd k the second one is a slot short)
 // (k = 6 in sets of 4 and 2 ran 3-10% slower than in two sets of 3 at
 // H = 7168, T = 8192: 139.5 against 135.0 us and 139.9 against 129.3 us in
 // two runs); with 2-vector runs, sets of 2 slots (4 KiB per wave).  (Runs of 4 vectors do not fit: two sets plus 32
 // accumulators and the held output spill at k >= 6.)
-constexpr int phase_set_slots(int k, int seg) { return seg == 1 ? k / 2 : 2; }
+constexpr int phase_set_slots(int k, int seg) { return seg == 1 ? (k + 1) / 2 : 2; }
 
 template <int SEG, int HELD, bool EVEN, int MAXT = kPhaseWpg * kWave>
 PhaseFn pick_phase_k(int k) {
   switch (k) {
+    case 1: return combine_phase_kernel<1, SEG, phase_set_slots(1, SEG), HELD, EVEN, MAXT>;
     case 2: return combine_phase_kernel<2, SEG, phase_set_slots(2, SEG), HELD, EVEN, MAXT>;
+    case 3: return combine_phase_kernel<3, SEG, phase_set_slots(3, SEG), HELD, EVEN, MAXT>;
     case 4: return combine_phase_kernel<4, SEG, phase_set_slots(4, SEG), HELD, EVEN, MAXT>;
+    case 5: return combine_phase_kernel<5, SEG, phase_set_slots(5, SEG), HELD, EVEN, MAXT>;
     case 6: return combine_phase_kernel<6, SEG, phase_set_slots(6, SEG), HELD, EVEN, MAXT>;
+    case 7: return combine_phase_kernel<7, SEG, phase_set_slots(7, SEG), HELD, EVEN, MAXT>;
     case 8: return combine_phase_kernel<8, SEG, phase_set_slots(8, SEG), HELD, EVEN, MAXT>;
     default: return nullptr;
   }
@@ -596,12 +601,19 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
 //  - the 16-wave shape at k = 2: three fifths.  At 55% 0.4% faster to 3.5%
 //    slower, at 60% 1% slower (H = 3072) to 4% faster, from 62.5% 2-5%
 //    faster (H = 1024 .. 7168).
-// On part of the device (128-192 CUs, not measured this way) the rule stays
-// at two thirds.  At k = 2 and 4 the kernel needs runs of 2 vectors per read
-// (see combine_phase_seg): with single vectors the register kernel was
-// 11-20% faster there.
+// Odd k: at a full launch the phased kernel is 3-16% faster than the any-k
+// register kernel at k = 1, 3, 5, 7 (H = 4096 and 7168; k = 7, H = 7168,
+// T = 16384: 293.0 against 347.1 us).  In the 16-wave shape odd k takes the
+// rule of the even k above it (k = 1 that of k = 2; k = 1 wins from 50%,
+// k = 3 from 47%, k = 5 and 7 from 40-47%).  In the two-row shape, whose
+// register sets split unevenly at odd k: k = 5 from 23/25 (H = 5120 and
+// 7168: 0-1.5% slower at 90%, 4% faster at 95%, 10-16% slower at 67-75%),
+// k = 7 from three quarters (4-8% slower at 67-72%, 3% faster at 80%).  On part of the device (128-192 CUs) the rule
+// stays at two thirds.  At k <= 4 the kernel needs runs of 2 vectors per
+// read (see combine_phase_seg): with single vectors the register kernel was
+// 11-20% faster at k = 2 and 4.
 bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
-  if (!(k == 2 || k == 4 || k == 6 || k == 8)) return false;
+  if (k < 1 || k > 8) return false;
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (2 * cus < b.all_cus) return false;
   const int seg_vec = combine_phase_seg(b, row_vec, k);
@@ -609,8 +621,12 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
   const int64_t slots = (int64_t)cus * ps.wpg;
-  if (cus >= b.all_cus && ps.held != kPhaseWideHeld) return k == 2 ? units * 5 >= slots * 3 : units * 20 >= slots * 9;
-  if (ps.held == kPhaseWideHeld && k == 8) return units * 10 >= slots * 7;
+  if (cus >= b.all_cus && ps.held != kPhaseWideHeld) return k <= 2 ? units * 5 >= slots * 3 : units * 20 >= slots * 9;
+  if (ps.held == kPhaseWideHeld) {
+    if (k == 5) return units * 25 >= slots * 23;
+    if (k == 7) return units * 4 >= slots * 3;
+    if (k == 8) return units * 10 >= slots * 7;
+  }
   return units * 3 >= slots * 2;
 }
 
@@ -690,9 +706,10 @@ hipError_t launch_combine(Variant v, const Budget& b, const void* y, int64_t rec
   if (recv_rows == 0) return launch_combine_zero(b, out, (int64_t)T * row_vec, stream);
   if (v == Variant::Lds3 || v == Variant::Pc || v == Variant::VgprWg) v = Variant::Auto;  // dispatch-only variants
   if (v == Variant::Auto) v = phase_preferred(b, row_vec, T, k) ? Variant::Phase : Variant::Vgpr;
+  if (v == Variant::Phase && k >= 1 && k <= 8)
+    return launch_phase(b, y, recv_rows, row_vec, dest_row, w, T, k, out, stream);
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if (!known_k) v = Variant::Vgpr;  // the any-k kernel
-  if (v == Variant::Phase) return launch_phase(b, y, recv_rows, row_vec, dest_row, w, T, k, out, stream);
   const bool even = row_vec % kWave == 0;
   // in-flight registers grow as k x VPL: two vectors per lane per slot for
   // the single-set kernel, one for the double-buffered and LDS ones

@@ -120,14 +120,15 @@ int ep_get_num_cus(void);
  *           registers and stores them only after all their source rows are
  *           read; for dispatch each wave loads up to 16 KiB of x rows into
  *           registers, then writes their k copies.  With one such unit per
- *           wave the whole grid reads first and writes last.  k must be 2,
- *           4, 6 or 8, else combine runs the any-k register kernel and
- *           dispatch lds1.  "auto" picks it for combine on at least half
- *           the device when each launch fills two thirds of a full grid
- *           (with every CU and units of at most 16 KiB per wave: 9/20 at
- *           k >= 4, 3/5 at k = 2; with two rows per wave at k = 8: seven
- *           tenths), at k = 2 and 4 reading runs of 2 vectors per source
- *           row where the row allows them;
+ *           wave the whole grid reads first and writes last.  k must be
+ *           at most 8 for combine (else the any-k register kernel runs) and
+ *           2, 4, 6 or 8 for dispatch (else lds1).  "auto" picks it for
+ *           combine on at least half the device when each launch fills two
+ *           thirds of a full grid (with every CU and units of at most
+ *           16 KiB per wave: 9/20 at k >= 3, 3/5 at k <= 2; with two rows
+ *           per wave: 23/25 at k = 5, 3/4 at k = 7, 7/10 at k = 8), at
+ *           k <= 4 reading runs of 2 vectors per source row where the row
+ *           allows them;
  *   "lds3"  (dispatch; combine takes its default) three stages per wave:
  *           the next two units' direct-to-LDS loads are in flight while the
  *           current one is stored (fewer waves fit a CU);

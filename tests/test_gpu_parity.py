@@ -448,14 +448,18 @@ def test_combine_phase_batches(T, budget, k):
 # The default combine with every CU on both sides of its fill thresholds for
 # the phased kernel (the fraction of the grid's waves one launch gives a
 # unit): 16-wave shapes take it from 9/20 at k >= 4 and 3/5 at k = 2, the
-# two-row 8-wave shape from 2/3 at k = 6 and 7/10 at k = 8.  (H, k, T):
+# two-row 8-wave shape from 23/25 at k = 5, 2/3 at k = 6, 3/4 at k = 7 and
+# 7/10 at k = 8; in the 16-wave shape odd k takes the rule of the even k
+# above it.  (H, k, T):
 # H = 2048 holds four tokens per unit (16384 per full launch), H = 3072 and
 # 4096 two (8192), H = 5120 and 7168 at k >= 6 two rows per wave in 8-wave
 # workgroups (4096).
 @pytest.mark.parametrize(
     "H,k,T",
     [(2048, 4, 7000), (2048, 4, 8192), (4096, 8, 3686), (4096, 6, 4505), (3072, 2, 4600), (3072, 2, 4915),
-     (2048, 2, 9830), (5120, 8, 2457), (5120, 8, 2800), (5120, 8, 2900), (7168, 8, 2860), (7168, 6, 2800)],
+     (2048, 2, 9830), (5120, 8, 2457), (5120, 8, 2800), (5120, 8, 2900), (7168, 8, 2860), (7168, 6, 2800),
+     (4096, 3, 3500), (4096, 3, 3700), (2048, 1, 9600), (2048, 1, 9900), (7168, 5, 3760), (7168, 5, 3780),
+     (7168, 7, 3068), (7168, 7, 3076)],
 )
 def test_combine_default_partial_fill(H, k, T):
     ep.ep_set_variant("auto")
