@@ -780,14 +780,16 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 // Callers whose x is cache-resident can ask for "lds1" or "pc".
 //
 // Smaller batches on every CU, from 2 tokens per CU (4 for rows of at most
-// 4 KiB) up: the register double buffer (vgpr2) on the ordinary grid, which
+// 8 KiB) up: the register double buffer (vgpr2) on the ordinary grid, which
 // also streams x.  lds1 there goes persistent on dispatch_write_cus(k) CUs
 // once it has that many units, and cold those CUs' reads are the bound.
 // Cold, us, H = 7168, k = 8: T = 512 15.9 against 16.6 for lds1, T = 1024
 // 28.0 against 44.1, T = 1536 41.0 against 66.1; k = 6, T = 1536 32.3
 // against 59.6; H = 4096, k = 2, T = 1024 9.1 against 10.1.  Below that,
 // lds1 on the ordinary grid: H = 7168, k = 8, T = 256 10.6 against 13.6;
-// H = 2048, k = 8, T = 512 7.7 against 9.6, T = 1024 10.9 against 11.2.
+// H = 2048, k = 8, T = 512 7.7 against 9.6, T = 1024 10.9 against 11.2;
+// H = 4096, T = 512 (2 per CU), k = 3, 4, 5: 8.2 / 8.8 / 10.0 against
+// 9.1 / 10.4 / 11.4, and from T = 1024 vgpr2 is as fast or faster.
 // On part of the device (a CU budget or mask) every batch size takes
 // vgpr_wg on the budget's CUs, whose reads are the bound there: cold, 1 to 6
 // tokens per CU on 24, 64 and 128 CUs, 7-59% faster than lds1 on the same
@@ -800,7 +802,7 @@ Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int* persistent_c
     *persistent_cus = cus;
     return Variant::VgprWg;
   }
-  const int64_t per_cu = row_vec <= 4 * kWave ? 4 : 2;
+  const int64_t per_cu = row_vec <= 8 * kWave ? 4 : 2;
   if (T >= per_cu * cus) return Variant::Vgpr2;
   return Variant::Lds1;
 }

@@ -104,7 +104,7 @@ int ep_get_num_cus(void);
  *           on 24), much slower once it is not (about 650 and 975 us), so a
  *           caller that has just written x may prefer them.  Smaller
  *           batches on every CU take "vgpr2" on an ordinary grid from 2
- *           tokens per CU (4 for rows of at most 4 KiB), which also streams
+ *           tokens per CU (4 for rows of at most 8 KiB), which also streams
  *           x, and the smallest ones "lds1".  On a CU budget or mask every
  *           batch size takes "vgpr_wg" on the budget's CUs;
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)

@@ -251,12 +251,13 @@ def test_dispatch_vgpr_wg_row_sizes(H, T, budget):
 
 
 # The default dispatch on every CU around its batch-size thresholds: lds1
-# below 2 tokens per CU (4 for rows of at most 4 KiB), vgpr2 on the ordinary
+# below 2 tokens per CU (4 for rows of at most 8 KiB), vgpr2 on the ordinary
 # grid up to 8 tokens per CU, the workgroup-phased kernel from there (the
 # thresholds scale with the device's CU count; these sizes bracket them on
 # a 256-CU device).
 @pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
-                                   (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536)])
+                                   (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536),
+                                   (4096, 3, 1023), (4096, 3, 1024)])
 def test_dispatch_default_batch_sizes(H, k, T):
     ep.ep_set_variant("auto")
     ep.ep_set_num_cus(0)
