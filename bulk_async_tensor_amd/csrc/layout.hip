@@ -449,17 +449,23 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(const int32
 
 using FusedFn = void (*)(const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*);
 
-// The one-launch kernel exists for these k only: with k known at run time a
-// token's ids could not stay in registers, and the kernel measured 30-40 us
-// at 32 Ki entries (k = 3, 7, 16, 32) against 8.5 us for k = 8.  Other k take
-// the count kernel, whose chunk of ids sits in LDS.
-bool fused_k(int k) { return k == 1 || k == 2 || k == 4 || k == 6 || k == 8; }
+// The one-launch kernel keeps a token's ids in registers, so k must be
+// known at compile time: instances for k = 1 .. 8.  With k known only at run
+// time it measured 30-40 us at 32 Ki entries (k = 3, 7, 16, 32) against
+// 8.5 us for k = 8, so larger k take the count kernel, whose chunk of ids
+// sits in LDS.  The odd-k instances against the two launches they replace,
+// cold: E = 256, T = 128 .. 4096, 7.0-11.6 against 12.0-15.2 us; E = 64,
+// T = 128 and 512, 6.8-7.7 against 11.7-13.8 us; bit-identical.
+bool fused_k(int k) { return k >= 1 && k <= 8; }
 
 FusedFn fused_for(int k) {
   switch (k) {
     case 1: return layout_fused_kernel<1>;
     case 2: return layout_fused_kernel<2>;
+    case 3: return layout_fused_kernel<3>;
     case 4: return layout_fused_kernel<4>;
+    case 5: return layout_fused_kernel<5>;
+    case 7: return layout_fused_kernel<7>;
     case 6: return layout_fused_kernel<6>;
     case 8: return layout_fused_kernel<8>;
     default: return nullptr;

@@ -108,6 +108,24 @@ def test_layout_flags_bad_ids():
         check_layout(got, ref, T, 4)
 
 
+# Odd k through the one-launch layout (a few chunks at any E, up to 64 with
+# E > 64) and past it into the two launches, with a repeated expert, an id
+# out of range and a negative id.
+@pytest.mark.parametrize("k", [3, 5, 7])
+@pytest.mark.parametrize("T,E", [(128, 64), (700, 64), (2048, 256), (9400, 256), (5000, 32)])
+def test_layout_odd_k(k, T, E):
+    wl = make_workload("train", seed=T + E + k, T=T, E=E, k=k, H=8)
+    idx = wl.topk_idx.copy()
+    idx[1, 1] = idx[1, 0]
+    idx[T // 2, 0] = E
+    idx[T - 1, k - 1] = -1
+    ref = oracle.layout(idx, E)
+    assert ref["status"] == 3
+    lay = ep.ep_layout(to_dev(idx), E)
+    torch.cuda.synchronize()
+    check_layout({key: v.cpu().numpy() for key, v in lay.items()}, ref, T, k)
+
+
 def test_layout_is_deterministic():
     wl = workload("train")
     a = gpu_layout(wl)
