@@ -790,20 +790,24 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 // H = 2048, k = 8, T = 512 7.7 against 9.6, T = 1024 10.9 against 11.2;
 // H = 4096, T = 512 (2 per CU), k = 3, 4, 5: 8.2 / 8.8 / 10.0 against
 // 9.1 / 10.4 / 11.4, and from T = 1024 vgpr2 is as fast or faster.
-// On part of the device (a CU budget or mask) every batch size takes
-// vgpr_wg on the budget's CUs, whose reads are the bound there: cold, 1 to 6
-// tokens per CU on 24, 64 and 128 CUs, 7-59% faster than lds1 on the same
-// CUs (H = 7168, k = 8, 128 CUs, T = 256: 12.4 against 18.8 us; 24 CUs,
+// On a CU budget below the device every batch size takes vgpr_wg on the
+// budget's CUs, whose reads are the bound there: cold, 1 to 6 tokens per CU
+// on 24, 64 and 128 CUs, 7-59% faster than lds1 persistent on the same CUs
+// (H = 7168, k = 8, 128 CUs, T = 256: 12.4 against 18.8 us; 24 CUs,
 // T = 96: 11.4 against 15.4, T = 144: 15.4 against 16.6; H = 4096, k = 2,
 // 64 CUs, T = 256: 7.5 against 10.9) and 15-49% faster than vgpr2 there.
+// A CU-masked stream without a budget keeps lds1 on an ordinary grid sized
+// to the mask below 8 tokens per CU: with several workgroups per CU it is
+// the faster of the two there (decode, T = 128, cold dispatch: 1279 against
+// 1054 GB/s on 24 masked CUs, 1570 against 1341 on 64).
 Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-  if (dispatch_auto_large(b, T) || cus < b.all_cus) {
+  if (dispatch_auto_large(b, T) || (b.num_cus > 0 && cus < b.all_cus)) {
     *persistent_cus = cus;
     return Variant::VgprWg;
   }
   const int64_t per_cu = row_vec <= 8 * kWave ? 4 : 2;
-  if (T >= per_cu * cus) return Variant::Vgpr2;
+  if (cus >= b.all_cus && T >= per_cu * cus) return Variant::Vgpr2;
   return Variant::Lds1;
 }
 

@@ -71,7 +71,7 @@ enum {
  * workgroups over the 8 XCDs); n is clamped to the device's CU count at
  * launch.  n == 0: no budget; the library picks the launch per kernel --
  * an ordinary grid over the whole device, except that a dispatch of at
- * least 8 tokens per CU (variant "auto"; any size on a budget or mask)
+ * least 8 tokens per CU (variant "auto"; any size on a budget)
  * runs the workgroup-phased register kernel ("vgpr_wg") with whole-row
  * slabs as a persistent grid on every CU it may use: its streaming loads of
  * x take the same time whether or not x is still in the Infinity Cache.  With another variant (or "auto" taking
@@ -105,8 +105,10 @@ int ep_get_num_cus(void);
  *           caller that has just written x may prefer them.  Smaller
  *           batches on every CU take "vgpr2" on an ordinary grid from 2
  *           tokens per CU (4 for rows of at most 8 KiB), which also streams
- *           x, and the smallest ones "lds1".  On a CU budget or mask every
- *           batch size takes "vgpr_wg" on the budget's CUs;
+ *           x, and the smallest ones "lds1".  On a CU budget every batch
+ *           size takes "vgpr_wg" on the budget's CUs; on a CU-masked stream
+ *           without a budget, batches below 8 tokens per CU take "lds1" on
+ *           an ordinary grid sized to the mask;
  *   "vgpr"  rows staged in registers, one load feeding k stores (dispatch)
  *           or k loads feeding one store (combine);
  *   "vgpr2" the same with the next work unit's loads issued before the
