@@ -194,11 +194,19 @@ __global__ __launch_bounds__(kLdThreads) void layout_dispatch_kernel(
 using LdFn = void (*)(const int32_t*, int, int, int, int, const u32x4*, u32x4*, int64_t, int, int, int32_t*,
                       int32_t*, int32_t*, int32_t*, int32_t*);
 
+// k known at compile time up to 8: against the run-time-k form, E = 64,
+// H = 7168, T = 32 .. 170, cold, 1-11% faster (k = 4, T = 170: 10.8 against
+// 12.1 us), bit-identical.
 template <int VPL, bool EVEN>
 LdFn ld_pick_k(int k) {
   switch (k) {
+    case 1: return layout_dispatch_kernel<VPL, 1, EVEN>;
     case 2: return layout_dispatch_kernel<VPL, 2, EVEN>;
+    case 3: return layout_dispatch_kernel<VPL, 3, EVEN>;
+    case 4: return layout_dispatch_kernel<VPL, 4, EVEN>;
+    case 5: return layout_dispatch_kernel<VPL, 5, EVEN>;
     case 6: return layout_dispatch_kernel<VPL, 6, EVEN>;
+    case 7: return layout_dispatch_kernel<VPL, 7, EVEN>;
     case 8: return layout_dispatch_kernel<VPL, 8, EVEN>;
     default: return layout_dispatch_kernel<VPL, 0, EVEN>;
   }

@@ -981,7 +981,7 @@ def test_graph_replay_one_launch_layout_dispatch(name, over):
      ("prefill", dict(T=1, H=8, E=1, k=1)), ("prefill", dict(T=32, E=1024, k=32)),
      ("train", dict(T=300)), ("prefill", dict(T=2000, E=64, k=6)),
      ("train", dict(T=128, k=1)), ("train", dict(T=300, k=3)), ("train", dict(T=777, k=5, H=7176)),
-     ("train", dict(T=512, k=7, E=100))],
+     ("train", dict(T=512, k=7, E=100)), ("prefill", dict(T=128, E=64, k=4)), ("prefill", dict(T=170, E=32, k=5))],
 )
 @pytest.mark.parametrize("budget", [0, 24])
 def test_layout_dispatch_matches_two_calls(name, over, budget):
