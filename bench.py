@@ -343,14 +343,23 @@ def budget_probes(budget):
 
 
 def cpu_model():
+    """The first processor's model name from /proc/cpuinfo, with its family,
+    model and stepping numbers (a virtual machine may report a short name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # end of the first processor's block
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip(), val.strip())
     except OSError:  # pragma: no cover - non-Linux
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def reduce_times(s, steps, budgets):
