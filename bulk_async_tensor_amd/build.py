@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libep.so")
-SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "combine_reduce.hip", "layout_dispatch.hip", "probe.hip"]
+SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "dispatch_rows.hip", "combine.hip", "combine_reduce.hip",
+           "layout_dispatch.hip", "probe.hip"]
 ARCH = "gfx950"
 
 
@@ -25,7 +26,7 @@ ARCH = "gfx950"
 # (the C ABI in ep_api.hip only validates arguments and forwards them).
 KERNEL_SOURCES = {
     "layout": ["layout.hip", "ep_device.hpp", "ep_internal.hpp"],
-    "dispatch": ["dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "dispatch": ["dispatch.hip", "dispatch_rows.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
     "combine": ["combine.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
     "combine_reduce": ["combine_reduce.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],
     "layout_dispatch": ["layout_dispatch.hip", "row_io.hpp", "ep_device.hpp", "ep_internal.hpp"],

@@ -142,10 +142,6 @@ __global__ __launch_bounds__(1024) void dispatch_vgpr2_kernel(EP_DISPATCH_ARGS) 
 // (four whole rows per wave in workgroups of four waves) beat many short
 // ones.  Every wave makes the workgroup's trip count, so each barrier is met
 // by all of its waves.
-constexpr int kWgWaves = 4;
-
-constexpr int wg_units_of(int vpl) { return vpl > 14 ? 2 : 4; }  // at most 224 VGPRs of row data per lane
-
 template <int VPL>
 constexpr int wg_units() {
   return wg_units_of(VPL);
@@ -216,93 +212,6 @@ __global__ __launch_bounds__(kWgWaves * kWave) void dispatch_wg_kernel(EP_DISPAT
   }
 }
 
-// The workgroup-phased kernel for its common case: rows of exactly VPL KiB
-// (row_vec == VPL * 64) with k known at compile time.  A unit is a token; its
-// loads and stores are straight-line, with no per-vector row-end checks (one
-// wave runs per SIMD, so every extra instruction between the memory
-// operations costs issue time), and every workgroup makes the same `trips`.
-template <int VPL, int K, bool NT>
-__global__ __launch_bounds__(kWgWaves * kWave) void dispatch_wg_rows_kernel(const u32x4* __restrict__ x,
-                                                                            u32x4* __restrict__ recv,
-                                                                            const int32_t* __restrict__ dest_row,
-                                                                            int64_t recv_rows, int T, int trips) {
-  constexpr int U = wg_units<VPL>();
-  constexpr int RV = VPL * kWave;
-  const int lane = lane_id();
-  const int wpg = blockDim.x >> 6;
-  const int stride = gridDim.x * wpg;
-  const int first = blockIdx.x * wpg + wave_in_group();
-  for (int r = 0; r < trips; ++r) {
-    u32x4 v[U][VPL];
-    int32_t d[U][K];
-    bool live[U];
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int t = first + (r * U + q) * stride;
-      live[q] = t < T;
-      const int64_t tc = live[q] ? t : 0;
-      const u32x4* src = x + tc * RV + lane;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) v[q][i] = ld16<NT>(src + i * kWave);
-#pragma unroll
-      for (int j = 0; j < K; ++j) d[q][j] = dest_row[tc * K + j];
-    }
-    // keeps every load and destination fetch above the barrier (see
-    // dispatch_wg_kernel)
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) asm volatile("" : "+v"(v[q][i]));
-#pragma unroll
-      for (int j = 0; j < K; ++j) asm volatile("" : "+s"(d[q][j]));
-    }
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-      if (!live[q]) continue;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        if ((uint64_t)(int64_t)d[q][j] >= (uint64_t)recv_rows) continue;
-        u32x4* p = recv + (int64_t)d[q][j] * RV + lane;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) st16<NT>(p + i * kWave, v[q][i]);
-      }
-    }
-  }
-}
-
-using WgRowsFn = void (*)(const u32x4*, u32x4*, const int32_t*, int64_t, int, int);
-
-template <int VPL>
-WgRowsFn wg_rows_pick_k(int k) {
-  switch (k) {
-    case 1: return dispatch_wg_rows_kernel<VPL, 1, true>;
-    case 2: return dispatch_wg_rows_kernel<VPL, 2, true>;
-    case 3: return dispatch_wg_rows_kernel<VPL, 3, true>;
-    case 4: return dispatch_wg_rows_kernel<VPL, 4, true>;
-    case 5: return dispatch_wg_rows_kernel<VPL, 5, true>;
-    case 6: return dispatch_wg_rows_kernel<VPL, 6, true>;
-    case 7: return dispatch_wg_rows_kernel<VPL, 7, true>;
-    case 8: return dispatch_wg_rows_kernel<VPL, 8, true>;
-    default: return nullptr;
-  }
-}
-
-WgRowsFn wg_rows_pick(int vpl, int k) {
-  switch (vpl) {
-    case 2: return wg_rows_pick_k<2>(k);
-    case 4: return wg_rows_pick_k<4>(k);
-    case 6: return wg_rows_pick_k<6>(k);
-    case 7: return wg_rows_pick_k<7>(k);
-    case 8: return wg_rows_pick_k<8>(k);
-    case 10: return wg_rows_pick_k<10>(k);
-    case 12: return wg_rows_pick_k<12>(k);
-    case 14: return wg_rows_pick_k<14>(k);
-    case 16: return wg_rows_pick_k<16>(k);
-    default: return nullptr;
-  }
-}
 
 template <int VPL, int K, bool EVEN, bool NT>
 __global__ __launch_bounds__(1024) void dispatch_lds1_kernel(EP_DISPATCH_ARGS) {
@@ -837,10 +746,10 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;
-  // the workgroup-phased kernel's common case: one slab per row, the row a
-  // whole number of KiB (rows_vpl vectors per lane)
-  const int rows_vpl = (v == Variant::VgprWg && nslab == 1 && row_vec % kWave == 0) ? row_vec / kWave : 0;
-  const WgRowsFn rows_fn = rows_vpl > 0 ? wg_rows_pick(rows_vpl, k) : nullptr;
+  // the workgroup-phased kernel's common case: one slab per row of at most
+  // 16 vectors per lane (rows_vpl), k <= 8: the straight-line kernel
+  const int rows_vpl = (v == Variant::VgprWg && nslab == 1) ? (row_vec + kWave - 1) / kWave : 0;
+  const void* rows_fn = rows_vpl > 0 ? wg_rows_kernel(row_vec, k) : nullptr;
   DispatchFn fn = even ? pick_vpl<true>(v, vpl, k) : pick_vpl<false>(v, vpl, k);
   if (!fn) return hipErrorInvalidValue;
 
@@ -892,7 +801,7 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   if (grid < 1) grid = 1;
   if (rows_fn) {
     if (lds_bytes > 64 * 1024) {
-      hipError_t e = allow_dynamic_lds((const void*)rows_fn, lds_bytes);
+      hipError_t e = allow_dynamic_lds(rows_fn, lds_bytes);
       if (e != hipSuccess) return e;
     }
     const int64_t per_trip = (int64_t)grid * wpg * wg_units_of(rows_vpl);
@@ -907,10 +816,8 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
     for (int64_t t0 = 0; t0 < T; t0 += batch) {
       const int tb = (int)(T - t0 < batch ? T - t0 : batch);
       const int trips = (int)((tb + per_trip - 1) / per_trip);
-      hipLaunchKernelGGL(rows_fn, dim3(grid), dim3(wpg * kWave), lds_bytes, stream,
-                         static_cast<const u32x4*>(x) + t0 * row_vec, static_cast<u32x4*>(recv), dest_row + t0 * k,
-                         recv_rows, tb, trips);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch_wg_rows(rows_fn, grid, wpg, lds_bytes, stream, static_cast<const u32x4*>(x) + t0 * row_vec,
+                                    recv, dest_row + t0 * k, recv_rows, tb, trips, row_vec);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

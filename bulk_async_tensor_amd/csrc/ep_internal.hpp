@@ -66,6 +66,19 @@ hipError_t launch_dispatch_rows(Variant v, const Budget& b, const void* x, int T
 // vectors, at most `cap` (a requested size is rounded down to a compiled one).
 int dispatch_slab_vpl(int row_vec, int cap, int requested);
 
+// The workgroup-phased register dispatch (vgpr_wg) runs workgroups of
+// kWgWaves waves; each wave holds wg_units_of(vpl) units of vpl vectors per
+// lane between its loads and its stores (at most 224 VGPRs of row data).
+constexpr int kWgWaves = 4;
+constexpr int wg_units_of(int vpl) { return vpl > 14 ? 2 : 4; }
+
+// ---- its whole-row kernel (dispatch_rows.hip): rows of row_vec vectors,
+// at most 16 per lane (a partial last KiB allowed), k = 1 .. 8; nullptr
+// otherwise.  launch_wg_rows runs it on `grid` workgroups of `wpg` waves.
+const void* wg_rows_kernel(int row_vec, int k);
+hipError_t launch_wg_rows(const void* kernel, int grid, int wpg, size_t lds_bytes, hipStream_t stream, const void* x,
+                          void* recv, const int32_t* dest_row, int64_t recv_rows, int T, int trips, int row_vec);
+
 // True when variant "auto" dispatches T tokens with its large-batch kernels
 // (at least 8 tokens per CU of the launch), which stream x instead of
 // staging it through cacheable direct-to-LDS loads.

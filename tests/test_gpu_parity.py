@@ -268,6 +268,26 @@ def test_dispatch_vgpr_wg_row_sizes(H, T, budget):
     np.testing.assert_array_equal(got, want)
 
 
+# Rows that are not a whole number of KiB (H a multiple of 8 but not of
+# 512): the whole-row kernel loads its last KiB's tail lanes from the row's
+# last vector and stores only the lanes inside the row.  The tails cover one
+# vector (H = 520, 7176), most of a KiB (H = 1000, 8184) and sizes between,
+# with rows of 1 .. 16 vectors per lane.
+@pytest.mark.parametrize("H,k", [(8, 3), (200, 8), (520, 1), (1000, 5), (2880, 8), (5000, 2), (7176, 7), (8184, 4)])
+@pytest.mark.parametrize("T,budget", [(300, 0), (300, 24), (2600, 256)])
+def test_dispatch_vgpr_wg_ragged_rows(H, k, T, budget):
+    ep.ep_set_variant("vgpr_wg")
+    ep.ep_set_num_cus(budget)
+    wl = make_workload("prefill", seed=3 * T + H + k, T=T, H=H, E=32, k=k)
+    lay = oracle.layout(wl.topk_idx, 32)
+    dest = lay["dest_row"].copy()
+    dest[T // 2, k - 1] = -1
+    dest[T - 1, 0] = 1 << 30
+    got = run_dispatch(wl, dest, T * k)  # receive buffer pre-filled with 0x7E57
+    want = oracle.dispatch(wl.x, dest, T * k, recv=np.full((T * k, H), 0x7E57, dtype=np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
 # The default dispatch on every CU around its batch-size thresholds: lds1
 # below 2 tokens per CU (4 for rows of at most 8 KiB), vgpr2 on the ordinary
 # grid up to 8 tokens per CU, the workgroup-phased kernel from there (the
@@ -275,7 +295,7 @@ def test_dispatch_vgpr_wg_row_sizes(H, T, budget):
 # a 256-CU device).
 @pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
                                    (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536),
-                                   (4096, 3, 1023), (4096, 3, 1024)])
+                                   (4096, 3, 1023), (4096, 3, 1024), (2880, 5, 2048), (7176, 8, 2100)])
 def test_dispatch_default_batch_sizes(H, k, T):
     ep.ep_set_variant("auto")
     ep.ep_set_num_cus(0)
