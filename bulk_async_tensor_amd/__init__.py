@@ -26,6 +26,7 @@ EP_STATUS_EXPERT_OUT_OF_RANGE = 1
 EP_STATUS_DUPLICATE_EXPERT = 2
 EP_MAX_TOPK = 32
 EP_MAX_EXPERTS = 1024
+EP_MAX_ENTRIES = (1 << 31) - 1 - (1 << 22)
 
 VARIANTS = ("auto", "vgpr", "vgpr2", "lds1", "lds2", "vgpr_cached", "phase", "lds3", "pc", "vgpr_wg")
 

@@ -113,17 +113,29 @@ int check_common(int T, int k, int H_or_E, const char* what) {
   (void)H_or_E;
   if (T < 0) return fail(EP_ERR_INVALID_ARG, "%s: T = %d < 0", what, T);
   if (k < 1 || k > EP_MAX_TOPK) return fail(EP_ERR_INVALID_ARG, "%s: k = %d outside [1, %d]", what, k, EP_MAX_TOPK);
-  if ((int64_t)T * k > INT32_MAX) return fail(EP_ERR_INVALID_ARG, "%s: T * k = %lld overflows int32", what,
-                                              (long long)T * k);
+  if ((int64_t)T * k > EP_MAX_ENTRIES)
+    return fail(EP_ERR_INVALID_ARG, "%s: T * k = %lld exceeds EP_MAX_ENTRIES", what, (long long)T * k);
   return EP_OK;
 }
 
-int check_rows(int H, int64_t recv_rows, const char* what) {
-  if (H <= 0 || H % 8 != 0) return fail(EP_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 8", what, H);
-  if (recv_rows < 0 || recv_rows > INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "%s: recv_rows = %lld outside [0, 2^31)", what, (long long)recv_rows);
-  if ((int64_t)recv_rows * H * 2 / 2 / H != recv_rows) return fail(EP_ERR_INVALID_ARG, "%s: size overflow", what);
+// Rows of H elements (T token rows or recv_rows receive rows): their count
+// in 512-element slabs, the finest slab a kernel runs, must stay within
+// EP_MAX_ENTRIES (unit counters are 32-bit).
+int check_slabs(int64_t rows, int H, const char* name, const char* what) {
+  const int64_t slabs = rows * ((H + 511) / 512);
+  if (slabs > EP_MAX_ENTRIES)
+    return fail(EP_ERR_INVALID_ARG, "%s: %s * ceil(H / 512) = %lld exceeds EP_MAX_ENTRIES", what, name,
+                (long long)slabs);
   return EP_OK;
+}
+
+int check_rows(int H, int64_t recv_rows, int T, const char* what) {
+  if (H <= 0 || H % 8 != 0) return fail(EP_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 8", what, H);
+  if (recv_rows < 0 || recv_rows > EP_MAX_ENTRIES)
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_rows = %lld outside [0, EP_MAX_ENTRIES]", what, (long long)recv_rows);
+  int rc = check_slabs(recv_rows, H, "recv_rows", what);
+  if (rc) return rc;
+  return T > 0 ? check_slabs(T, H, "T", what) : EP_OK;
 }
 
 // Scratch of ep_layout_noalloc: the (chunk, expert) count table and the
@@ -314,7 +326,7 @@ int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, voi
                 void* stream) {
   int rc = check_common(T, k, H, "ep_dispatch");
   if (rc) return rc;
-  rc = check_rows(H, recv_rows, "ep_dispatch");
+  rc = check_rows(H, recv_rows, T, "ep_dispatch");
   if (rc) return rc;
   if (T > 0 && (!x || !dest_row || (!recv && recv_rows > 0)))
     return fail(EP_ERR_INVALID_ARG, "ep_dispatch: null x/dest_row/recv");
@@ -337,7 +349,7 @@ int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void*
   int rc = check_layout_args(topk_idx, T, k, E, counts, offsets, dest_row, src_token, status, workspace,
                              workspace_bytes, "ep_layout_dispatch");
   if (rc) return rc;
-  rc = check_rows(H, recv_rows, "ep_layout_dispatch");
+  rc = check_rows(H, recv_rows, T, "ep_layout_dispatch");
   if (rc) return rc;
   if (T > 0 && (!x || (!recv && recv_rows > 0)))
     return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch: null x/recv");
@@ -356,7 +368,7 @@ int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void*
 int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void* recv, int64_t recv_rows,
                      void* stream) {
   if (T < 0) return fail(EP_ERR_INVALID_ARG, "ep_dispatch_rows: T = %d < 0", T);
-  int rc = check_rows(H, recv_rows, "ep_dispatch_rows");
+  int rc = check_rows(H, recv_rows, T, "ep_dispatch_rows");
   if (rc) return rc;
   if (recv_rows > 0 && (!x || !src_token || !recv))
     return fail(EP_ERR_INVALID_ARG, "ep_dispatch_rows: null x/src_token/recv");
@@ -378,7 +390,7 @@ int ep_combine(const void* y, int64_t recv_rows, int H, const int32_t* dest_row,
                void* out, void* stream) {
   int rc = check_common(T, k, H, "ep_combine");
   if (rc) return rc;
-  rc = check_rows(H, recv_rows, "ep_combine");
+  rc = check_rows(H, recv_rows, T, "ep_combine");
   if (rc) return rc;
   if (T > 0 && (!dest_row || !topk_w || !out || (!y && recv_rows > 0)))
     return fail(EP_ERR_INVALID_ARG, "ep_combine: null y/dest_row/topk_w/out");
@@ -406,7 +418,7 @@ int ep_combine_reduce(const void* y, int64_t recv_rows, int H, const int32_t* sr
                       void* stream) {
   int rc = check_common(T, k, H, "ep_combine_reduce");
   if (rc) return rc;
-  rc = check_rows(H, recv_rows, "ep_combine_reduce");
+  rc = check_rows(H, recv_rows, T, "ep_combine_reduce");
   if (rc) return rc;
   if (T > 0 && (!dest_row || !topk_w || !out || (recv_rows > 0 && (!y || !src_token))))
     return fail(EP_ERR_INVALID_ARG, "ep_combine_reduce: null y/src_token/dest_row/topk_w/out");

@@ -63,6 +63,16 @@ enum {
 #define EP_MAX_EXPERTS 1024
 
 /*
+ * Largest count of (token, slot) entries (T*k), of receive rows, and of
+ * 512-element row slabs (T*ceil(H/512) and recv_rows*ceil(H/512)) that a
+ * call accepts: 2^31 - 1 - 2^22.  The kernels count their work in 32-bit
+ * integers and may step one grid stride past the last unit before they
+ * stop; the margin keeps that step from wrapping.  At H = 512 the slab
+ * bound is a 2 TiB buffer, beyond any single device.
+ */
+#define EP_MAX_ENTRIES 2143289343
+
+/*
  * Compute-unit budget of the copy kernels, after [DeepEP-TMA] section
  * "Minimal SM Occupancy Configuration" (a process-wide cap on the SMs the
  * communication kernels occupy).  n > 0: dispatch, combine and the probes
@@ -191,7 +201,7 @@ size_t ep_layout_workspace_bytes(int T, int k, int E);
  * inside one token is flagged but still placed as its own entry.
  * workspace: device scratch of at least ep_layout_workspace_bytes(T, k, E)
  * bytes, 16-byte aligned, owned by the caller, clobbered by the call.
- * Limits: 1 <= k <= EP_MAX_TOPK, k <= E <= EP_MAX_EXPERTS, T*k < 2^31.
+ * Limits: 1 <= k <= EP_MAX_TOPK, k <= E <= EP_MAX_EXPERTS, T*k <= EP_MAX_ENTRIES.
  */
 int ep_layout(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
               int32_t* dest_row, int32_t* src_token, int32_t* status, void* workspace,
@@ -229,7 +239,9 @@ int ep_layout_noalloc(const int32_t* topk_idx, int T, int k, int E, int32_t* cou
  *   recv      bf16 [recv_rows, H]; an entry whose dest_row is outside
  *             [0, recv_rows) is skipped; rows nobody targets are untouched.
  * With valid, distinct routing recv_rows = T*k covers every entry.
- * Limits: 1 <= k <= EP_MAX_TOPK, 0 <= recv_rows < 2^31, T*k < 2^31.
+ * Limits: 1 <= k <= EP_MAX_TOPK, 0 <= recv_rows <= EP_MAX_ENTRIES,
+ * T*k <= EP_MAX_ENTRIES, and T and recv_rows times ceil(H/512) at most
+ * EP_MAX_ENTRIES.
  */
 int ep_dispatch(const void* x, int T, int H, const int32_t* dest_row, int k, void* recv,
                 int64_t recv_rows, void* stream);
@@ -266,7 +278,8 @@ int ep_layout_dispatch(const int32_t* topk_idx, int T, int k, int E, const void*
  *   x          bf16 [T, H]
  *   src_token  int32 [recv_rows]
  *   recv       bf16 [recv_rows, H]
- * Limits: 0 <= recv_rows < 2^31.  The variant "vgpr_cached" selects
+ * Limits: 0 <= recv_rows <= EP_MAX_ENTRIES, and T and recv_rows times
+ * ceil(H/512) at most EP_MAX_ENTRIES.  The variant "vgpr_cached" selects
  * streaming (non-temporal) loads of x; every other keeps them cacheable.
  */
 int ep_dispatch_rows(const void* x, int T, int H, const int32_t* src_token, void* recv, int64_t recv_rows,

@@ -168,6 +168,47 @@ def dispatch(lib, x=A16, T=16, H=1024, dest=A4, k=2, recv=A16, rows=32):
     return lib.ep_dispatch(x, T, H, dest, k, recv, rows, None)
 
 
+def test_max_entries_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define EP_MAX_ENTRIES (\d+)", text)
+    assert m and int(m.group(1)) == ep.EP_MAX_ENTRIES == 2**31 - 1 - 2**22
+
+
+# Counts at EP_MAX_ENTRIES pass the size checks; one more is refused before
+# anything is launched.  A count that passes reaches the null-pointer check
+# (x = None here), so the two codes tell which check stopped the call.
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(T=ep.EP_MAX_ENTRIES, k=1, H=8, rows=0), ep.EP_ERR_INVALID_ARG),
+        (dict(T=ep.EP_MAX_ENTRIES // 2, k=2, H=8, rows=0), ep.EP_ERR_INVALID_ARG),
+        (dict(T=ep.EP_MAX_ENTRIES + 1, k=1, H=8, rows=0), ep.EP_ERR_INVALID_ARG),
+        (dict(T=ep.EP_MAX_ENTRIES // 2 + 1, k=2, H=8, rows=0), ep.EP_ERR_INVALID_ARG),
+        (dict(T=1, k=1, H=8, rows=ep.EP_MAX_ENTRIES + 1), ep.EP_ERR_INVALID_ARG),
+        (dict(T=1, k=1, H=1024, rows=ep.EP_MAX_ENTRIES // 2 + 1), ep.EP_ERR_INVALID_ARG),
+        (dict(T=ep.EP_MAX_ENTRIES // 2 + 1, k=1, H=1024, rows=0), ep.EP_ERR_INVALID_ARG),
+    ],
+)
+def test_dispatch_size_limits(lib, kw, code):
+    assert dispatch(lib, x=None, **kw) == code
+    msg = lib.ep_last_error().decode()
+    over = kw["T"] * kw["k"] > ep.EP_MAX_ENTRIES or kw["rows"] > ep.EP_MAX_ENTRIES or \
+        max(kw["T"], kw["rows"]) * -(-kw["H"] // 512) > ep.EP_MAX_ENTRIES
+    assert ("EP_MAX_ENTRIES" in msg) == over, msg
+    if not over:
+        assert "null" in msg
+
+
+def test_combine_and_rows_size_limits(lib):
+    big = ep.EP_MAX_ENTRIES // 2 + 1  # two slabs per row at H = 1024
+    assert lib.ep_combine(A16, 32, 1024, A4, A4, big, 1, A16, None) == ep.EP_ERR_INVALID_ARG
+    assert "EP_MAX_ENTRIES" in lib.ep_last_error().decode()
+    assert lib.ep_dispatch_rows(A16, 16, 1024, A4, A16, big, None) == ep.EP_ERR_INVALID_ARG
+    assert "EP_MAX_ENTRIES" in lib.ep_last_error().decode()
+    assert lib.ep_dispatch_rows(A16, big, 1024, A4, A16, 32, None) == ep.EP_ERR_INVALID_ARG
+    assert "EP_MAX_ENTRIES" in lib.ep_last_error().decode()
+
+
 @pytest.mark.parametrize(
     "kw,code",
     [
