@@ -39,9 +39,11 @@ BUDGETS = [0, 16, 24, 32, 64, 256]
 def _reset_settings():
     ep.ep_set_num_cus(0)
     ep.ep_set_variant("auto")
+    ep.ep_set_slab(0)
     yield
     ep.ep_set_num_cus(0)
     ep.ep_set_variant("auto")
+    ep.ep_set_slab(0)
 
 
 def gpu_layout(wl):
@@ -1206,7 +1208,9 @@ def _random_cases(n, seed=2026):
             continue
         cases.append(dict(name=str(rng.choice(["train", "prefill"])), T=T, H=H, E=E, k=k,
                           budget=int(rng.choice([0, 0, 24, 64, 200, 256])),
-                          variant=str(rng.choice(["auto", "auto", "lds1", "vgpr", "phase", "vgpr_wg", "vgpr2"])),
+                          variant=str(rng.choice(["auto", "auto", "auto", "lds1", "vgpr", "phase", "vgpr_wg", "vgpr2",
+                                                  "lds2", "lds3", "pc", "vgpr_cached"])),
+                          slab=int(rng.choice([0, 0, 0, 1, 2, 4, 7, 8, 14, 16])),
                           one_launch=bool(rng.integers(0, 2))))
     return cases
 
@@ -1214,11 +1218,12 @@ def _random_cases(n, seed=2026):
 # Seeded random shapes through the default and forced launches: layout and
 # dispatch bit-exact, combine against the oracle, with and without the
 # one-launch layout + dispatch.
-@pytest.mark.parametrize("case", _random_cases(150), ids=lambda c: "{name}-T{T}-H{H}-E{E}-k{k}-b{budget}-{variant}"
+@pytest.mark.parametrize("case", _random_cases(150), ids=lambda c: "{name}-T{T}-H{H}-E{E}-k{k}-b{budget}-{variant}-s{slab}"
                          .format(**c) + ("-one" if c["one_launch"] else ""))
 def test_random_shapes(case):
     ep.ep_set_num_cus(case["budget"])
     ep.ep_set_variant(case["variant"])
+    ep.ep_set_slab(case["slab"])
     wl = make_workload(case["name"], seed=case["T"] + case["H"], T=case["T"], H=case["H"], E=case["E"],
                        k=case["k"])
     c = wl.config
