@@ -536,10 +536,29 @@ int combine_phase_seg(const Budget& b, int row_vec, int k) {
 // the reads in flight: 4.2 against 5.1 TB/s on 128 CUs, 4.3 against 5.8 on
 // 192, so there the 16-wave shape stays.  Larger rows would drop to one row
 // per wave and smaller ones to fewer rows per CU.
-PhaseShape combine_phase_shape(int row_vec, int seg_vec, int cus, int all_cus) {
+//
+// At 9 vectors a wave could hold three rows.  It takes two when that needs
+// fewer passes over the grid (launches times rows per wave): at T = 8192 on
+// 256 CUs three rows give 2731 units, two launches at two-thirds fill, and
+// two rows give two full launches.  Cold, H = 4608, k = 8: T = 4096 65.2
+// against 56.2 us, T = 8192 128.6 against 111.6; H = 4160, k = 6, 7, 8 at
+// T = 4096 and 8192 6 to 13% faster (k = 8 had taken vgpr, whose fill rule
+// the two-thirds fill failed); k = 5 and T = 2048 or 16384 within 2%.
+//
+// The 16-wave shape keeps its packing: the same rule there (at least two
+// tokens per wave) measured within +-5% of it on rows of 2 to 8 KiB, k = 4,
+// 6, 8, T = 2048 to 16384, a mean of +0.5%, with as many losses as gains.
+PhaseShape combine_phase_shape(int row_vec, int seg_vec, int cus, int all_cus, int64_t T) {
   const int nv = (row_vec + kWave - 1) / kWave;
-  if (seg_vec == 1 && nv >= 9 && nv <= 14 && cus >= all_cus)
-    return phase_shape(row_vec, kPhaseWideHeld, kPhaseWideWpg);
+  if (seg_vec == 1 && nv >= 9 && nv <= 14 && cus >= all_cus) {
+    PhaseShape p = phase_shape(row_vec, kPhaseWideHeld, kPhaseWideWpg);
+    if (p.tpu > 2 && T > 0) {
+      const int64_t slots = (int64_t)cus * p.wpg;
+      auto passes = [&](int t) { return (T + slots * t - 1) / (slots * t) * t; };
+      if (passes(2) < passes(p.tpu)) p.tpu = 2;
+    }
+    return p;
+  }
   return phase_shape(row_vec);
 }
 
@@ -551,7 +570,7 @@ hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int r
   // in the 16-wave shape), which frees registers for the reads
   const int seg_vec = combine_phase_seg(b, row_vec, k);
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
-  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
+  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus, T);
   const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
   const int held = ps.held == kPhaseWideHeld ? kPhaseWideHeld : unit_vec <= 14 ? 14 : 16;
   PhaseFn fn = even ? pick_phase<true>(seg_vec, held, k) : pick_phase<false>(seg_vec, held, k);
@@ -618,7 +637,7 @@ bool phase_preferred(const Budget& b, int row_vec, int T, int k) {
   if (2 * cus < b.all_cus) return false;
   const int seg_vec = combine_phase_seg(b, row_vec, k);
   if (k <= 4 && seg_vec != 2) return false;
-  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus);
+  const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus, T);
   const int64_t units = phase_units(ps, phase_batch(ps, T, cus));  // the largest launch's
   const int64_t slots = (int64_t)cus * ps.wpg;
   if (cus >= b.all_cus && ps.held != kPhaseWideHeld) return k <= 2 ? units * 5 >= slots * 3 : units * 20 >= slots * 9;

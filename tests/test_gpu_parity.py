@@ -494,13 +494,17 @@ def test_combine_phase_batches(T, budget, k):
 # above it.  (H, k, T):
 # H = 2048 holds four tokens per unit (16384 per full launch), H = 3072 and
 # 4096 two (8192), H = 5120 and 7168 at k >= 6 two rows per wave in 8-wave
-# workgroups (4096).
+# workgroups (4096).  Rows of 9 vectors per lane (H = 4104 .. 4608) take
+# three rows per wave, or two where that needs fewer passes over the grid:
+# two at T = 4096 and 8192, three at T = 6144 and 12288 (a tie), with
+# a ragged last vector at H = 4104 and 4160.
 @pytest.mark.parametrize(
     "H,k,T",
     [(2048, 4, 7000), (2048, 4, 8192), (4096, 8, 3686), (4096, 6, 4505), (3072, 2, 4600), (3072, 2, 4915),
      (2048, 2, 9830), (5120, 8, 2457), (5120, 8, 2800), (5120, 8, 2900), (7168, 8, 2860), (7168, 6, 2800),
      (4096, 3, 3500), (4096, 3, 3700), (2048, 1, 9600), (2048, 1, 9900), (7168, 5, 3760), (7168, 5, 3780),
-     (7168, 7, 3068), (7168, 7, 3076)],
+     (7168, 7, 3068), (7168, 7, 3076), (4608, 8, 8192), (4160, 6, 4096), (4104, 7, 6144), (4160, 5, 12288),
+     (4160, 8, 4097)],
 )
 def test_combine_default_partial_fill(H, k, T):
     ep.ep_set_variant("auto")
