@@ -709,14 +709,30 @@ bool dispatch_auto_large(const Budget& b, int64_t T) {
 // to the mask below 8 tokens per CU: with several workgroups per CU it is
 // the faster of the two there (decode, T = 128, cold dispatch: 1279 against
 // 1054 GB/s on 24 masked CUs, 1570 against 1341 on 64).
-Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int* persistent_cus) {
+//
+// Rows of more than 8 KiB that are not a whole number of KiB, at k = 6 or
+// 8, take the whole-row workgroup-phased kernel on the ordinary grid instead
+// of vgpr2 in that range: vgpr2 runs them in 14-vector slabs that spill
+// registers to scratch (9 to 14 vectors per lane) or in 1 KiB slabs (15
+// and 16).  Cold, us, every CU, same-run A/B, H = 4104 / 5000 / 6000 /
+// 7176, k = 8: T = 512 12.8 / 14.2 / 15.8 / 18.6 against 16.7 / 18.4 /
+// 19.8 / 21.4, T = 2000 36.4 / 43.1 / 51.4 / 63.4 against 40.4 / 47.6 /
+// 53.6 / 68.1; k = 6 up to 24% faster (one point 2% slower).  k = 7 lost
+// 1-9% and k = 5 was even, and at k = 2 and 4 vgpr2 was ahead from
+// T = 1536 (up to 22%), so they keep vgpr2.  Whole-KiB rows stay on vgpr2
+// (H = 7168, k = 8: 16.0 / 28.0 / 40.2 against 17.1 / 29.1 / 43.0 us at
+// T = 512 / 1024 / 1536).
+Variant dispatch_auto(const Budget& b, int64_t T, int row_vec, int k, int* persistent_cus) {
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   if (dispatch_auto_large(b, T) || (b.num_cus > 0 && cus < b.all_cus)) {
     *persistent_cus = cus;
     return Variant::VgprWg;
   }
   const int64_t per_cu = row_vec <= 8 * kWave ? 4 : 2;
-  if (cus >= b.all_cus && T >= per_cu * cus) return Variant::Vgpr2;
+  if (cus >= b.all_cus && T >= per_cu * cus) {
+    const bool ragged_wide = row_vec > 8 * kWave && row_vec <= 16 * kWave && row_vec % kWave != 0;
+    return ragged_wide && (k == 6 || k == 8) ? Variant::VgprWg : Variant::Vgpr2;
+  }
   return Variant::Lds1;
 }
 
@@ -725,7 +741,7 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const int row_vec = H / 8;
   int auto_cus = 0;  // the persistent grid the default chose (0: none)
   const bool chosen = v == Variant::Auto;
-  if (chosen) v = dispatch_auto(b, T, row_vec, &auto_cus);
+  if (chosen) v = dispatch_auto(b, T, row_vec, k, &auto_cus);
   const bool known_k = (k == 2 || k == 4 || k == 6 || k == 8);
   if ((v == Variant::Lds2 || v == Variant::Lds3 || v == Variant::Phase) && !known_k) v = Variant::Lds1;
   if (v == Variant::Phase) return launch_dispatch_phase(b, x, T, row_vec, dest_row, k, recv, recv_rows, stream);
@@ -763,12 +779,14 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   // write throughput was measured highest with about a quarter of the CUs
   // issuing them (more add contention, not bandwidth); smaller k carry more
   // reads and take more CUs.  Small batches keep the ordinary grid, whose
-  // start-up is cheaper, and so does the default's choice of vgpr2 for
-  // smaller batches (measured on the ordinary grid).
+  // start-up is cheaper, and so does the default's choice of vgpr2 or of
+  // the workgroup-phased kernel for smaller batches (measured on the
+  // ordinary grid).
   int budget = b.num_cus;
   const int write_cus = dispatch_write_cus(k);
   if (auto_cus > 0) budget = auto_cus;
-  else if (budget == 0 && !(chosen && v == Variant::Vgpr2) && units >= write_cus * 16 * 2) budget = write_cus;
+  else if (budget == 0 && !(chosen && (v == Variant::Vgpr2 || v == Variant::VgprWg)) && units >= write_cus * 16 * 2)
+    budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W
     // slabs each; always a persistent grid (one workgroup per CU)

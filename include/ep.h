@@ -115,7 +115,9 @@ int ep_get_num_cus(void);
  *           caller that has just written x may prefer them.  Smaller
  *           batches on every CU take "vgpr2" on an ordinary grid from 2
  *           tokens per CU (4 for rows of at most 8 KiB), which also streams
- *           x, and the smallest ones "lds1".  On a CU budget every batch
+ *           x; rows of 8 to 16 KiB that are not a whole number of KiB take
+ *           "vgpr_wg" on that ordinary grid instead at k = 6 and 8.  The
+ *           smallest batches take "lds1".  On a CU budget every batch
  *           size takes "vgpr_wg" on the budget's CUs; on a CU-masked stream
  *           without a budget, batches below 8 tokens per CU take "lds1" on
  *           an ordinary grid sized to the mask;

@@ -294,10 +294,14 @@ def test_dispatch_vgpr_wg_ragged_rows(H, k, T, budget):
 # below 2 tokens per CU (4 for rows of at most 8 KiB), vgpr2 on the ordinary
 # grid up to 8 tokens per CU, the workgroup-phased kernel from there (the
 # thresholds scale with the device's CU count; these sizes bracket them on
-# a 256-CU device).
+# a 256-CU device).  Rows of 8 to 16 KiB with a partial last KiB at k = 6
+# or 8 take the workgroup-phased kernel on the ordinary grid in vgpr2's
+# range (H = 4104, 5000, 7176, 8184); at k = 7 they keep vgpr2.
 @pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
                                    (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536),
-                                   (4096, 3, 1023), (4096, 3, 1024), (2880, 5, 2048), (7176, 8, 2100)])
+                                   (4096, 3, 1023), (4096, 3, 1024), (2880, 5, 2048), (7176, 8, 2100),
+                                   (4104, 8, 511), (4104, 8, 512), (5000, 6, 1000), (7176, 8, 2047), (7176, 6, 1537),
+                                   (8184, 8, 700), (5000, 7, 1000)])
 def test_dispatch_default_batch_sizes(H, k, T):
     ep.ep_set_variant("auto")
     ep.ep_set_num_cus(0)
