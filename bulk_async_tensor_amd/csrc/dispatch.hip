@@ -774,19 +774,23 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
   const size_t per_wave = lds ? (size_t)stages * vpl * kWaveVecBytes : 0;
   int wpg, grid;
   size_t lds_bytes;
-  // With no budget set, a large dispatch still runs as a persistent grid on
-  // dispatch_write_cus(k) CUs: at k = 8 its traffic is 8/9 writes, and HBM
-  // write throughput was measured highest with about a quarter of the CUs
-  // issuing them (more add contention, not bandwidth); smaller k carry more
-  // reads and take more CUs.  Small batches keep the ordinary grid, whose
-  // start-up is cheaper, and so does the default's choice of vgpr2 or of
-  // the workgroup-phased kernel for smaller batches (measured on the
-  // ordinary grid).
+  // With no budget set, a large dispatch by a named variant still runs as a
+  // persistent grid on dispatch_write_cus(k) CUs: at k = 8 its traffic is
+  // 8/9 writes, and HBM write throughput was measured highest with about a
+  // quarter of the CUs issuing them (more add contention, not bandwidth);
+  // smaller k carry more reads and take more CUs.  Small batches keep the
+  // ordinary grid, whose start-up is cheaper.  The default's own choices
+  // never take this grid: it picks its persistent grid itself from 8 tokens
+  // per CU and keeps the ordinary grid below that.  lds1 persistent on 64
+  // CUs, where its many 1-2 KiB slabs of rows with a partial last KiB, or
+  // the slabs of rows over 16 KiB, reached the unit count, ran up to 1.9x
+  // slower cold (H = 9000, k = 6, T = 256: 20.6 against 11.0 us; H = 32768,
+  // k = 8, T = 511: 106.1 against 70.1; H = 5000, k = 8, T = 511: 23.8
+  // against 14.1), and no point measured gained from it.
   int budget = b.num_cus;
   const int write_cus = dispatch_write_cus(k);
   if (auto_cus > 0) budget = auto_cus;
-  else if (budget == 0 && !(chosen && (v == Variant::Vgpr2 || v == Variant::VgprWg)) && units >= write_cus * 16 * 2)
-    budget = write_cus;
+  else if (budget == 0 && !chosen && units >= write_cus * 16 * 2) budget = write_cus;
   if (v == Variant::Pc) {
     // one producer and W consumer waves per workgroup, a two-slot ring of W
     // slabs each; always a persistent grid (one workgroup per CU)

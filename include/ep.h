@@ -84,8 +84,9 @@ enum {
  * least 8 tokens per CU (variant "auto"; any size on a budget)
  * runs the workgroup-phased register kernel ("vgpr_wg") with whole-row
  * slabs as a persistent grid on every CU it may use: its streaming loads of
- * x take the same time whether or not x is still in the Infinity Cache.  With another variant (or "auto" taking
- * "lds1"), a dispatch of at least 32 work units per CU of its default
+ * x take the same time whether or not x is still in the Infinity Cache;
+ * "auto" keeps its smaller batches on an ordinary grid.  With another
+ * variant named, a dispatch of at least 32 work units per CU of its default
  * budget runs persistent on that budget: 64 CUs for k >= 5 (at k = 8 its
  * traffic is 8/9 writes, and HBM write throughput peaks with about a
  * quarter of the CUs issuing them), 96 for k = 2..4 and 128 for k = 1,

@@ -296,12 +296,15 @@ def test_dispatch_vgpr_wg_ragged_rows(H, k, T, budget):
 # thresholds scale with the device's CU count; these sizes bracket them on
 # a 256-CU device).  Rows of 8 to 16 KiB with a partial last KiB at k = 6
 # or 8 take the workgroup-phased kernel on the ordinary grid in vgpr2's
-# range (H = 4104, 5000, 7176, 8184); at k = 7 they keep vgpr2.
+# range (H = 4104, 5000, 7176, 8184); at k = 7 they keep vgpr2.  lds1 under
+# the default stays on the ordinary grid also where its slabs are many
+# (H = 5000 and 9000: 2 and 1 KiB slabs; H = 32768: 8 slabs per row).
 @pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
                                    (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536),
                                    (4096, 3, 1023), (4096, 3, 1024), (2880, 5, 2048), (7176, 8, 2100),
                                    (4104, 8, 511), (4104, 8, 512), (5000, 6, 1000), (7176, 8, 2047), (7176, 6, 1537),
-                                   (8184, 8, 700), (5000, 7, 1000)])
+                                   (8184, 8, 700), (5000, 7, 1000), (9000, 6, 256), (5000, 8, 511),
+                                   (32768, 4, 384)])
 def test_dispatch_default_batch_sizes(H, k, T):
     ep.ep_set_variant("auto")
     ep.ep_set_num_cus(0)
@@ -371,17 +374,21 @@ def run_combine(wl, y_u16, dest_row_np):
     return from_dev_bf16(out)
 
 
-# The default launches depend on k: the dispatch's persistent budget (128 CUs
-# at k = 1, 96 at k = 2..4, 64 from k = 5) and the combine's choice between
-# the phased and the register kernel (by k and by how full each phased launch
-# would be).  Each k runs once at a size that takes the persistent dispatch,
-# with the per-expert scale as the expert.
+# Launches that depend on k: the persistent budget a named dispatch variant
+# takes with no budget set (128 CUs at k = 1, 96 at k = 2..4, 64 from k = 5;
+# lds1 here, with half-row slabs), the default dispatch (the workgroup-phased
+# kernel on every CU at these sizes), and the combine's choice between the
+# phased and the register kernel (by k and by how full each phased launch
+# would be).  The per-expert scale is the expert.
 @pytest.mark.parametrize("k,T", [(1, 4500), (2, 3100), (3, 3000), (4, 2500), (5, 2100), (6, 5461), (8, 4500)])
 def test_default_launch_across_k(k, T):
     wl = make_workload("train", seed=40 + k, T=T, k=k)
     lay = oracle.layout(wl.topk_idx, wl.config.E)
     R = T * k
     ref_recv = oracle.dispatch(wl.x, lay["dest_row"], R)
+    ep.ep_set_variant("lds1")
+    np.testing.assert_array_equal(run_dispatch(wl, lay["dest_row"], R), ref_recv)
+    ep.ep_set_variant("auto")
     np.testing.assert_array_equal(run_dispatch(wl, lay["dest_row"], R), ref_recv)
     y = oracle.expert_scale(ref_recv, lay["offsets"], wl.scales)
     assert_combine_close(run_combine(wl, y, lay["dest_row"]), oracle.combine(y, lay["dest_row"], wl.topk_w))
