@@ -758,7 +758,16 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
                 : v == Variant::Vgpr2 ? 14
                 : v == Variant::Pc ? (b.slab_vpl > 0 ? 16 : 14)
                 : (ring || b.slab_vpl == 0) ? 8 : 16;
-  const int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
+  int vpl = choose_vpl(row_vec, cap, b.slab_vpl);
+  // Rows of more than 16 vectors per lane that no compiled slab divides
+  // would get the largest slab that does (2 vectors at 18, 22, 26 and 30):
+  // the workgroup-phased kernel takes 14-vector slabs there, the last one
+  // partial.  Cold, us, every CU, T = 4096, k = 8: H = 9216 138.7 against
+  // 148.2, H = 11264 165.2 against 178.0, H = 13312 197.3 against 211.7,
+  // H = 15360 233.9 against 244.1; k = 2 3-7% faster; H = 12288 (24
+  // vectors, 8-vector slabs) 1.6% faster.
+  const int vpr = (row_vec + kWave - 1) / kWave;
+  if (v == Variant::VgprWg && b.slab_vpl == 0 && vpr > 16 && vpr % 16 != 0) vpl = 14;
   const int nslab = (row_vec + vpl * kWave - 1) / (vpl * kWave);
   if ((int64_t)T * nslab > INT32_MAX) return hipErrorInvalidValue;
   const int units = T * nslab;

@@ -170,9 +170,12 @@ const char* ep_get_variant(void);
 /*
  * Staging geometry (process-wide): the row slab a wave moves per work unit,
  * in 16-byte vectors per lane (one vector per lane = 1 KiB per wave).
- * 0 = each kernel's default (dispatch: the whole row when it is at most
- * 8 KiB, else slabs of at most 8 KiB -- half rows at H = 7168; combine:
- * 2 KiB per source row).  Accepted: 0, 1, 2, 4, 7, 8, 14, 16; a kernel
+ * 0 = each kernel's default (dispatch: "vgpr_wg" the whole row up to
+ * 16 KiB, else 16 KiB slabs where they divide the row and 14 KiB slabs
+ * otherwise, the last one partial; "vgpr2" and "pc" the whole row up
+ * to 14 KiB; the LDS-staged kernels the whole row up to 8 KiB, else slabs
+ * of at most 8 KiB -- half rows at H = 7168; combine: 2 KiB per source
+ * row).  Accepted: 0, 1, 2, 4, 7, 8, 14, 16; a kernel
  * rounds a value down to the sizes it is compiled for (combine: 1, 2, 4).
  * The choice changes only speed, never results.  Returns EP_OK or
  * EP_ERR_UNSUPPORTED.
