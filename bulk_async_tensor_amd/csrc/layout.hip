@@ -487,11 +487,19 @@ size_t fused_lds_bytes(int T, int k, int E) {
 //    on a few addresses (with E <= 64 some always do);
 //  - the two-launch path costs 10.4 to 12.4 us over the same range.
 // So: one launch up to a few chunks, and up to 64 chunks when E > 64.
+// Past 12288 tokens the one-launch kernel's cost grows with the tokens, not
+// the entries, and the two launches win at any k (cold, E = 128 / 256:
+// k = 2, T = 32768 19.7 / 20.0 against 14.3 / 15.4 us, T = 20000 15.0 /
+// 15.4 against 14.2 / 15.1; k = 4, T = 16384 16.6 / 17.4 against 14.4 /
+// 15.9), while up to it the one launch stays ahead (k = 4, T = 12288
+// 14.2 / 14.8 against 14.5 / 15.6; k = 8, T = 6144 13.3 / 13.6 against
+// 15.2 / 16.4).
 #ifndef EP_LAYOUT_FUSED_MAX_CHUNKS
 #define EP_LAYOUT_FUSED_MAX_CHUNKS 64
 #endif
 constexpr int64_t kFusedFewChunks = 4;
 constexpr int kFusedMinExperts = 65;  // one launch past a few chunks only above this many experts
+constexpr int kFusedMaxTokens = 12288;  // and for at most this many tokens
 // The two-launch path reads the whole (chunk, expert) table in every
 // workgroup; past this many counts the three-launch path scans it once.
 constexpr int64_t kRankTableMax = 64 * 1024;
@@ -503,7 +511,8 @@ Path layout_path(int T, int k, int E) {
   const int64_t N = (int64_t)T * k;
   const int64_t nf = (N + kFusedChunk - 1) / kFusedChunk;
   const bool fits = fused_lds_bytes(T, k, E) <= 144 * 1024;
-  if (fused_k(k) && fits && (nf <= kFusedFewChunks || (E >= kFusedMinExperts && nf <= EP_LAYOUT_FUSED_MAX_CHUNKS)))
+  if (fused_k(k) && fits &&
+      (nf <= kFusedFewChunks || (E >= kFusedMinExperts && nf <= EP_LAYOUT_FUSED_MAX_CHUNKS && T <= kFusedMaxTokens)))
     return Path::Fused;
   const int64_t ct = kChunkEntries / k;
   const int64_t nch = (T + ct - 1) / ct;

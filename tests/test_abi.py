@@ -70,11 +70,17 @@ def test_slab_setting(lib):
 
 def test_workspace_bytes(lib):
     # the one-launch path needs no workspace: a few 1024-entry chunks, or up to 64 chunks with E > 64
+    # and at most 12288 tokens
     assert lib.ep_layout_workspace_bytes(128, 8, 256) == 0
     assert lib.ep_layout_workspace_bytes(128, 2, 8) == 0
     assert lib.ep_layout_workspace_bytes(4096, 8, 256) == 0
     assert lib.ep_layout_workspace_bytes(8192, 8, 256) == 0
     assert lib.ep_layout_workspace_bytes(512, 8, 64) == 0
+    assert lib.ep_layout_workspace_bytes(12288, 4, 128) == 0  # 48 chunks, at the token cap
+    # past 12288 tokens two launches even within 64 chunks: 12289 x 4 -> 49 chunks of 256 tokens,
+    # 49 * 256 * 4 = 50,176 (256-aligned); 20000 x 2 -> 40 chunks of 512 tokens
+    assert lib.ep_layout_workspace_bytes(12289, 4, 256) == 49 * 256 * 4 + 49 * 4
+    assert lib.ep_layout_workspace_bytes(20000, 2, 128) == 40 * 128 * 4 + 40 * 4
     # the two-launch path counts per chunk of 1024 // k tokens into a (chunk, expert) table,
     # 256-aligned, followed by one status word per chunk.  E <= 64 past four chunks:
     # 16384 x 6 -> 97 chunks of 170 tokens; 97 * 64 * 4 = 24,832 is already 256-aligned

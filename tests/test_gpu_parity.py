@@ -71,11 +71,13 @@ def test_layout_full_size(name):
 @pytest.mark.parametrize(
     "T,E,k",
     [
-        # one launch: at most four 1024-entry chunks, or up to 64 with E > 64
+        # one launch: at most four 1024-entry chunks, or up to 64 with E > 64 and T <= 12288
         (1, 1, 1), (1, 8, 8), (7, 5, 3), (171, 64, 6), (512, 256, 8), (128, 1024, 32), (513, 256, 8),
-        (129, 1024, 32), (5000, 1024, 1), (8192, 256, 8),
-        # two launches (count, then scan and rank): E <= 64 past four chunks, or more than 64 chunks
+        (129, 1024, 32), (5000, 1024, 1), (8192, 256, 8), (12288, 128, 4),
+        # two launches (count, then scan and rank): E <= 64 past four chunks, more than 64 chunks,
+        # or more than 12288 tokens
         (513, 64, 8), (1000, 64, 6), (3000, 3, 2), (16384, 64, 1), (2047, 7, 7), (8193, 256, 8), (1024, 1024, 32),
+        (12289, 256, 4), (20000, 128, 2),
         # three launches: a (chunk, expert) table too large to read in every workgroup
         (140000, 256, 8), (20001, 1024, 7),
     ],
