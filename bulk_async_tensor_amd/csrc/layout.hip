@@ -20,10 +20,10 @@
 // then scan and rank in one launch, each workgroup summing the small
 // (chunk, expert) table instead of all ids.
 //
-// Three-launch path (tables too large to read per workgroup): count, scan
-// (one workgroup: totals, offsets and the base row of every (chunk, expert)),
-// place (one wave per chunk walking its entries 64 at a time, advancing
-// per-expert cursors in LDS).
+// Three-launch path (tables too large to read per workgroup): count, a scan
+// of the table over chunks (one workgroup per 64 experts, running counts
+// written in place), then the rank kernel of the two-launch path reading
+// two table entries per expert instead of the whole table.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -32,9 +32,7 @@ namespace ep {
 namespace {
 
 constexpr int kChunkEntries = 1024;   // entries per chunk (tokens * k), at most
-constexpr int kMaxSteps = kChunkEntries / kWave;  // 64-entry steps of one chunk
 constexpr int kCountThreads = 256;
-constexpr int kScanThreads = 1024;
 constexpr int kStatusOutOfRange = 1;
 constexpr int kStatusDuplicate = 2;
 
@@ -101,128 +99,48 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(const int32
   if (threadIdx.x == 0) chunk_status[c] = s_status;
 }
 
-// Single workgroup.  Threads form G = 1024 / Epad groups of Epad lanes
-// (Epad = E rounded up to a power of two, at least 64); group g owns a
-// contiguous range of chunks and lane e an expert.  chunk_counts is
-// overwritten in place with the first receive row of each (chunk, expert).
-__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __restrict__ chunk_counts,
-                                                                   const int32_t* __restrict__ chunk_status,
-                                                                   int nchunks, int E, int epad,
-                                                                   int32_t* __restrict__ counts,
-                                                                   int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ status) {
-  extern __shared__ int32_t lds[];
-  const int G = kScanThreads / epad;
-  int32_t* part = lds;                 // [G][epad]
-  int32_t* scan = lds + G * epad;      // [2][epad] ping-pong
-  __shared__ int32_t s_status;
-
-  const int tid = threadIdx.x;
-  const int g = tid / epad;
-  const int e = tid - g * epad;
-  const int cpg = (nchunks + G - 1) / G;
-  const int c0 = min(nchunks, g * cpg);
-  const int c1 = min(nchunks, c0 + cpg);
-
-  if (tid == 0) s_status = 0;
-
+// Middle launch of the three-launch path, for (chunk, expert) tables too
+// large for every rank workgroup to read: one workgroup per 64 experts.  Its
+// 16 waves take consecutive ranges of chunks and lane e of each wave an
+// expert; the table is overwritten in place with each expert's running count
+// up to and including each chunk.  The rank kernel then finds the rows of
+// its expert before its chunk in the previous chunk's entry and the expert's
+// total in the last chunk's.  Each entry is read and written by one thread
+// only.
+__global__ __launch_bounds__(1024) void layout_colscan_kernel(int32_t* __restrict__ chunk_counts, int nchunks,
+                                                              int E) {
+  constexpr int kWaves = 1024 / kWave;
+  __shared__ int32_t part[kWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * kWave + lane;
+  const int cpw = (nchunks + kWaves - 1) / kWaves;
+  const int c0 = min(nchunks, wave * cpw);
+  const int c1 = min(nchunks, c0 + cpw);
   int sum = 0;
   if (e < E) {
-#pragma unroll 8
-    for (int c = c0; c < c1; ++c) sum += chunk_counts[(int64_t)c * E + e];
-  }
-  part[g * epad + e] = sum;
-  int st = 0;
-  for (int c = tid; c < nchunks; c += kScanThreads) st |= chunk_status[c];
-  __syncthreads();
-  if (st) atomicOr(&s_status, st);
-
-  int pre = 0, tot = 0;
-  for (int g2 = 0; g2 < G; ++g2) {
-    const int v = part[g2 * epad + e];
-    pre += (g2 < g) ? v : 0;
-    tot += v;
-  }
-  // inclusive scan of tot over e (Hillis-Steele, ping-pong buffers)
-  if (g == 0) scan[e] = tot;
-  __syncthreads();
-  int src = 0;
-  for (int d = 1; d < epad; d <<= 1) {
-    if (g == 0) {
-      const int v = scan[src * epad + e] + ((e >= d) ? scan[src * epad + e - d] : 0);
-      scan[(src ^ 1) * epad + e] = v;
+    for (int cb = c0; cb < c1; cb += 8) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = cb + q < c1 ? chunk_counts[(int64_t)(cb + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += v[q];
     }
-    src ^= 1;
-    __syncthreads();
   }
-  const int incl = scan[src * epad + e];
-  const int excl = incl - tot;
-  if (g == 0 && e < E) {
-    counts[e] = tot;
-    offsets[e] = excl;
-    if (e == E - 1) offsets[E] = incl;
-  }
+  part[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += part[w][lane];
   if (e < E) {
-    int run = excl + pre;
-#pragma unroll 8
-    for (int c = c0; c < c1; ++c) {
-      const int64_t at = (int64_t)c * E + e;
-      const int v = chunk_counts[at];
-      chunk_counts[at] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  if (tid == 0 && status) status[0] = s_status;
-}
-
-// One wave per chunk.  run[e] (LDS) is the next free receive row of expert e
-// for this chunk.
-__global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
-                                                            int nbits, int chunk_tokens,
-                                                            const int32_t* __restrict__ chunk_base,
-                                                            int32_t* __restrict__ dest_row,
-                                                            int32_t* __restrict__ src_token) {
-  extern __shared__ int32_t run[];  // [E]
-  const int lane = lane_id();
-  const int c = blockIdx.x;
-  const int t0 = c * chunk_tokens;
-  const int nt = min(chunk_tokens, T - t0);
-  const int n = nt * k;
-  const int64_t i0 = (int64_t)t0 * k;
-
-  for (int e = lane; e < E; e += kWave) run[e] = chunk_base[(int64_t)c * E + e];
-
-  // fetch the whole chunk up front: one memory latency instead of one per step
-  int ent[kMaxSteps];
+    for (int cb = c0; cb < c1; cb += 8) {
+      int v[8];
 #pragma unroll
-  for (int s = 0; s < kMaxSteps; ++s) {
-    const int i = s * kWave + lane;
-    ent[s] = (i < n) ? idx[i0 + i] : -1;
-  }
-  __syncthreads();
-
-  const int nsteps = (n + kWave - 1) / kWave;
+      for (int q = 0; q < 8; ++q) v[q] = cb + q < c1 ? chunk_counts[(int64_t)(cb + q) * E + e] : 0;
 #pragma unroll
-  for (int s = 0; s < kMaxSteps; ++s) {
-    if (s >= nsteps) continue;  // uniform; keeps the loop fully unrolled so ent[] stays in VGPRs
-    const int i = s * kWave + lane;
-    const bool in_chunk = i < n;
-    const int e = ent[s];
-    const bool ok = in_chunk && (unsigned)e < (unsigned)E;
-    const uint64_t m = same_value_lanes(ok, e, nbits);
-    const int rank = mask_rank(m);
-    int r = -1;
-    if (ok) r = run[e] + rank;
-    // the highest lane of each group moves the expert's cursor past the group
-    if (ok && (m >> lane) == 1ull) run[e] = r + 1;
-    // one wave: its LDS operations complete in program order, so the next
-    // step's reads see these writes; no barrier (a barrier would also wait
-    // for the global stores below)
-    __builtin_amdgcn_wave_barrier();
-    if (in_chunk) {
-      dest_row[i0 + i] = r;
-      if (ok && src_token) src_token[r] = t0 + i / k;
+      for (int q = 0; q < 8; ++q) {
+        run += v[q];
+        if (cb + q < c1) chunk_counts[(int64_t)(cb + q) * E + e] = run;
+      }
     }
   }
 }
@@ -235,10 +153,12 @@ __global__ __launch_bounds__(kWave) void layout_place_kernel(const int32_t* __re
 // path histograms -- and sums it in G = 1024 / Epad groups of Epad lanes
 // (lane e an expert, group g a range of chunks): the totals give the
 // offsets, the chunks before its own the start of each expert's rows in this
-// chunk.  Ranks inside the chunk as in the one-launch path.
+// chunk.  Ranks inside the chunk as in the one-launch path.  With
+// `prefixed` (the three-launch path) the table already holds running counts
+// (layout_colscan_kernel): it reads two entries per expert instead.
 __global__ __launch_bounds__(1024) void layout_rank_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
                                                            int nbits, int epad, int chunk_tokens, int nchunks,
-                                                           const int32_t* __restrict__ chunk_counts,
+                                                           int prefixed, const int32_t* __restrict__ chunk_counts,
                                                            const int32_t* __restrict__ chunk_status,
                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ dest_row,
@@ -270,34 +190,42 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(const int32_t* __rest
   for (int cc = tid; cc < nchunks; cc += 1024) st |= chunk_status[cc];
   const int g = tid / epad;
   const int e = tid - g * epad;
-  const int cpg = (nchunks + G - 1) / G;
-  const int c0 = min(nchunks, g * cpg);
-  const int c1 = min(nchunks, c0 + cpg);
-  // up to 8 counts per trip, all loads issued before the first is used
-  int sum = 0, before = 0;
-  if (e < E) {
-    for (int cb = c0; cb < c1; cb += 8) {
-      int v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = cb + q < c1 ? chunk_counts[(int64_t)(cb + q) * E + e] : 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        sum += v[q];
-        before += cb + q < c ? v[q] : 0;
-      }
-    }
-  }
-  part_tot[g * epad + e] = sum;
-  part_pre[g * epad + e] = before;
-  __syncthreads();
-  if (st) atomicOr(&s_status, st);
-
   // expert totals and the part before this chunk; thread e of group 0 holds expert e
   int tot = 0, pre = 0;
-  if (g == 0 && e < E) {
-    for (int g2 = 0; g2 < G; ++g2) {
-      tot += part_tot[g2 * epad + e];
-      pre += part_pre[g2 * epad + e];
+  if (prefixed) {
+    if (g == 0 && e < E) {
+      tot = chunk_counts[(int64_t)(nchunks - 1) * E + e];
+      pre = c > 0 ? chunk_counts[(int64_t)(c - 1) * E + e] : 0;
+    }
+    __syncthreads();
+    if (st) atomicOr(&s_status, st);
+  } else {
+    const int cpg = (nchunks + G - 1) / G;
+    const int c0 = min(nchunks, g * cpg);
+    const int c1 = min(nchunks, c0 + cpg);
+    // up to 8 counts per trip, all loads issued before the first is used
+    int sum = 0, before = 0;
+    if (e < E) {
+      for (int cb = c0; cb < c1; cb += 8) {
+        int v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = cb + q < c1 ? chunk_counts[(int64_t)(cb + q) * E + e] : 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          sum += v[q];
+          before += cb + q < c ? v[q] : 0;
+        }
+      }
+    }
+    part_tot[g * epad + e] = sum;
+    part_pre[g * epad + e] = before;
+    __syncthreads();
+    if (st) atomicOr(&s_status, st);
+    if (g == 0 && e < E) {
+      for (int g2 = 0; g2 < G; ++g2) {
+        tot += part_tot[g2 * epad + e];
+        pre += part_pre[g2 * epad + e];
+      }
     }
   }
   int all = 0;
@@ -501,8 +429,13 @@ constexpr int64_t kFusedFewChunks = 4;
 constexpr int kFusedMinExperts = 65;  // one launch past a few chunks only above this many experts
 constexpr int kFusedMaxTokens = 12288;  // and for at most this many tokens
 // The two-launch path reads the whole (chunk, expert) table in every
-// workgroup; past this many counts the three-launch path scans it once.
-constexpr int64_t kRankTableMax = 64 * 1024;
+// workgroup; past this many counts the three-launch path scans it first.
+// Cold, us, two against three launches: 64 Ki counts (E = 128 / 512 /
+// 1024, k = 8, T = 65536 / 16384 / 8192) 28.2 / 21.3 / 21.2 against 25.1 /
+// 19.7 / 19.4; 32 Ki counts (E = 256 / 1024 / 64, k = 8 / 2 / 8) 18.1 /
+// 17.5 / 22.9 against 18.8 / 17.6 / 24.3.  At 128 Ki the three launches
+// take 19-26 us.
+constexpr int64_t kRankTableMax = 48 * 1024;
 
 enum class Path { Fused, Two, Three };
 
@@ -574,32 +507,21 @@ hipError_t launch_layout(const int32_t* idx, int T, int k, int E, int32_t* count
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (path == Path::Two) {
-    const size_t lds = rank_lds_bytes(E, epad);
-    if (lds > 64 * 1024) {
-      hipError_t e = allow_dynamic_lds((const void*)layout_rank_kernel, lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(nch), dim3(1024), lds, stream, idx, T, k, E, nbits, epad, ct, nch,
-                       chunk_counts, chunk_status, counts, offsets, dest_row, src_token, status);
-    return hipGetLastError();
-  }
-  {
-    const int G = kScanThreads / epad;
-    const size_t lds = (size_t)(G * epad + 2 * epad) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), lds, stream, chunk_counts, chunk_status,
-                       nch, E, epad, counts, offsets, status);
+  if (path == Path::Three) {
+    hipLaunchKernelGGL(layout_colscan_kernel, dim3((E + kWave - 1) / kWave), dim3(1024), 0, stream, chunk_counts, nch,
+                       E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  {
-    const size_t lds = (size_t)E * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_place_kernel, dim3(nch), dim3(kWave), lds, stream, idx, T, k, E, nbits, ct,
-                       chunk_counts, dest_row, src_token);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  const size_t lds = rank_lds_bytes(E, epad);
+  if (lds > 64 * 1024) {
+    hipError_t e = allow_dynamic_lds((const void*)layout_rank_kernel, lds);
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL(layout_rank_kernel, dim3(nch), dim3(1024), lds, stream, idx, T, k, E, nbits, epad, ct, nch,
+                     path == Path::Three ? 1 : 0, chunk_counts, chunk_status, counts, offsets, dest_row, src_token,
+                     status);
+  return hipGetLastError();
 }
 
 }  // namespace ep

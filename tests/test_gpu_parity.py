@@ -78,8 +78,8 @@ def test_layout_full_size(name):
         # or more than 12288 tokens
         (513, 64, 8), (1000, 64, 6), (3000, 3, 2), (16384, 64, 1), (2047, 7, 7), (8193, 256, 8), (1024, 1024, 32),
         (12289, 256, 4), (20000, 128, 2),
-        # three launches: a (chunk, expert) table too large to read in every workgroup
-        (140000, 256, 8), (20001, 1024, 7),
+        # three launches: a (chunk, expert) table too large to read in every workgroup (past 48 Ki counts)
+        (140000, 256, 8), (20001, 1024, 7), (14000, 512, 8), (65536, 1024, 2),
     ],
 )
 def test_layout_ragged_and_extreme(T, E, k):
