@@ -842,7 +842,13 @@ hipError_t launch_dispatch(Variant v, const Budget& b, const void* x, int T, int
     // x evicted: 314.6 us in four launches against 337.4 in one).  On fewer
     // CUs each CU's reads are the bound and a launch per trip only adds
     // ramps (24 CUs: 743 against 666 us), so the grid stays persistent.
-    const bool per_trip_launch = 2 * (int64_t)grid >= b.all_cus;
+    // A trip that moves less than 32 MB (small rows at small k) does not pay
+    // for its launch: H = 896 / 1024, k = 2 (22 and 25 MB per trip on 256
+    // CUs), T = 8192 to 32768, one launch 7-13% faster (47.1 against 42.0
+    // us at H = 1024, T = 32768); at 51 to 113 MB per trip the launch per
+    // trip was even or up to 4% ahead.
+    const int64_t trip_bytes = per_trip * (int64_t)row_vec * kVecBytes * (1 + k);
+    const bool per_trip_launch = 2 * (int64_t)grid >= b.all_cus && trip_bytes >= (32ll << 20);
     const int64_t batch = per_trip_launch ? per_trip : (int64_t)T;
     for (int64_t t0 = 0; t0 < T; t0 += batch) {
       const int tb = (int)(T - t0 < batch ? T - t0 : batch);

@@ -303,12 +303,15 @@ def test_dispatch_vgpr_wg_ragged_rows(H, k, T, budget):
 # (H = 5000 and 9000: 2 and 1 KiB slabs; H = 32768: 8 slabs per row).
 # Rows of more than 16 vectors per lane that no slab size divides take
 # 14-vector slabs in the workgroup-phased kernel (H = 9000, 11264, 15360).
+# Trips of less than 32 MB run as one persistent launch of several trips
+# (H = 1024, k = 1 and H = 896, k = 2: 16 and 21 MB per trip).
 @pytest.mark.parametrize("H,k,T", [(7168, 8, 511), (7168, 8, 512), (7168, 8, 1536), (7168, 6, 2047), (7168, 6, 2048),
                                    (2048, 8, 1023), (2048, 8, 1024), (5120, 4, 1024), (4096, 2, 1536),
                                    (4096, 3, 1023), (4096, 3, 1024), (2880, 5, 2048), (7176, 8, 2100),
                                    (4104, 8, 511), (4104, 8, 512), (5000, 6, 1000), (7176, 8, 2047), (7176, 6, 1537),
                                    (8184, 8, 700), (5000, 7, 1000), (9000, 6, 256), (5000, 8, 511),
-                                   (32768, 4, 384), (9000, 8, 2100), (11264, 2, 2048), (15360, 6, 2200)])
+                                   (32768, 4, 384), (9000, 8, 2100), (11264, 2, 2048), (15360, 6, 2200),
+                                   (1024, 1, 16384), (896, 2, 12000)])
 def test_dispatch_default_batch_sizes(H, k, T):
     ep.ep_set_variant("auto")
     ep.ep_set_num_cus(0)
