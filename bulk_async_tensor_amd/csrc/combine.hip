@@ -519,9 +519,23 @@ PhaseFn pick_phase(int seg_vec, int held, int k) {
 // to keep in flight (H = 7168, T k = 32 Ki: 5.82 against 4.91 TB/s at
 // k = 4, 5.73 against 4.87 at k = 2); a requested slab of 1 or of 2 and
 // more takes 1 or 2.
+// Rows of 5 or 7 vectors per lane, which hold two tokens per unit, take
+// 2-vector runs over the row padded by one vector: a token then spans an
+// even number of vectors, so no run straddles two tokens, and k <= 4 takes
+// the phased kernel instead of the register one.  The padding vector is
+// loaded as the row's last one and never stored.  Cold, same-run A/B, k = 2,
+// 3, 4, T = 8192 and 16384: H = 2304 / 2560 / 3584 4-14% faster (3584,
+// k = 4, T = 16384: 113.0 against 99.5 us), T = 2048 and 4096 within 1%
+// but for one 7% loss (2304, k = 3, T = 4096).  At 3 vectors the padding
+// adds a third more loads: H = 1152, T = 8192 lost 14-19%.
+bool phase_pad(int row_vec) {
+  const int nv = (row_vec + kWave - 1) / kWave;
+  return nv == 5 || nv == 7;
+}
+
 int combine_phase_seg(const Budget& b, int row_vec, int k) {
   const PhaseShape p16 = phase_shape(row_vec);
-  const bool can2 = p16.tpu == 1 || p16.nv % 2 == 0;
+  const bool can2 = p16.tpu == 1 || p16.nv % 2 == 0 || phase_pad(row_vec);
   const bool want2 = b.slab_vpl >= 2 || (b.slab_vpl == 0 && k <= 4);
   return want2 && can2 ? 2 : 1;
 }
@@ -559,18 +573,21 @@ PhaseShape combine_phase_shape(int row_vec, int seg_vec, int cus, int all_cus, i
     }
     return p;
   }
+  // (a padded row reads as one vector longer; the launch then takes the
+  // kernel instance that clamps and skips columns past the row)
+  if (seg_vec == 2 && phase_pad(row_vec)) return phase_shape(row_vec + kWave);
   return phase_shape(row_vec);
 }
 
 
 hipError_t launch_phase(const Budget& b, const void* y, int64_t recv_rows, int row_vec, const int32_t* dest_row,
                         const float* w, int T, int k, void* out, hipStream_t stream) {
-  const bool even = row_vec % kWave == 0;
   // 14 held vectors when a unit never needs more (whole tokens at H = 7168
   // in the 16-wave shape), which frees registers for the reads
   const int seg_vec = combine_phase_seg(b, row_vec, k);
   const int cus = b.num_cus > 0 && b.num_cus < b.device_cus ? b.num_cus : b.device_cus;
   const PhaseShape ps = combine_phase_shape(row_vec, seg_vec, cus, b.all_cus, T);
+  const bool even = row_vec % kWave == 0 && (int64_t)ps.nv * kWave <= row_vec;  // no padded column
   const int unit_vec = ps.nseg == 1 ? ps.tpu * ps.nv : ps.seg;
   const int held = ps.held == kPhaseWideHeld ? kPhaseWideHeld : unit_vec <= 14 ? 14 : 16;
   PhaseFn fn = even ? pick_phase<true>(seg_vec, held, k) : pick_phase<false>(seg_vec, held, k);

@@ -515,14 +515,16 @@ def test_combine_phase_batches(T, budget, k):
 # workgroups (4096).  Rows of 9 vectors per lane (H = 4104 .. 4608) take
 # three rows per wave, or two where that needs fewer passes over the grid:
 # two at T = 4096 and 8192, three at T = 6144 and 12288 (a tie), with
-# a ragged last vector at H = 4104 and 4160.
+# a ragged last vector at H = 4104 and 4160.  At k <= 4, rows of 5 and 7
+# vectors per lane run padded by one vector (H = 2304 ragged, 2560 whole,
+# 3584, 3000 ragged); 3 vectors (H = 1152) keep the register kernel.
 @pytest.mark.parametrize(
     "H,k,T",
     [(2048, 4, 7000), (2048, 4, 8192), (4096, 8, 3686), (4096, 6, 4505), (3072, 2, 4600), (3072, 2, 4915),
      (2048, 2, 9830), (5120, 8, 2457), (5120, 8, 2800), (5120, 8, 2900), (7168, 8, 2860), (7168, 6, 2800),
      (4096, 3, 3500), (4096, 3, 3700), (2048, 1, 9600), (2048, 1, 9900), (7168, 5, 3760), (7168, 5, 3780),
      (7168, 7, 3068), (7168, 7, 3076), (4608, 8, 8192), (4160, 6, 4096), (4104, 7, 6144), (4160, 5, 12288),
-     (4160, 8, 4097)],
+     (4160, 8, 4097), (2304, 4, 8192), (2560, 3, 8191), (3584, 2, 16384), (3000, 4, 5000), (1152, 4, 8192)],
 )
 def test_combine_default_partial_fill(H, k, T):
     ep.ep_set_variant("auto")
